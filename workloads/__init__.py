@@ -1,0 +1,327 @@
+"""Seeded synthetic workloads for paged KV-cache attention.
+
+This module only *draws inputs*: sequence lengths, the order in which the
+physical block pool hands out blocks, the logical K/V values of every
+sequence, the query rows, and the order of cache operations (add a sequence,
+fork it from a shared prefix holder, append tokens).  It holds none of the
+method's arithmetic: no block-table or slot computation, no attention, no
+copy-on-write decision.  Both the CPU oracle and the HIP path consume the same
+drawn inputs and each applies its own block manager and kernels to them.
+
+Workloads follow the problem statement of the PagedAttention pages (fixed
+block size in tokens, per-sequence block tables, context lengths that include
+the token appended in the step, read-only shared prefix blocks), with the
+sizes of the five synthetic configurations:
+
+  tiny_decode            4 seqs, lens {1,15,16,33}, BS 16, 2/2 heads, D 64, fp32
+  mha_decode_7b          64 seqs, lens U{128..2048}, BS 16, 32/32 heads, D 128, fp16
+  gqa_shared_prefix      256 seqs in groups of 8 sharing a 512-token prefix,
+                         lens lognormal(median 512, sigma 1, cap 8192),
+                         BS 16, 32/8 heads, D 128, bf16
+  long_splitk_decode     4 seqs x 131072 tokens, BS 32, 32/8 heads, D 128,
+                         bf16, 512-token partitions
+  mixed_chunked_prefill  8 chunks of 512 tokens on cached contexts U{0..4096}
+                         plus 120 decode seqs with lens U{256..4096},
+                         BS 16, 32/8 heads, D 128, bf16
+
+Values are fp32 N(0,1) draws rounded to the storage type with round to
+nearest even.  Storage representations on the host: fp32 -> float32,
+fp16 -> float16, bf16 -> uint16 bit patterns (NumPy has no bfloat16).
+"""
+from __future__ import annotations
+
+import math
+import os
+from concurrent.futures import ThreadPoolExecutor
+from dataclasses import dataclass, field
+
+import numpy as np
+
+SEED_ROOT = 403
+
+# storage type name -> (host numpy dtype of the stored bits/values, bytes)
+STORAGE = {"f32": (np.float32, 4), "f16": (np.float16, 2), "bf16": (np.uint16, 2)}
+
+# value draws are made in fixed-size chunks, each from its own child seed, so
+# the result does not depend on how many threads fill it
+_CHUNK = 1 << 22
+
+CONFIG_NAMES = (
+    "tiny_decode",
+    "mha_decode_7b",
+    "gqa_shared_prefix",
+    "long_splitk_decode",
+    "mixed_chunked_prefill",
+)
+
+
+@dataclass(frozen=True)
+class Spec:
+    """Shape of one paged-cache workload (structure only)."""
+
+    name: str
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    block_size: int
+    dtype: str  # "f32" | "f16" | "bf16"
+    num_blocks: int  # physical blocks in the pool, the poison block included
+    partition_size: int = 0  # decode split-K partition in tokens, 0 = one pass
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.head_dim)
+
+    @property
+    def poison_block(self) -> int:
+        """Reserved block that table padding points at; never handed out."""
+        return self.num_blocks - 1
+
+    @property
+    def elem_bytes(self) -> int:
+        return STORAGE[self.dtype][1]
+
+
+@dataclass
+class SeqPlan:
+    """One sequence of the workload.
+
+    parent/keep: the sequence is forked from `parent` sharing its first
+    `keep` tokens (parent == -1: a fresh sequence, keep == 0).
+    pre_len: tokens in the cache before the step (shared ones included).
+    n_new: tokens appended in the step; they are also the query rows.
+    in_batch: False for prefix holders that only own shared blocks.
+    """
+
+    seq_id: int
+    parent: int
+    keep: int
+    pre_len: int
+    n_new: int
+    in_batch: bool
+
+    @property
+    def context_len(self) -> int:
+        return self.pre_len + self.n_new
+
+
+@dataclass
+class Op:
+    """A cache operation in the order the workload issues it."""
+
+    kind: str  # "add" | "fork" | "append"
+    seq: int
+    parent: int = -1
+    keep: int = 0
+    n: int = 0
+    k: np.ndarray | None = None  # [n][Hkv][D] storage repr, for "append"
+    v: np.ndarray | None = None
+
+
+@dataclass
+class Workload:
+    spec: Spec
+    seqs: list  # SeqPlan, setup order (prefix holders first, then the batch)
+    free_order: np.ndarray  # int32 permutation of 0..num_blocks-2
+    own_k: dict  # seq_id -> [pre_len - keep + n_new][Hkv][D]
+    own_v: dict
+    q: dict  # seq_id -> [n_new][Hq][D]
+    seed: tuple = ()
+    notes: dict = field(default_factory=dict)
+
+    # ---- views (structure only) -------------------------------------------------
+    @property
+    def batch(self) -> list:
+        return [p for p in self.seqs if p.in_batch]
+
+    def plan(self, seq_id: int) -> SeqPlan:
+        for p in self.seqs:
+            if p.seq_id == seq_id:
+                return p
+        raise KeyError(seq_id)
+
+    def setup_ops(self):
+        """Operations that build the pre-step cache, in issue order."""
+        ops = []
+        for p in self.seqs:
+            if p.parent < 0:
+                ops.append(Op("add", p.seq_id))
+            else:
+                ops.append(Op("fork", p.seq_id, parent=p.parent, keep=p.keep))
+            n_own = p.pre_len - p.keep
+            if n_own > 0:
+                ops.append(Op("append", p.seq_id, n=n_own,
+                              k=self.own_k[p.seq_id][:n_own], v=self.own_v[p.seq_id][:n_own]))
+        return ops
+
+    def step_ops(self):
+        """The step's appends, one per batch sequence in batch order."""
+        ops = []
+        for p in self.batch:
+            n_own = p.pre_len - p.keep
+            ops.append(Op("append", p.seq_id, n=p.n_new,
+                          k=self.own_k[p.seq_id][n_own:], v=self.own_v[p.seq_id][n_own:]))
+        return ops
+
+    def logical_kv(self, seq_id: int):
+        """Full logical K/V of a sequence: inherited prefix then own tokens."""
+        p = self.plan(seq_id)
+        if p.parent < 0:
+            return self.own_k[seq_id], self.own_v[seq_id]
+        pk, pv = self.logical_kv(p.parent)
+        return (np.concatenate([pk[: p.keep], self.own_k[seq_id]]),
+                np.concatenate([pv[: p.keep], self.own_v[seq_id]]))
+
+    def step_q(self):
+        """Query rows of the batch, concatenated in batch order: [sum n_new][Hq][D]."""
+        return np.concatenate([self.q[p.seq_id] for p in self.batch])
+
+    def step_kv(self):
+        """New tokens' K/V concatenated in batch order: [sum n_new][Hkv][D]."""
+        ks, vs = [], []
+        for p in self.batch:
+            n_own = p.pre_len - p.keep
+            ks.append(self.own_k[p.seq_id][n_own:])
+            vs.append(self.own_v[p.seq_id][n_own:])
+        return np.concatenate(ks), np.concatenate(vs)
+
+
+# ---- value draws ----------------------------------------------------------------
+
+def round_to_storage(x: np.ndarray, dtype: str) -> np.ndarray:
+    """fp32 values -> storage representation, round to nearest even."""
+    if dtype == "f32":
+        return x.astype(np.float32, copy=False)
+    if dtype == "f16":
+        return x.astype(np.float16)
+    if dtype == "bf16":
+        u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+        # finite inputs only: add half an ulp of bf16, ties to the even result
+        r = u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))
+        return (r >> np.uint32(16)).astype(np.uint16)
+    raise ValueError(dtype)
+
+
+def normal_values(key: tuple, shape, dtype: str, threads: int | None = None) -> np.ndarray:
+    """N(0,1) fp32 draws for the stream `key`, rounded to `dtype`."""
+    n = int(np.prod(shape))
+    out = np.empty(n, dtype=np.float32)
+    chunks = [(c, c * _CHUNK, min(n, (c + 1) * _CHUNK)) for c in range((n + _CHUNK - 1) // _CHUNK)]
+
+    def fill(item):
+        c, a, b = item
+        g = np.random.default_rng(np.random.SeedSequence(list(key) + [c]))
+        g.standard_normal(b - a, dtype=np.float32, out=out[a:b])
+
+    nt = threads or min(16, len(os.sched_getaffinity(0)))
+    if len(chunks) > 1 and nt > 1:
+        with ThreadPoolExecutor(nt) as ex:
+            list(ex.map(fill, chunks))
+    else:
+        for it in chunks:
+            fill(it)
+    return round_to_storage(out, dtype).reshape(shape)
+
+
+def _stream(cfg_key, *parts):
+    return (SEED_ROOT,) + tuple(cfg_key) + tuple(parts)
+
+
+def synthesize(spec: Spec, plans: list, cfg_key: tuple, notes=None) -> Workload:
+    """Draw the pool order and every value for a list of sequence plans."""
+    H, D = spec.num_kv_heads, spec.head_dim
+    g = np.random.default_rng(np.random.SeedSequence(list(_stream(cfg_key, 1))))
+    free_order = g.permutation(spec.num_blocks - 1).astype(np.int32)
+    own_k, own_v, q = {}, {}, {}
+    for p in plans:
+        n_own = p.context_len - p.keep
+        own_k[p.seq_id] = normal_values(_stream(cfg_key, 2, p.seq_id), (n_own, H, D), spec.dtype)
+        own_v[p.seq_id] = normal_values(_stream(cfg_key, 3, p.seq_id), (n_own, H, D), spec.dtype)
+    for p in plans:
+        if p.in_batch:
+            q[p.seq_id] = normal_values(_stream(cfg_key, 4, p.seq_id),
+                                        (p.n_new, spec.num_q_heads, D), spec.dtype)
+    return Workload(spec, plans, free_order, own_k, own_v, q, seed=tuple(cfg_key), notes=notes or {})
+
+
+def pool_blocks_needed(plans: list, block_size: int) -> int:
+    """Upper bound of blocks the plans can occupy (a partially shared last
+    block may be replaced by a private copy, counted once more)."""
+    need = 0
+    for p in plans:
+        need += -(-p.context_len // block_size) - (p.keep // block_size)
+    return need
+
+
+def sized_pool(plans, block_size, fixed=None) -> int:
+    """Pool = needed + 10% + 1 (the +1 is the poison block)."""
+    if fixed is not None:
+        return fixed
+    need = pool_blocks_needed(plans, block_size)
+    return need + -(-need // 10) + 1
+
+
+# ---- the five configurations ----------------------------------------------------
+
+def _decode_plans(ctx_lens):
+    return [SeqPlan(i, -1, 0, int(L) - 1, 1, True) for i, L in enumerate(ctx_lens)]
+
+
+def make(name: str, reduced: bool = False, seed: int = 0) -> Workload:
+    """Build a named configuration.  `reduced=True` keeps the shape (heads,
+    head_dim, block size, dtype, sharing structure) but shrinks the batch and
+    lengths so the fp64 oracle finishes in seconds while still spanning many
+    blocks, several partitions and ragged tails."""
+    k = CONFIG_NAMES.index(name) + 1
+    key = (k, seed, 1 if reduced else 0)
+    lg = np.random.default_rng(np.random.SeedSequence(list(_stream(key, 0))))
+    if name == "tiny_decode":
+        plans = _decode_plans([1, 15, 16, 33])
+        spec = Spec(name, 2, 2, 64, 16, "f32", num_blocks=16)
+        return synthesize(spec, plans, key)
+    if name == "mha_decode_7b":
+        S, lo, hi = (64, 128, 2048) if not reduced else (6, 1, 300)
+        lens = lg.integers(lo, hi, size=S, endpoint=True)
+        plans = _decode_plans(lens)
+        spec = Spec(name, 32, 32, 128, 16, "f16", num_blocks=sized_pool(plans, 16))
+        return synthesize(spec, plans, key)
+    if name == "gqa_shared_prefix":
+        groups, per, prefix, cap = (32, 8, 512, 8192) if not reduced else (2, 4, 64, 400)
+        median = prefix
+        S = groups * per
+        lens = np.clip(np.rint(np.exp(lg.normal(math.log(median), 1.0, size=S))), 1, cap).astype(np.int64)
+        plans = []
+        for gi in range(groups):
+            plans.append(SeqPlan(S + gi, -1, 0, prefix, 0, False))
+        for s in range(S):
+            L = int(lens[s])
+            plans.append(SeqPlan(s, S + s // per, min(L - 1, prefix), L - 1, 1, True))
+        spec = Spec(name, 32, 8, 128, 16, "bf16", num_blocks=sized_pool(plans, 16))
+        return synthesize(spec, plans, key, notes={"groups": groups, "group_size": per,
+                                                   "prefix_tokens": prefix})
+    if name == "long_splitk_decode":
+        S, L, P = (4, 131072, 512) if not reduced else (2, 1500, 512)
+        plans = _decode_plans([L] * S)
+        spec = Spec(name, 32, 8, 128, 32, "bf16", num_blocks=sized_pool(plans, 32), partition_size=P)
+        return synthesize(spec, plans, key)
+    if name == "mixed_chunked_prefill":
+        n_chunk, chunk, cmax, n_dec, dlo, dhi = ((8, 512, 4096, 120, 256, 4096) if not reduced
+                                                 else (3, 70, 200, 5, 1, 300))
+        cached = lg.integers(0, cmax, size=n_chunk, endpoint=True)
+        dec = lg.integers(dlo, dhi, size=n_dec, endpoint=True)
+        plans = [SeqPlan(i, -1, 0, int(c), chunk, True) for i, c in enumerate(cached)]
+        plans += [SeqPlan(n_chunk + i, -1, 0, int(L) - 1, 1, True) for i, L in enumerate(dec)]
+        spec = Spec(name, 32, 8, 128, 16, "bf16", num_blocks=sized_pool(plans, 16))
+        return synthesize(spec, plans, key, notes={"num_chunks": n_chunk, "chunk_tokens": chunk})
+    raise ValueError(name)
+
+
+def custom(num_q_heads, num_kv_heads, head_dim, block_size, dtype, ctx_lens, n_new=None,
+           seed=0, partition_size=0, num_blocks=None, name="custom") -> Workload:
+    """Independent fresh sequences with given context lengths (tests)."""
+    n_new = n_new if n_new is not None else [1] * len(ctx_lens)
+    plans = [SeqPlan(i, -1, 0, int(L) - int(n), int(n), True) for i, (L, n) in enumerate(zip(ctx_lens, n_new))]
+    spec = Spec(name, num_q_heads, num_kv_heads, head_dim, block_size, dtype,
+                num_blocks=sized_pool(plans, block_size, num_blocks), partition_size=partition_size)
+    return synthesize(spec, plans, (99, seed, num_q_heads, num_kv_heads, head_dim, block_size,
+                                    ["f32", "f16", "bf16"].index(dtype)))
