@@ -1,0 +1,292 @@
+#!/usr/bin/env python3
+"""Benchmark of the paged KV-cache attention hot path on one MI355X.
+
+A step is one pass of the hot path over one batch: the block manager's slot
+mapping and copy-on-write pairs for the step's new tokens (host, prepared once
+since repeating the step is idempotent), then on one HIP stream the
+copy-on-write block copies, the KV append through the slot mapping, and the
+attention kernels (paged decode for one-token sequences, chunked prefill for
+chunks).  Inputs are resident in HBM before the timed region.
+
+Headline workload: 7B-shaped MHA decode (64 sequences, contexts U{128..2048},
+32 q = 32 KV heads, head_dim 128, fp16, block_size 16).  `value` is the
+step's algorithmic bytes (K/V read, q/out, tables, append) over the step time.
+A secondary measurement times chunked prefill on the mixed workload (8 chunks
+of 512 tokens on cached contexts U{0..4096}, 32/8 heads, bf16) in TFLOP/s.
+
+Prints one JSON line on stdout; progress goes to stderr.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2516.6  # MI355X dense bf16/fp16 matrix peak
+METRIC = "paged decode KV-read GB/s (% HBM peak) + seqs/s; prefill TFLOP/s (% MFMA)"
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def decode_bytes(lens, num_q_heads, num_kv_heads, head_dim, block_size, eb):
+    import numpy as np
+
+    lens = np.asarray(lens, dtype=np.int64)
+    kv = int(lens.sum()) * num_kv_heads * head_dim * eb * 2
+    qo = len(lens) * num_q_heads * head_dim * eb * 2
+    meta = int(((lens + block_size - 1) // block_size).sum()) * 4 + len(lens) * 4
+    return kv + qo + meta, kv
+
+
+def prefill_flops(cached, n_new, num_q_heads, head_dim):
+    """QK^T and PV over the causal (unmasked) region only: per chunk of n rows
+    on C cached tokens, Hq * 4 * D * (n*C + n(n+1)/2)."""
+    tot = 0
+    for c, n in zip(cached, n_new):
+        tot += num_q_heads * 4 * head_dim * (n * c + n * (n + 1) // 2)
+    return tot
+
+
+class Step:
+    """Device state of one workload's step, ready to be replayed."""
+
+    def __init__(self, wl, partition_size, device="cuda"):
+        import numpy as np
+        import torch
+
+        import paged_kv_cache_403_amd as P
+        from paged_kv_cache_403_amd.runtime import PagedKVCache, to_device
+
+        self.P = P
+        sp = wl.spec
+        self.wl = wl
+        t0 = time.time()
+        self.cache = PagedKVCache(sp.num_blocks, sp.num_kv_heads, sp.block_size, sp.head_dim, sp.dtype, device,
+                                  wl.free_order, fill_value=1.0e4)
+        self.cache.apply_ops(wl.setup_ops())
+        batch = wl.batch
+        self.plan = self.cache.prepare_step([p.seq_id for p in batch], [p.n_new for p in batch], sp.poison_block)
+        k_new, v_new = wl.step_kv()
+        self.k_new = to_device(k_new, sp.dtype, device)
+        self.v_new = to_device(v_new, sp.dtype, device)
+        q_all = wl.step_q()
+        n_new = self.plan.n_new
+        starts = np.concatenate([[0], np.cumsum(n_new)])
+        dec = np.array([i for i in range(len(batch)) if n_new[i] == 1], dtype=np.int64)
+        pre = np.array([i for i in range(len(batch)) if n_new[i] > 1], dtype=np.int64)
+        self.dec, self.pre = dec, pre
+        self.partition_size = partition_size
+        if len(dec):
+            self.q_dec = to_device(q_all[starts[dec]], sp.dtype, device)
+            self.out_dec = torch.empty_like(self.q_dec)
+            idx = torch.from_numpy(dec).to(device)
+            self.tab_dec = self.plan.block_tables[idx].contiguous()
+            self.len_dec = self.plan.context_lens[idx].contiguous()
+            self.max_dec = int(self.plan.host_lens[dec].max())
+            wsb = P.pa_decode_workspace_bytes(len(dec), sp.num_q_heads, sp.head_dim, self.max_dec, partition_size)
+            self.ws = torch.empty(max(wsb, 4), dtype=torch.uint8, device=device) if wsb else None
+            self.part_used = (P.pa_decode_choose_partition(self.cache.desc, len(dec), sp.num_q_heads, self.max_dec)
+                              if partition_size == -1 else partition_size)
+            self.dec_bytes, self.dec_kv_bytes = decode_bytes(self.plan.host_lens[dec], sp.num_q_heads,
+                                                             sp.num_kv_heads, sp.head_dim, sp.block_size,
+                                                             sp.elem_bytes)
+        else:
+            self.dec_bytes = self.dec_kv_bytes = 0
+        if len(pre):
+            rows = np.concatenate([np.arange(starts[i], starts[i + 1]) for i in pre])
+            self.q_pre = to_device(q_all[rows], sp.dtype, device)
+            self.out_pre = torch.empty_like(self.q_pre)
+            cu = np.concatenate([[0], np.cumsum(n_new[pre])]).astype(np.int32)
+            self.cu_pre = torch.from_numpy(cu).to(device)
+            idx = torch.from_numpy(pre).to(device)
+            self.tab_pre = self.plan.block_tables[idx].contiguous()
+            self.len_pre = self.plan.context_lens[idx].contiguous()
+            self.maxq_pre = int(n_new[pre].max())
+            self.maxc_pre = int(self.plan.host_lens[pre].max())
+            cached = self.plan.host_lens[pre] - n_new[pre]
+            self.pre_flops = prefill_flops(cached, n_new[pre], sp.num_q_heads, sp.head_dim)
+        else:
+            self.pre_flops = 0
+        T = int(n_new.sum())
+        eb = sp.elem_bytes
+        self.append_bytes = T * sp.num_kv_heads * sp.head_dim * eb * 4 + T * 8
+        npairs = len(self.plan.host_pairs)
+        self.copy_bytes = npairs * sp.num_kv_heads * sp.block_size * sp.head_dim * eb * 4 + npairs * 8
+        torch.cuda.synchronize()
+        log(f"{sp.name}: setup {time.time() - t0:.1f}s, {len(dec)} decode seqs, {len(pre)} chunks, "
+            f"{npairs} copy pairs")
+
+    def copy_append(self):
+        self.P.pa_copy_blocks(self.cache.desc, self.plan.cow_pairs)
+        self.P.pa_kv_append(self.cache.desc, self.k_new, self.v_new, self.plan.slot_mapping)
+
+    def decode(self):
+        sp = self.wl.spec
+        self.P.pa_decode(self.cache.desc, self.q_dec, self.out_dec, self.tab_dec, self.len_dec, self.max_dec,
+                         sp.scale, self.partition_size, self.ws)
+
+    def prefill(self):
+        sp = self.wl.spec
+        self.P.pa_prefill_chunk(self.cache.desc, self.q_pre, self.out_pre, self.cu_pre, self.len_pre, self.tab_pre,
+                                self.maxq_pre, self.maxc_pre, sp.scale)
+
+
+def time_steps(st, steps, warmup):
+    """Time `steps` whole steps, plus each kernel group with events on the
+    stream the library launches on (torch's current stream)."""
+    import torch
+
+    for _ in range(warmup):
+        st.copy_append()
+        if len(st.pre):
+            st.prefill()
+        if len(st.dec):
+            st.decode()
+    torch.cuda.synchronize()
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    marks = []
+    t0 = time.perf_counter()
+    start = ev()
+    start.record()
+    for _ in range(steps):
+        e = [ev(), ev(), ev(), ev()]
+        e[0].record()
+        st.copy_append()
+        e[1].record()
+        if len(st.pre):
+            st.prefill()
+        e[2].record()
+        if len(st.dec):
+            st.decode()
+        e[3].record()
+        marks.append(e)
+    end = ev()
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    total_ms = start.elapsed_time(end)
+    ca = sum(m[0].elapsed_time(m[1]) for m in marks) / steps
+    pf = sum(m[1].elapsed_time(m[2]) for m in marks) / steps
+    dc = sum(m[2].elapsed_time(m[3]) for m in marks) / steps
+    return total_ms / steps, wall * 1e3 / steps, ca, pf, dc
+
+
+def cpu_baseline(wl, budget_s=15.0):
+    """The fp64 oracle on a bounded sample of the same workload (leading
+    sequences of the batch until about budget_s of work), in GB/s of the same
+    algorithmic decode bytes."""
+    import numpy as np
+
+    from oracle import attention as A
+    from oracle.cache import run_workload
+
+    sp = wl.spec
+    st = run_workload(wl)
+    q = wl.step_q()
+    rows = np.concatenate([[0], np.cumsum(st.q_lens)])
+    done, t_used, byts = 0, 0.0, 0
+    while done < len(st.context_lens) and t_used < budget_s:
+        s = done
+        t0 = time.perf_counter()
+        A.paged_attention(q[rows[s]:rows[s + 1]], st.pool.k, st.pool.v, st.tables[s:s + 1],
+                          st.context_lens[s:s + 1], st.q_lens[s:s + 1], sp.scale, sp.dtype)
+        t_used += time.perf_counter() - t0
+        b, _ = decode_bytes(st.context_lens[s:s + 1], sp.num_q_heads, sp.num_kv_heads, sp.head_dim,
+                            sp.block_size, sp.elem_bytes)
+        byts += b
+        done += 1
+    try:
+        threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
+    except Exception:
+        threads = os.cpu_count()
+    return {"value": round(byts / t_used / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"{done} of {len(st.context_lens)} sequences of {sp.name} (fp64 NumPy oracle, "
+                      f"{t_used:.1f}s), decode bytes of the sample over oracle time"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="mha_decode_7b")
+    ap.add_argument("--partition", type=int, default=-1, help="decode partition tokens (0 one pass, -1 auto)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true", help="skip the chunked-prefill measurement")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import workloads
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    log(f"device {torch.cuda.get_device_name(0)}")
+    wl = workloads.make(args.workload)
+    sp = wl.spec
+    st = Step(wl, args.partition)
+    ms, wall_ms, ca_ms, pf_ms, dc_ms = time_steps(st, args.steps, args.warmup)
+    step_bytes = st.dec_bytes + st.append_bytes + st.copy_bytes
+    value = step_bytes / (ms * 1e-3) / 1e9
+    n_seqs = len(wl.batch)
+    log(f"{sp.name}: {ms * 1e3:.1f} us/step (wall {wall_ms * 1e3:.1f}), decode {dc_ms * 1e3:.1f} us, "
+        f"copy+append {ca_ms * 1e3:.1f} us, {value:.0f} GB/s")
+    dom_bytes, dom_ms, bound = st.dec_bytes, dc_ms, "hbm"
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": sp.dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": sp.name, "num_seqs": n_seqs, "num_q_heads": sp.num_q_heads,
+            "num_kv_heads": sp.num_kv_heads, "head_dim": sp.head_dim, "block_size": sp.block_size,
+            "context_tokens": int(st.plan.host_lens.sum()), "max_context": int(st.plan.host_lens.max()),
+            "decode_partition_tokens": getattr(st, "part_used", None), "parallelism": "none (1 GPU)",
+        },
+        "seqs_per_s": round(n_seqs / (ms * 1e-3), 1),
+        "breakdown_us": {"copy_append": round(ca_ms * 1e3, 2), "prefill": round(pf_ms * 1e3, 2),
+                         "decode": round(dc_ms * 1e3, 2)},
+        "roofline": {"bound": bound, "achieved": round(dom_bytes / (dom_ms * 1e-3) / 1e9, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(dom_bytes / (dom_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                     "traffic": None, "kernel": "decode_kernel", "bytes_per_launch": dom_bytes},
+    }
+    if not args.no_prefill:
+        wl5 = workloads.make("mixed_chunked_prefill")
+        st5 = Step(wl5, -1)
+        ms5, _, ca5, pf5, dc5 = time_steps(st5, max(5, args.steps // 5), 2)
+        tf = st5.pre_flops / (pf5 * 1e-3) / 1e12
+        dec_gbs = st5.dec_bytes / (dc5 * 1e-3) / 1e9
+        log(f"mixed_chunked_prefill: step {ms5 * 1e3:.1f} us, prefill {pf5 * 1e3:.1f} us = {tf:.1f} TFLOP/s, "
+            f"decode {dc5 * 1e3:.1f} us = {dec_gbs:.0f} GB/s")
+        result["prefill"] = {
+            "workload": "mixed_chunked_prefill", "ms_per_step": round(ms5, 5),
+            "prefill_us": round(pf5 * 1e3, 2), "flops": st5.pre_flops,
+            "tflops": round(tf, 2), "peak": MFMA_BF16_PEAK_TFLOPS, "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
+            "decode_us": round(dc5 * 1e3, 2), "decode_gbs": round(dec_gbs, 1), "copy_append_us": round(ca5 * 1e3, 2),
+        }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a sample")
+        result["cpu_baseline"] = cpu_baseline(wl)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,196 @@
+/*
+ * pagedattn.h — C ABI of the paged KV-cache attention library (gfx950).
+ *
+ * The operation (PagedAttention, as the pages describe it): the KV cache is
+ * cut into fixed-size physical blocks of `block_size` token slots drawn from
+ * one global pool; each sequence keeps a block table mapping its logical
+ * blocks to physical ones; decode appends the current token's K/V to the
+ * cache and then attends over the whole context read block by block through
+ * the table; chunked prefill attends a chunk of new tokens causally over the
+ * cached context plus itself; identical prefixes share read-only blocks and
+ * are copied on write.  Sources: lshu.cn/news/11644, "方案：页式内存管理",
+ * "收益分析" and "性能关键路径与瓶颈"; zzmblog.top vLLM guide,
+ * "Transformer推理与KV缓存" and "PagedAttention核心设计"; 5x10.cn/post/462,
+ * "分块预填充".
+ *
+ * Conventions for every call
+ *  - Pointers marked "device" are HIP device (or managed) memory; "host"
+ *    pointers are ordinary CPU memory.  The caller owns every buffer; the
+ *    library keeps no pointer after a call returns and allocates nothing.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *    Device calls are asynchronous on that stream; a call returns once its
+ *    kernels are enqueued.  Calls hold no global state and may be issued
+ *    from several host threads.
+ *  - Arguments the host can see are validated before anything is launched:
+ *    PA_EINVAL (bad pointer/size/range), PA_EUNSUPPORTED (a shape outside
+ *    the compiled instances), PA_EWORKSPACE (workspace too small).  Then
+ *    nothing is enqueued.  PA_EHIP reports a failed launch.
+ *  - Device-resident metadata (slot ids, block tables, context lengths,
+ *    copy pairs) is trusted: values outside their range are skipped by the
+ *    kernels (never dereferenced), which leaves the result undefined for
+ *    that token/sequence but does not fault.
+ *  - Compiled instances: dtype {f32, f16, bf16} x head_dim {64, 128} x
+ *    block_size {16, 32}; num_q_heads a multiple of num_kv_heads with group
+ *    size num_q_heads/num_kv_heads in {1, 2, 4, 8}.  pa_prefill_chunk needs
+ *    f16 or bf16 (its contractions run on the matrix cores).
+ */
+#ifndef PAGEDATTN_H
+#define PAGEDATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { PA_F32 = 0, PA_F16 = 1, PA_BF16 = 2 } pa_dtype;
+
+typedef enum {
+  PA_OK = 0,
+  PA_EINVAL = 1,
+  PA_EUNSUPPORTED = 2,
+  PA_EWORKSPACE = 3,
+  PA_ENOMEM = 4, /* block manager: the free pool cannot cover the request */
+  PA_EHIP = 5
+} pa_status;
+
+/* The paged pool.  k_cache and v_cache are separate device arrays, each
+ * [num_blocks][num_kv_heads][block_size][head_dim] row-major in `dtype`
+ * (the pages leave the layout open; one (block, head) tile is one
+ * contiguous block_size x head_dim slab).  Token slot s lives at block
+ * s / block_size, row s % block_size. */
+typedef struct {
+  void* k_cache;
+  void* v_cache;
+  int32_t num_blocks;
+  int32_t num_kv_heads;
+  int32_t block_size;
+  int32_t head_dim;
+  int32_t dtype; /* pa_dtype */
+} pa_cache;
+
+/* Write new tokens' K/V into their cache slots (decode appends the current
+ * token before attending: zzmblog.top vLLM guide, "Transformer推理与KV缓存";
+ * lshu.cn/news/11644, "方案：页式内存管理", the append rule).
+ *   k_new, v_new  device [num_tokens][num_kv_heads][head_dim], cache dtype
+ *   slot_mapping  device int64 [num_tokens]; slot < 0 skips the token
+ * Slots of one call must be distinct. */
+int pa_kv_append(const pa_cache* cache, const void* k_new, const void* v_new,
+                 const int64_t* slot_mapping, int32_t num_tokens, void* stream);
+
+/* Copy-on-write of shared prefix blocks (lshu.cn/news/11644, "收益分析":
+ * identical prompts share read-only physical blocks; a later divergence is
+ * handled by copy-on-write).  For each pair (src, dst), in order, the whole
+ * K and V tiles of block src (all heads, all slots) are copied to block dst.
+ *   pairs  device int32 [num_pairs][2] = (src, dst)
+ * A dst must not appear as a src or dst of another pair of the same call. */
+int pa_copy_blocks(const pa_cache* cache, const int32_t* pairs, int32_t num_pairs, void* stream);
+
+/* Bytes of device workspace pa_decode needs for split-K partitions
+ * (0 when partition_size == 0). */
+size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                                 int32_t max_context_len, int32_t partition_size);
+
+/* Paged decode attention: one query token per sequence attends over its
+ * whole context read through its block table (lshu.cn/news/11644,
+ * "方案：页式内存管理": the kernel reads the scattered blocks of a request
+ * through its block table as one logical K/V sequence; "性能关键路径与瓶颈":
+ * decode is bound by reading the KV cache).
+ *   q, out          device [num_seqs][num_q_heads][head_dim], cache dtype;
+ *                   q head h reads KV head h / (num_q_heads / num_kv_heads)
+ *   block_tables    device int32 [num_seqs][max_blocks_per_seq]
+ *   context_lens    device int32 [num_seqs]; counts the token appended this
+ *                   step; 0 gives a zero output row
+ *   max_context_len host bound on every context_lens entry
+ *                   (<= max_blocks_per_seq * block_size)
+ *   scale           softmax scale (usually 1/sqrt(head_dim))
+ *   partition_size  0 = one pass per (sequence, KV head); otherwise a
+ *                   multiple of block_size: the context is split into
+ *                   partitions of that many tokens whose softmax states are
+ *                   merged by log-sum-exp in a second kernel; -1 lets the
+ *                   library choose from the shape
+ *   workspace       device scratch of at least pa_decode_workspace_bytes()
+ *                   for the partition size actually used (may be NULL when
+ *                   that is 0); for -1, size it with the largest
+ *                   pa_decode_workspace_bytes over the choices, or query
+ *                   pa_decode_choose_partition first
+ * Output is rounded to the cache dtype (round to nearest even). */
+int pa_decode(const pa_cache* cache, const void* q, void* out, int32_t num_seqs, int32_t num_q_heads,
+              const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
+              int32_t max_context_len, float scale, int32_t partition_size, void* workspace,
+              size_t workspace_bytes, void* stream);
+
+/* The partition size pa_decode uses for partition_size == -1 (host only). */
+int32_t pa_decode_choose_partition(const pa_cache* cache, int32_t num_seqs, int32_t num_q_heads,
+                                   int32_t max_context_len);
+
+/* Chunked-prefill attention (5x10.cn/post/462, "分块预填充"; lshu.cn/news/11644,
+ * "整体架构": long prompts are split into chunks over several iterations and
+ * batched with decode tokens).  Sequence s has n_s = cu_q_lens[s+1] -
+ * cu_q_lens[s] query rows, already appended to its cache, so its context has
+ * context_lens[s] >= n_s tokens; row i sits at position
+ * context_lens[s] - n_s + i and attends keys 0..that position (causal).
+ *   q, out        device [total_q][num_q_heads][head_dim], f16 or bf16
+ *   cu_q_lens     device int32 [num_seqs + 1], cu_q_lens[0] = 0,
+ *                 cu_q_lens[num_seqs] = total_q
+ *   context_lens  device int32 [num_seqs]
+ *   max_q_len, max_context_len  host bounds of n_s and context_lens */
+int pa_prefill_chunk(const pa_cache* cache, const void* q, void* out, const int32_t* cu_q_lens,
+                     const int32_t* context_lens, int32_t num_seqs, int32_t total_q, int32_t num_q_heads,
+                     const int32_t* block_tables, int32_t max_blocks_per_seq, int32_t max_q_len,
+                     int32_t max_context_len, float scale, void* stream);
+
+const char* pa_status_str(int status);
+
+/* ---- host block manager (CPU only, no HIP calls) -------------------------
+ * Bookkeeping of the paged cache (lshu.cn/news/11644, "方案：页式内存管理" and
+ * "收益分析"): one global pool; a FIFO free pool (blocks handed out from the
+ * front, returned to the back); a per-sequence block table; a new block only
+ * when the last one is full; all blocks returned when a sequence is freed;
+ * forks share the parent's blocks read-only with reference counts, and the
+ * first write into a block held by more than one sequence first moves the
+ * writer to a fresh block and emits a (shared, fresh) copy pair.
+ * Sequence ids are caller-chosen int32 values.  Not thread-safe per handle. */
+typedef struct pa_bm pa_bm;
+
+/* free_order: host int32 [free_len], the pool's initial free list, front
+ * first; blocks not listed are never handed out (e.g. a poison block that
+ * table padding points at).  NULL = 0..num_blocks-1.  Returns NULL on bad
+ * arguments. */
+pa_bm* pa_bm_create(int32_t num_blocks, int32_t block_size, const int32_t* free_order, int32_t free_len);
+void pa_bm_destroy(pa_bm* bm);
+int pa_bm_add_seq(pa_bm* bm, int32_t seq);
+/* child shares parent's first ceil(keep/block_size) blocks; keep <= parent length */
+int pa_bm_fork(pa_bm* bm, int32_t parent, int32_t child, int32_t keep);
+/* Grow `seq` by n_tokens: slots_out host int64 [n_tokens]; cow_pairs_out
+ * host int32 [cow_cap][2]; *n_cow_out pairs written.  All-or-nothing:
+ * PA_ENOMEM leaves the state unchanged. */
+int pa_bm_append(pa_bm* bm, int32_t seq, int32_t n_tokens, int64_t* slots_out, int32_t* cow_pairs_out,
+                 int32_t cow_cap, int32_t* n_cow_out);
+/* pa_bm_append for num_seqs sequences in order, slots concatenated in that
+ * order (the step's slot mapping) and copy pairs concatenated.  Stops at the
+ * first failure; *n_done_out tells how many sequences were appended. */
+int pa_bm_append_batch(pa_bm* bm, const int32_t* seqs, const int32_t* n_tokens, int32_t num_seqs,
+                       int64_t* slots_out, int32_t* cow_pairs_out, int32_t cow_cap, int32_t* n_cow_out,
+                       int32_t* n_done_out);
+int pa_bm_free_seq(pa_bm* bm, int32_t seq);
+/* Table of one sequence: out host int32 [cap]; *len_out = blocks held. */
+int pa_bm_table(const pa_bm* bm, int32_t seq, int32_t* out, int32_t cap, int32_t* len_out);
+/* Padded tables of several sequences: out host int32 [num_seqs][max_blocks],
+ * entries past a table's end set to pad_block; lens_out host int32
+ * [num_seqs] (may be NULL) receives the sequences' token counts. */
+int pa_bm_tables(const pa_bm* bm, const int32_t* seqs, int32_t num_seqs, int32_t* out, int32_t max_blocks,
+                 int32_t pad_block, int32_t* lens_out);
+int pa_bm_seq_len(const pa_bm* bm, int32_t seq, int32_t* len_out);
+int32_t pa_bm_num_free(const pa_bm* bm);
+/* The free list front first: out host int32 [cap]; returns entries written. */
+int32_t pa_bm_free_list(const pa_bm* bm, int32_t* out, int32_t cap);
+/* Reference count of a block (0 when free or never handed out). */
+int32_t pa_bm_refcount(const pa_bm* bm, int32_t block);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDATTN_H */

@@ -1,0 +1,202 @@
+// C ABI of the paged KV-cache attention library: argument validation, launch
+// configuration, workspace sizing and error mapping.  Every check that needs
+// only host-visible values runs before anything is enqueued.
+#include <cmath>
+#include <cstdint>
+
+#include "launch.h"
+#include "pagedattn.h"
+
+namespace {
+
+constexpr int32_t kMaxGridYZ = 65535;
+
+int elem_bytes(int32_t dtype) { return dtype == PA_F32 ? 4 : 2; }
+
+// Validate the pool descriptor.
+int check_cache(const pa_cache* c) {
+  if (!c || !c->k_cache || !c->v_cache) return PA_EINVAL;
+  if (c->num_blocks <= 0 || c->num_kv_heads <= 0 || c->block_size <= 0 || c->head_dim <= 0) return PA_EINVAL;
+  if (c->dtype != PA_F32 && c->dtype != PA_F16 && c->dtype != PA_BF16) return PA_EINVAL;
+  if (c->head_dim != 64 && c->head_dim != 128) return PA_EUNSUPPORTED;
+  if (c->block_size != 16 && c->block_size != 32) return PA_EUNSUPPORTED;
+  if (c->num_kv_heads > kMaxGridYZ) return PA_EUNSUPPORTED;
+  return PA_OK;
+}
+
+int check_group(const pa_cache* c, int32_t num_q_heads, int32_t* group) {
+  if (num_q_heads <= 0 || num_q_heads % c->num_kv_heads != 0) return PA_EINVAL;
+  const int32_t g = num_q_heads / c->num_kv_heads;
+  if (g != 1 && g != 2 && g != 4 && g != 8) return PA_EUNSUPPORTED;
+  *group = g;
+  return PA_OK;
+}
+
+int check_scale(float scale) { return (std::isfinite(scale) && scale > 0.f) ? PA_OK : PA_EINVAL; }
+
+int hip_status(hipError_t e) { return e == hipSuccess ? PA_OK : PA_EHIP; }
+
+int32_t round_up(int32_t x, int32_t m) { return (x + m - 1) / m * m; }
+
+// Tokens per partition actually used for a requested partition_size.
+int32_t effective_partition(int32_t requested, int32_t block_size, int32_t max_context_len, int32_t chosen) {
+  const int32_t p = requested == -1 ? chosen : requested;
+  if (p == 0) return round_up(max_context_len > 0 ? max_context_len : 1, block_size);
+  return p;
+}
+
+size_t workspace_for(int64_t num_seqs, int64_t num_q_heads, int64_t head_dim, int64_t num_parts) {
+  if (num_parts <= 1) return 0;
+  return static_cast<size_t>(num_seqs * num_q_heads * num_parts * (head_dim + 2) * sizeof(float));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pa_status_str(int status) {
+  switch (status) {
+    case PA_OK: return "ok";
+    case PA_EINVAL: return "invalid argument";
+    case PA_EUNSUPPORTED: return "unsupported shape or dtype";
+    case PA_EWORKSPACE: return "workspace too small";
+    case PA_ENOMEM: return "block pool exhausted";
+    case PA_EHIP: return "HIP launch failed";
+  }
+  return "unknown status";
+}
+
+int pa_kv_append(const pa_cache* cache, const void* k_new, const void* v_new, const int64_t* slot_mapping,
+                 int32_t num_tokens, void* stream) {
+  int rc = check_cache(cache);
+  if (rc != PA_OK) return rc;
+  if (num_tokens < 0) return PA_EINVAL;
+  if (num_tokens == 0) return PA_OK;
+  if (!k_new || !v_new || !slot_mapping) return PA_EINVAL;
+  return hip_status(pa::launch_kv_append(k_new, v_new, slot_mapping, num_tokens, cache->k_cache, cache->v_cache,
+                                         cache->num_blocks, cache->num_kv_heads, cache->block_size, cache->head_dim,
+                                         elem_bytes(cache->dtype), static_cast<hipStream_t>(stream)));
+}
+
+int pa_copy_blocks(const pa_cache* cache, const int32_t* pairs, int32_t num_pairs, void* stream) {
+  int rc = check_cache(cache);
+  if (rc != PA_OK) return rc;
+  if (num_pairs < 0) return PA_EINVAL;
+  if (num_pairs == 0) return PA_OK;
+  if (!pairs) return PA_EINVAL;
+  const int64_t block_bytes = static_cast<int64_t>(cache->num_kv_heads) * cache->block_size * cache->head_dim *
+                              elem_bytes(cache->dtype);
+  return hip_status(pa::launch_copy_blocks(pairs, num_pairs, cache->k_cache, cache->v_cache, cache->num_blocks,
+                                           block_bytes, static_cast<hipStream_t>(stream)));
+}
+
+int32_t pa_decode_choose_partition(const pa_cache* cache, int32_t num_seqs, int32_t num_q_heads,
+                                   int32_t max_context_len) {
+  (void)num_q_heads;
+  if (!cache || cache->num_kv_heads <= 0) return 0;
+  const int64_t units = static_cast<int64_t>(num_seqs) * cache->num_kv_heads;
+  // one pass when the batch alone fills the chip several times over and
+  // contexts are short; otherwise 512-token partitions
+  if (units >= 2048 && max_context_len <= 2048) return 0;
+  return max_context_len > 512 ? 512 : 0;
+}
+
+size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim, int32_t max_context_len,
+                                 int32_t partition_size) {
+  if (num_seqs <= 0 || num_q_heads <= 0 || head_dim <= 0 || max_context_len <= 0) return 0;
+  // -1: the chooser never picks partitions shorter than 512 tokens
+  const int32_t p = partition_size == -1 ? 512 : partition_size;
+  if (p <= 0) return 0;
+  const int64_t parts = (static_cast<int64_t>(max_context_len) + p - 1) / p;
+  return workspace_for(num_seqs, num_q_heads, head_dim, parts);
+}
+
+int pa_decode(const pa_cache* cache, const void* q, void* out, int32_t num_seqs, int32_t num_q_heads,
+              const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
+              int32_t max_context_len, float scale, int32_t partition_size, void* workspace, size_t workspace_bytes,
+              void* stream) {
+  int rc = check_cache(cache);
+  if (rc != PA_OK) return rc;
+  int32_t group = 0;
+  if ((rc = check_group(cache, num_q_heads, &group)) != PA_OK) return rc;
+  if ((rc = check_scale(scale)) != PA_OK) return rc;
+  if (num_seqs < 0 || max_blocks_per_seq <= 0 || max_context_len < 0) return PA_EINVAL;
+  if (static_cast<int64_t>(max_context_len) > static_cast<int64_t>(max_blocks_per_seq) * cache->block_size)
+    return PA_EINVAL;
+  if (num_seqs > kMaxGridYZ) return PA_EUNSUPPORTED;
+  if (partition_size < -1) return PA_EINVAL;
+  if (partition_size > 0 && partition_size % cache->block_size != 0) return PA_EINVAL;
+  if (num_seqs == 0) return PA_OK;
+  if (!q || !out || !block_tables || !context_lens) return PA_EINVAL;
+  const int32_t chosen = pa_decode_choose_partition(cache, num_seqs, num_q_heads, max_context_len);
+  const int32_t part_tokens = effective_partition(partition_size, cache->block_size, max_context_len, chosen);
+  const int32_t num_parts = max_context_len > 0 ? (max_context_len + part_tokens - 1) / part_tokens : 1;
+  const size_t need = workspace_for(num_seqs, num_q_heads, cache->head_dim, num_parts);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return PA_EWORKSPACE;
+
+  pa::DecodeArgs a{};
+  a.q = q;
+  a.out = out;
+  a.k_cache = cache->k_cache;
+  a.v_cache = cache->v_cache;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.ws_ml = need > 0 ? static_cast<float*>(workspace) : nullptr;
+  a.ws_o = need > 0 ? a.ws_ml + static_cast<int64_t>(num_seqs) * num_q_heads * num_parts * 2 : nullptr;
+  a.scale = scale;
+  a.dtype = cache->dtype;
+  a.head_dim = cache->head_dim;
+  a.block_size = cache->block_size;
+  a.group = group;
+  a.num_seqs = num_seqs;
+  a.num_kv_heads = cache->num_kv_heads;
+  a.num_blocks = cache->num_blocks;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.max_context_len = max_context_len;
+  a.part_tokens = part_tokens;
+  a.num_parts = num_parts;
+  return hip_status(pa::launch_decode(a, static_cast<hipStream_t>(stream)));
+}
+
+int pa_prefill_chunk(const pa_cache* cache, const void* q, void* out, const int32_t* cu_q_lens,
+                     const int32_t* context_lens, int32_t num_seqs, int32_t total_q, int32_t num_q_heads,
+                     const int32_t* block_tables, int32_t max_blocks_per_seq, int32_t max_q_len,
+                     int32_t max_context_len, float scale, void* stream) {
+  int rc = check_cache(cache);
+  if (rc != PA_OK) return rc;
+  if (cache->dtype == PA_F32) return PA_EUNSUPPORTED;
+  int32_t group = 0;
+  if ((rc = check_group(cache, num_q_heads, &group)) != PA_OK) return rc;
+  if ((rc = check_scale(scale)) != PA_OK) return rc;
+  if (num_seqs < 0 || total_q < 0 || max_q_len < 0 || max_context_len < 0 || max_blocks_per_seq <= 0)
+    return PA_EINVAL;
+  if (max_q_len > max_context_len) return PA_EINVAL;
+  if (static_cast<int64_t>(max_context_len) > static_cast<int64_t>(max_blocks_per_seq) * cache->block_size)
+    return PA_EINVAL;
+  if (num_seqs > kMaxGridYZ) return PA_EUNSUPPORTED;
+  if (num_seqs == 0 || total_q == 0 || max_q_len == 0) return PA_OK;
+  if (!q || !out || !cu_q_lens || !context_lens || !block_tables) return PA_EINVAL;
+  pa::PrefillArgs a{};
+  a.q = q;
+  a.out = out;
+  a.k_cache = cache->k_cache;
+  a.v_cache = cache->v_cache;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.cu_q_lens = cu_q_lens;
+  a.scale = scale;
+  a.dtype = cache->dtype;
+  a.head_dim = cache->head_dim;
+  a.block_size = cache->block_size;
+  a.group = group;
+  a.num_seqs = num_seqs;
+  a.total_q = total_q;
+  a.num_kv_heads = cache->num_kv_heads;
+  a.num_blocks = cache->num_blocks;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.max_q_len = max_q_len;
+  a.max_context_len = max_context_len;
+  return hip_status(pa::launch_prefill(a, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,112 @@
+// Data movement into the paged pool: token append through a slot mapping,
+// and whole-block copies for copy-on-write.
+//
+// Append (zzmblog.top vLLM guide, "Transformer推理与KV缓存"; lshu.cn/news/11644,
+// "方案：页式内存管理"): token t's K and V rows ([num_kv_heads][head_dim]) go
+// to block slot_mapping[t] / block_size, row slot_mapping[t] % block_size of
+// every head's tile.  Copy (lshu.cn/news/11644, "收益分析"): a shared block
+// about to be written is duplicated whole into a fresh block first.
+//
+// Pool layout: K tiles are [block_size][head_dim] (token rows), V tiles are
+// [head_dim][block_size] (V kept transposed inside each block, so the PV
+// contraction reads keys contiguously).  Both are HBM streams: each thread
+// moves one 16-byte chunk of a source row; a wavefront reads 1 KiB of
+// consecutive source bytes per instruction.
+#include "common.h"
+#include "launch.h"
+
+namespace pa {
+
+namespace {
+
+// One thread per 16-byte chunk of a (token, head) row; grid-stride.  The K
+// chunk is stored whole; the V chunk's elements go to VEC rows of the
+// transposed V tile, block_size elements apart.
+template <typename E>
+__global__ __launch_bounds__(256) void kv_append_kernel(const u32x4* __restrict__ k_new,
+                                                        const u32x4* __restrict__ v_new,
+                                                        const int64_t* __restrict__ slots, int64_t total_chunks,
+                                                        int chunks_per_row, int num_kv_heads, int block_size,
+                                                        int64_t num_slots, u32x4* __restrict__ kc,
+                                                        E* __restrict__ vc) {
+  constexpr int VEC = 16 / sizeof(E);
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < total_chunks;
+       i += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+    const int c = static_cast<int>(i % chunks_per_row);
+    const int64_t th = i / chunks_per_row;  // token * heads + head
+    const int h = static_cast<int>(th % num_kv_heads);
+    const int64_t t = th / num_kv_heads;
+    const int64_t slot = slots[t];
+    if (slot < 0 || slot >= num_slots) continue;
+    const int64_t blk = slot / block_size;
+    const int64_t off = slot % block_size;
+    const int64_t tile = blk * num_kv_heads + h;  // (block, head) tile index
+    kc[(tile * block_size + off) * chunks_per_row + c] = k_new[i];
+    const u32x4 v = v_new[i];
+    E e[VEC];
+    __builtin_memcpy(e, &v, 16);
+    const int64_t d0 = static_cast<int64_t>(c) * VEC;
+    E* vt = vc + (tile * (chunks_per_row * VEC) + d0) * block_size + off;
+#pragma unroll
+    for (int k = 0; k < VEC; ++k) vt[static_cast<int64_t>(k) * block_size] = e[k];
+  }
+}
+
+// blockIdx.y = pair; the block's tiles are copied as 16-byte chunks.
+__global__ __launch_bounds__(256) void copy_blocks_kernel(const int32_t* __restrict__ pairs, int num_blocks,
+                                                          int64_t chunks_per_block, u32x4* __restrict__ kc,
+                                                          u32x4* __restrict__ vc) {
+  const int p = blockIdx.y;
+  const int src = pairs[2 * p], dst = pairs[2 * p + 1];
+  if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks) return;
+  const u32x4* ks = kc + src * chunks_per_block;
+  const u32x4* vs = vc + src * chunks_per_block;
+  u32x4* kd = kc + dst * chunks_per_block;
+  u32x4* vd = vc + dst * chunks_per_block;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < chunks_per_block;
+       i += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+    kd[i] = ks[i];
+    vd[i] = vs[i];
+  }
+}
+
+}  // namespace
+
+hipError_t launch_kv_append(const void* k_new, const void* v_new, const int64_t* slots, int32_t num_tokens,
+                            void* k_cache, void* v_cache, int32_t num_blocks, int32_t num_kv_heads,
+                            int32_t block_size, int32_t head_dim, int32_t elem_bytes, hipStream_t st) {
+  const int chunks_per_row = head_dim * elem_bytes / 16;
+  const int64_t total = static_cast<int64_t>(num_tokens) * num_kv_heads * chunks_per_row;
+  if (total == 0) return hipSuccess;
+  const int64_t want = (total + 255) / 256;
+  const int grid = static_cast<int>(want < 8192 ? want : 8192);
+  const int64_t num_slots = static_cast<int64_t>(num_blocks) * block_size;
+  if (elem_bytes == 4) {
+    hipLaunchKernelGGL(kv_append_kernel<uint32_t>, dim3(grid), dim3(256), 0, st, static_cast<const u32x4*>(k_new),
+                       static_cast<const u32x4*>(v_new), slots, total, chunks_per_row, num_kv_heads, block_size,
+                       num_slots, static_cast<u32x4*>(k_cache), static_cast<uint32_t*>(v_cache));
+  } else {
+    hipLaunchKernelGGL(kv_append_kernel<uint16_t>, dim3(grid), dim3(256), 0, st, static_cast<const u32x4*>(k_new),
+                       static_cast<const u32x4*>(v_new), slots, total, chunks_per_row, num_kv_heads, block_size,
+                       num_slots, static_cast<u32x4*>(k_cache), static_cast<uint16_t*>(v_cache));
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_copy_blocks(const int32_t* pairs, int32_t num_pairs, void* k_cache, void* v_cache,
+                              int32_t num_blocks, int64_t block_bytes, hipStream_t st) {
+  if (num_pairs == 0) return hipSuccess;
+  const int64_t chunks = block_bytes / 16;
+  const int64_t want = (chunks + 255) / 256;
+  const int gx = static_cast<int>(want < 16 ? want : 16);
+  for (int32_t p0 = 0; p0 < num_pairs; p0 += 65535) {
+    const int32_t np = num_pairs - p0 < 65535 ? num_pairs - p0 : 65535;
+    hipLaunchKernelGGL(copy_blocks_kernel, dim3(gx, np), dim3(256), 0, st, pairs + 2 * static_cast<int64_t>(p0),
+                       num_blocks, chunks, static_cast<u32x4*>(k_cache), static_cast<u32x4*>(v_cache));
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+}  // namespace pa

@@ -1,0 +1,52 @@
+// Internal launch interface between the C ABI layer (api.hip) and the
+// kernels.  Arguments arrive here already validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pa {
+
+struct DecodeArgs {
+  const void* q;
+  void* out;
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  float* ws_ml;  // [S][Hq][num_parts][2]  (max in log2 units, sum of weights)
+  float* ws_o;   // [S][Hq][num_parts][D]  normalised partial outputs
+  float scale;
+  int32_t dtype, head_dim, block_size, group;
+  int32_t num_seqs, num_kv_heads, num_blocks, max_blocks_per_seq;
+  int32_t max_context_len;  // host bound; device lengths are clamped to it
+  int32_t part_tokens;  // tokens per partition (multiple of block_size)
+  int32_t num_parts;    // ceil(max_context_len / part_tokens)
+};
+
+struct PrefillArgs {
+  const void* q;
+  void* out;
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  const int32_t* cu_q_lens;
+  float scale;
+  int32_t dtype, head_dim, block_size, group;
+  int32_t num_seqs, total_q, num_kv_heads, num_blocks, max_blocks_per_seq;
+  int32_t max_q_len, max_context_len;
+};
+
+hipError_t launch_kv_append(const void* k_new, const void* v_new, const int64_t* slots, int32_t num_tokens,
+                            void* k_cache, void* v_cache, int32_t num_blocks, int32_t num_kv_heads,
+                            int32_t block_size, int32_t head_dim, int32_t elem_bytes, hipStream_t st);
+
+hipError_t launch_copy_blocks(const int32_t* pairs, int32_t num_pairs, void* k_cache, void* v_cache,
+                              int32_t num_blocks, int64_t block_bytes, hipStream_t st);
+
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t st);
+
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st);
+
+}  // namespace pa

@@ -202,25 +202,52 @@ def round_to_storage(x: np.ndarray, dtype: str) -> np.ndarray:
     raise ValueError(dtype)
 
 
+def _round_fast(x: np.ndarray, dtype: str) -> np.ndarray:
+    """Same rounding as round_to_storage, through torch's multi-threaded casts."""
+    if dtype == "f32":
+        return x
+    import torch
+
+    t = torch.from_numpy(x)
+    if dtype == "f16":
+        return t.to(torch.float16).numpy()
+    return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def _threads(threads=None):
+    return threads or min(16, len(os.sched_getaffinity(0)))
+
+
+def normal_values_many(requests, dtype: str, threads: int | None = None):
+    """N(0,1) fp32 draws for several streams at once: requests is a list of
+    (key, shape); each stream is filled in fixed-size chunks, chunk c from the
+    seed (key..., c), so values do not depend on the thread count."""
+    outs, jobs = [], []
+    for key, shape in requests:
+        n = int(np.prod(shape))
+        buf = np.empty(n, dtype=np.float32)
+        outs.append((buf, shape))
+        for c in range((n + _CHUNK - 1) // _CHUNK):
+            jobs.append((key, c, buf, c * _CHUNK, min(n, (c + 1) * _CHUNK)))
+
+    def fill(job):
+        key, c, buf, a, b = job
+        g = np.random.default_rng(np.random.SeedSequence(list(key) + [c]))
+        g.standard_normal(b - a, dtype=np.float32, out=buf[a:b])
+
+    nt = _threads(threads)
+    if len(jobs) > 1 and nt > 1:
+        with ThreadPoolExecutor(nt) as ex:
+            list(ex.map(fill, jobs))
+    else:
+        for j in jobs:
+            fill(j)
+    return [_round_fast(buf, dtype).reshape(shape) for buf, shape in outs]
+
+
 def normal_values(key: tuple, shape, dtype: str, threads: int | None = None) -> np.ndarray:
     """N(0,1) fp32 draws for the stream `key`, rounded to `dtype`."""
-    n = int(np.prod(shape))
-    out = np.empty(n, dtype=np.float32)
-    chunks = [(c, c * _CHUNK, min(n, (c + 1) * _CHUNK)) for c in range((n + _CHUNK - 1) // _CHUNK)]
-
-    def fill(item):
-        c, a, b = item
-        g = np.random.default_rng(np.random.SeedSequence(list(key) + [c]))
-        g.standard_normal(b - a, dtype=np.float32, out=out[a:b])
-
-    nt = threads or min(16, len(os.sched_getaffinity(0)))
-    if len(chunks) > 1 and nt > 1:
-        with ThreadPoolExecutor(nt) as ex:
-            list(ex.map(fill, chunks))
-    else:
-        for it in chunks:
-            fill(it)
-    return round_to_storage(out, dtype).reshape(shape)
+    return normal_values_many([(key, shape)], dtype, threads)[0]
 
 
 def _stream(cfg_key, *parts):
@@ -232,15 +259,22 @@ def synthesize(spec: Spec, plans: list, cfg_key: tuple, notes=None) -> Workload:
     H, D = spec.num_kv_heads, spec.head_dim
     g = np.random.default_rng(np.random.SeedSequence(list(_stream(cfg_key, 1))))
     free_order = g.permutation(spec.num_blocks - 1).astype(np.int32)
-    own_k, own_v, q = {}, {}, {}
+    reqs, slots = [], []
     for p in plans:
         n_own = p.context_len - p.keep
-        own_k[p.seq_id] = normal_values(_stream(cfg_key, 2, p.seq_id), (n_own, H, D), spec.dtype)
-        own_v[p.seq_id] = normal_values(_stream(cfg_key, 3, p.seq_id), (n_own, H, D), spec.dtype)
+        reqs.append((_stream(cfg_key, 2, p.seq_id), (n_own, H, D)))
+        slots.append(("k", p.seq_id))
+        reqs.append((_stream(cfg_key, 3, p.seq_id), (n_own, H, D)))
+        slots.append(("v", p.seq_id))
     for p in plans:
         if p.in_batch:
-            q[p.seq_id] = normal_values(_stream(cfg_key, 4, p.seq_id),
-                                        (p.n_new, spec.num_q_heads, D), spec.dtype)
+            reqs.append((_stream(cfg_key, 4, p.seq_id), (p.n_new, spec.num_q_heads, D)))
+            slots.append(("q", p.seq_id))
+    vals = normal_values_many(reqs, spec.dtype)
+    own_k, own_v, q = {}, {}, {}
+    dst = {"k": own_k, "v": own_v, "q": q}
+    for (kind, sid), arr in zip(slots, vals):
+        dst[kind][sid] = arr
     return Workload(spec, plans, free_order, own_k, own_v, q, seed=tuple(cfg_key), notes=notes or {})
 
 
