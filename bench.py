@@ -41,7 +41,7 @@ def decode_bytes(lens, num_q_heads, num_kv_heads, head_dim, block_size, eb):
     kv = int(lens.sum()) * num_kv_heads * head_dim * eb * 2
     qo = len(lens) * num_q_heads * head_dim * eb * 2
     meta = int(((lens + block_size - 1) // block_size).sum()) * 4 + len(lens) * 4
-    return kv + qo + meta, kv
+    return int(kv + qo + meta), int(kv)
 
 
 def prefill_flops(cached, n_new, num_q_heads, head_dim):
@@ -49,6 +49,7 @@ def prefill_flops(cached, n_new, num_q_heads, head_dim):
     on C cached tokens, Hq * 4 * D * (n*C + n(n+1)/2)."""
     tot = 0
     for c, n in zip(cached, n_new):
+        c, n = int(c), int(n)
         tot += num_q_heads * 4 * head_dim * (n * c + n * (n + 1) // 2)
     return tot
 
@@ -91,7 +92,7 @@ class Step:
             self.max_dec = int(self.plan.host_lens[dec].max())
             wsb = P.pa_decode_workspace_bytes(len(dec), sp.num_q_heads, sp.head_dim, self.max_dec, partition_size)
             self.ws = torch.empty(max(wsb, 4), dtype=torch.uint8, device=device) if wsb else None
-            self.part_used = (P.pa_decode_choose_partition(self.cache.desc, len(dec), sp.num_q_heads, self.max_dec)
+            self.part_used = int(P.pa_decode_choose_partition(self.cache.desc, len(dec), sp.num_q_heads, self.max_dec)
                               if partition_size == -1 else partition_size)
             self.dec_bytes, self.dec_kv_bytes = decode_bytes(self.plan.host_lens[dec], sp.num_q_heads,
                                                              sp.num_kv_heads, sp.head_dim, sp.block_size,

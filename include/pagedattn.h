@@ -26,9 +26,10 @@
  *    the compiled instances), PA_EWORKSPACE (workspace too small).  Then
  *    nothing is enqueued.  PA_EHIP reports a failed launch.
  *  - Device-resident metadata (slot ids, block tables, context lengths,
- *    copy pairs) is trusted: values outside their range are skipped by the
- *    kernels (never dereferenced), which leaves the result undefined for
- *    that token/sequence but does not fault.
+ *    copy pairs) is trusted, but never used as an address when out of range:
+ *    such slots and copy pairs are skipped, such block ids replaced by block
+ *    0 and lengths clamped to the host bounds; the result for that
+ *    token/sequence is then undefined, and nothing faults.
  *  - Compiled instances: dtype {f32, f16, bf16} x head_dim {64, 128} x
  *    block_size {16, 32}; num_q_heads a multiple of num_kv_heads with group
  *    size num_q_heads/num_kv_heads in {1, 2, 4, 8}.  pa_prefill_chunk needs
@@ -55,11 +56,12 @@ typedef enum {
   PA_EHIP = 5
 } pa_status;
 
-/* The paged pool.  k_cache and v_cache are separate device arrays, each
- * [num_blocks][num_kv_heads][block_size][head_dim] row-major in `dtype`
- * (the pages leave the layout open; one (block, head) tile is one
- * contiguous block_size x head_dim slab).  Token slot s lives at block
- * s / block_size, row s % block_size. */
+/* The paged pool (the pages leave the layout open).  Two device arrays in
+ * `dtype`, each made of one contiguous tile per (block, KV head):
+ *   k_cache  [num_blocks][num_kv_heads][block_size][head_dim]  (token rows)
+ *   v_cache  [num_blocks][num_kv_heads][head_dim][block_size]  (V transposed
+ *            inside the tile, so the PV contraction reads keys contiguously)
+ * Token slot s lives in block s / block_size at position s % block_size. */
 typedef struct {
   void* k_cache;
   void* v_cache;
@@ -142,6 +144,10 @@ int pa_prefill_chunk(const pa_cache* cache, const void* q, void* out, const int3
                      int32_t max_context_len, float scale, void* stream);
 
 const char* pa_status_str(int status);
+
+/* HIP's text for the calling thread's most recent PA_EHIP ("" if none);
+ * the string is static, owned by the HIP runtime. */
+const char* pa_last_error(void);
 
 /* ---- host block manager (CPU only, no HIP calls) -------------------------
  * Bookkeeping of the paged cache (lshu.cn/news/11644, "方案：页式内存管理" and

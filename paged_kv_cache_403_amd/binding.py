@@ -23,7 +23,10 @@ PA_OK, PA_EINVAL, PA_EUNSUPPORTED, PA_EWORKSPACE, PA_ENOMEM, PA_EHIP = range(6)
 class PagedAttnError(RuntimeError):
     def __init__(self, status: int, where: str):
         self.status = status
-        super().__init__(f"{where}: {status_str(status)} (status {status})")
+        detail = ""
+        if status == PA_EHIP:
+            detail = f": {lib().pa_last_error().decode()}"
+        super().__init__(f"{where}: {status_str(status)} (status {status}){detail}")
 
 
 class pa_cache(ctypes.Structure):
@@ -54,6 +57,7 @@ _SIGNATURES = {
     "pa_prefill_chunk": (ctypes.c_int, [_cp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp, _i32, _i32, _i32,
                                         ctypes.c_float, _vp]),
     "pa_status_str": (ctypes.c_char_p, [ctypes.c_int]),
+    "pa_last_error": (ctypes.c_char_p, []),
     "pa_bm_create": (_vp, [_i32, _i32, _vp, _i32]),
     "pa_bm_destroy": (None, [_vp]),
     "pa_bm_add_seq": (ctypes.c_int, [_vp, _i32]),

@@ -34,7 +34,14 @@ int check_group(const pa_cache* c, int32_t num_q_heads, int32_t* group) {
 
 int check_scale(float scale) { return (std::isfinite(scale) && scale > 0.f) ? PA_OK : PA_EINVAL; }
 
-int hip_status(hipError_t e) { return e == hipSuccess ? PA_OK : PA_EHIP; }
+// Text of the calling thread's last HIP failure, for pa_last_error().
+thread_local const char* g_last_hip_error = "";
+
+int hip_status(hipError_t e) {
+  if (e == hipSuccess) return PA_OK;
+  g_last_hip_error = hipGetErrorString(e);
+  return PA_EHIP;
+}
 
 int32_t round_up(int32_t x, int32_t m) { return (x + m - 1) / m * m; }
 
@@ -65,6 +72,8 @@ const char* pa_status_str(int status) {
   }
   return "unknown status";
 }
+
+const char* pa_last_error(void) { return g_last_hip_error; }
 
 int pa_kv_append(const pa_cache* cache, const void* k_new, const void* v_new, const int64_t* slot_mapping,
                  int32_t num_tokens, void* stream) {

@@ -52,21 +52,26 @@ __device__ __forceinline__ typename ST::elem narrow(float x) {
 
 // fp32 dot product of one 16-byte chunk of K with the matching q chunk, added
 // to acc.  For 16-bit types q is kept packed (exact) and v_dot2 is used.
+// Vector elements are copied to scalars before __builtin_bit_cast: the
+// compiler mis-selects the element when it reinterprets an element lvalue.
 template <typename ST>
 __device__ __forceinline__ float dot16(const u32x4& qv, const u32x4& kv, float acc);
 template <>
 __device__ __forceinline__ float dot16<F16>(const u32x4& qv, const u32x4& kv, float acc) {
 #pragma unroll
-  for (int c = 0; c < 4; ++c)
-    acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, qv[c]), __builtin_bit_cast(f16x2, kv[c]), acc, false);
+  for (int c = 0; c < 4; ++c) {
+    const uint32_t a = qv[c], b = kv[c];
+    acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, a), __builtin_bit_cast(f16x2, b), acc, false);
+  }
   return acc;
 }
 template <>
 __device__ __forceinline__ float dot16<BF16>(const u32x4& qv, const u32x4& kv, float acc) {
 #pragma unroll
-  for (int c = 0; c < 4; ++c)
-    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, qv[c]), __builtin_bit_cast(bf16x2, kv[c]), acc,
-                                          false);
+  for (int c = 0; c < 4; ++c) {
+    const uint32_t a = qv[c], b = kv[c];
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), acc, false);
+  }
   return acc;
 }
 template <>

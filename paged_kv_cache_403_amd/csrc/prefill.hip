@@ -19,7 +19,11 @@
 //    consecutive keys of its own row per 16-key step, which is exactly the
 //    B-operand layout of O^T = V^T P^T -- probabilities never leave the lane;
 //  * online softmax per row in the exp2 domain (fp32 state), causal masking
-//    only on tiles that cross a row's diagonal, fully masked tiles skipped.
+//    only on tiles that cross a row's diagonal, fully masked tiles skipped;
+//  * P enters the PV contraction as two 16-bit parts (nearest value and
+//    remainder), two MFMAs per step, so the probabilities carry ~16
+//    significant bits: with bf16 outputs the output rounding then dominates
+//    the error budget.
 #include "common.h"
 #include "launch.h"
 
@@ -240,7 +244,10 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(
     const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
     m_run = m_new;
     float psum = 0.f;
-    u32x4 pb[4];  // P^T as B operand, one per 16-key step
+    // P^T as B operand, one per 16-key step: the 16-bit value nearest p and
+    // the 16-bit value nearest the remainder, so P V keeps fp32-like accuracy
+    // and the output's own rounding is the only visible error
+    u32x4 pb[4], pl[4];
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
@@ -251,8 +258,16 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(
           p[u] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[ks][a8 * 8 + u], scale_log2, -m_new));
           psum += p[u];
         }
-        pb[ks * 2 + a8] = u32x4{pack2<ST>(p[0], p[1]), pack2<ST>(p[2], p[3]), pack2<ST>(p[4], p[5]),
-                                pack2<ST>(p[6], p[7])};
+        uint32_t hi[4], lo[4];
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          hi[w] = pack2<ST>(p[2 * w], p[2 * w + 1]);
+          float h0, h1;
+          widen2<ST>(hi[w], h0, h1);
+          lo[w] = pack2<ST>(p[2 * w] - h0, p[2 * w + 1] - h1);
+        }
+        pb[ks * 2 + a8] = u32x4{hi[0], hi[1], hi[2], hi[3]};
+        pl[ks * 2 + a8] = u32x4{lo[0], lo[1], lo[2], lo[3]};
       }
     l_run = l_run * alpha + psum;
 #pragma unroll
@@ -264,6 +279,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(
       for (int ds = 0; ds < S::DSUB; ++ds) {
         const u32x4 a = *reinterpret_cast<const u32x4*>(vl + (ds * 32 + nl) * S::VPAD + kk2 * 16 + half * 8);
         o_acc[ds] = mfma32<ST>(a, pb[kk2], o_acc[ds]);
+        o_acc[ds] = mfma32<ST>(a, pl[kk2], o_acc[ds]);
       }
     }
     if (t + 1 < ntiles) stage(t + 1, buf ^ 1);
