@@ -220,6 +220,9 @@ def main():
     ap.add_argument("--partition", type=int, default=-1, help="decode partition tokens (0 one pass, -1 auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true", help="skip the chunked-prefill measurement")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB a few times (the known-size reference for "
+                         "the HBM byte counters) and exit")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)",
@@ -232,6 +235,15 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     log(f"device {torch.cuda.get_device_name(0)}")
+    if args.calibrate_copy:
+        n = args.calibrate_copy << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copied {n} bytes 3 times")
+        return
     wl = workloads.make(args.workload)
     sp = wl.spec
     st = Step(wl, args.partition)

@@ -110,13 +110,18 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t 
  *   partition_size  0 = one pass per (sequence, KV head); otherwise a
  *                   multiple of block_size: the context is split into
  *                   partitions of that many tokens whose softmax states are
- *                   merged by log-sum-exp in a second kernel; -1 lets the
- *                   library choose from the shape
+ *                   merged by log-sum-exp; -1 lets the library choose from
+ *                   the shape (pa_decode_choose_partition).  Split decode runs
+ *                   three kernels on `stream`: a one-workgroup planner lists
+ *                   the (sequence, partition) pairs that hold tokens, a
+ *                   device-sized grid walks that list, and a merge kernel
+ *                   combines each row's partitions
  *   workspace       device scratch of at least pa_decode_workspace_bytes()
  *                   for the partition size actually used (may be NULL when
- *                   that is 0); for -1, size it with the largest
- *                   pa_decode_workspace_bytes over the choices, or query
- *                   pa_decode_choose_partition first
+ *                   that is 0; for -1, pa_decode_workspace_bytes(..., -1)
+ *                   covers every choice): partial states, the work list and
+ *                   its length, all rewritten by each call, so calls that
+ *                   share a workspace must be ordered on one stream
  * Output is rounded to the cache dtype (round to nearest even). */
 int pa_decode(const pa_cache* cache, const void* q, void* out, int32_t num_seqs, int32_t num_q_heads,
               const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,

@@ -52,9 +52,12 @@ int32_t effective_partition(int32_t requested, int32_t block_size, int32_t max_c
   return p;
 }
 
+// Split-K workspace: partial softmax states [S][Hq][P][2] and outputs
+// [S][Hq][P][D] (fp32), the work list [S * P][2] and its length (int32).
 size_t workspace_for(int64_t num_seqs, int64_t num_q_heads, int64_t head_dim, int64_t num_parts) {
   if (num_parts <= 1) return 0;
-  return static_cast<size_t>(num_seqs * num_q_heads * num_parts * (head_dim + 2) * sizeof(float));
+  return static_cast<size_t>(num_seqs * num_q_heads * num_parts * (head_dim + 2) * sizeof(float) +
+                             num_seqs * num_parts * 2 * sizeof(int32_t) + 16);
 }
 
 }  // namespace
@@ -102,18 +105,25 @@ int pa_copy_blocks(const pa_cache* cache, const int32_t* pairs, int32_t num_pair
 int32_t pa_decode_choose_partition(const pa_cache* cache, int32_t num_seqs, int32_t num_q_heads,
                                    int32_t max_context_len) {
   (void)num_q_heads;
-  if (!cache || cache->num_kv_heads <= 0) return 0;
+  if (!cache || cache->num_kv_heads <= 0 || cache->block_size <= 0) return 0;
   const int64_t units = static_cast<int64_t>(num_seqs) * cache->num_kv_heads;
-  // one pass when the batch alone fills the chip several times over and
-  // contexts are short; otherwise 512-token partitions
-  if (units >= 2048 && max_context_len <= 2048) return 0;
-  return max_context_len > 512 ? 512 : 0;
+  // One pass when the batch alone fills the chip and contexts are short.
+  // Otherwise split: with many sequences (lengths likely uneven) into
+  // 512-token partitions, which balance the load; with few, into the
+  // longest partitions (up to 2048 tokens) that still give about a thousand
+  // work items, since every partition has a fixed start-up cost.
+  if (max_context_len <= 512 || (units >= 1024 && max_context_len <= 2048)) return 0;
+  if (units >= 256) return 512;
+  int32_t p = 2048;
+  while (p > 512 && units * ((max_context_len + p - 1) / p) < 1024) p /= 2;
+  return p < cache->block_size ? cache->block_size : p;
 }
 
 size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim, int32_t max_context_len,
                                  int32_t partition_size) {
   if (num_seqs <= 0 || num_q_heads <= 0 || head_dim <= 0 || max_context_len <= 0) return 0;
-  // -1: the chooser never picks partitions shorter than 512 tokens
+  // -1: the chooser never picks partitions shorter than 512 tokens (nor
+  // shorter than a block)
   const int32_t p = partition_size == -1 ? 512 : partition_size;
   if (p <= 0) return 0;
   const int64_t parts = (static_cast<int64_t>(max_context_len) + p - 1) / p;
@@ -152,6 +162,10 @@ int pa_decode(const pa_cache* cache, const void* q, void* out, int32_t num_seqs,
   a.context_lens = context_lens;
   a.ws_ml = need > 0 ? static_cast<float*>(workspace) : nullptr;
   a.ws_o = need > 0 ? a.ws_ml + static_cast<int64_t>(num_seqs) * num_q_heads * num_parts * 2 : nullptr;
+  a.ws_items = need > 0 ? reinterpret_cast<int32_t*>(a.ws_o + static_cast<int64_t>(num_seqs) * num_q_heads * num_parts *
+                                                                 cache->head_dim)
+                        : nullptr;
+  a.ws_count = need > 0 ? a.ws_items + static_cast<int64_t>(num_seqs) * num_parts * 2 : nullptr;
   a.scale = scale;
   a.dtype = cache->dtype;
   a.head_dim = cache->head_dim;

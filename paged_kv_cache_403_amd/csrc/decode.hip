@@ -29,6 +29,9 @@
 //  * the four wavefronts' states are merged in LDS; with one partition the
 //    normalised row is written in the storage type, otherwise (m, l, o) go to
 //    the workspace and a second kernel merges partitions by log-sum-exp.
+#include <algorithm>
+#include <atomic>
+
 #include "common.h"
 #include "launch.h"
 
@@ -39,6 +42,12 @@ namespace {
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr float kLog2e = 1.4426950408889634f;
+#ifndef PA_DECODE_NBUF16
+#define PA_DECODE_NBUF16 2
+#endif
+#ifndef PA_DECODE_NBUF32
+#define PA_DECODE_NBUF32 1
+#endif
 
 template <typename ST, int D, int BS, int G>
 struct DecodeShape {
@@ -51,7 +60,8 @@ struct DecodeShape {
   static constexpr int HALV = ilog2(NV / NRED);         // halving steps of the transpose
   static constexpr int LOG_G = ilog2(G);
   static constexpr int CPD = BS / VEC;  // V chunks per head_dim row
-  static constexpr bool PREFETCH = NI <= 4;
+  // register buffers of the tile pipeline (each NI 16-byte chunks of K and V)
+  static constexpr int NBUF = NI <= 4 ? PA_DECODE_NBUF16 : PA_DECODE_NBUF32;
   static_assert(LPR >= 8 && LPR <= 32 && (LPR & (LPR - 1)) == 0, "row lanes");
   static_assert(NI >= 1 && RPI * NI == BS, "tile rows");
   static_assert(NRED <= NI, "a lane's scores share one head");
@@ -155,30 +165,55 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// Arguments shared by the decode kernels.
+struct DecodeParams {
+  const void* q;
+  const void* kc;
+  const void* vc;
+  const int32_t* tables;
+  const int32_t* ctx_lens;
+  const int32_t* items;    // persistent kernel: (sequence, partition) pairs
+  const int32_t* n_items;  // persistent kernel: number of pairs
+  void* out;
+  float* ws_ml;
+  float* ws_o;
+  float scale_log2;
+  int32_t max_blocks, max_context, num_blocks, num_kv_heads, part_tokens, max_parts;
+};
+
+template <int G, int D, int BS>
+struct DecodeLds {
+  float red_acc[kWaves][G][D];
+  float red_m[kWaves][G];
+  float red_l[kWaves][G];
+  __attribute__((aligned(16))) float p_lds[kWaves][G][BS];
+};
+
+__device__ __forceinline__ int clamp_len(int L, int max_context) {
+  return L < 0 ? 0 : (L > max_context ? max_context : L);
+}
+
+// One work item: the G q heads of KV head `kvh` of sequence `s` over the
+// tokens of partition `part` (the whole context when it is the only one).
+// L is the sequence's clamped context length.  With one partition the
+// normalised rows are written to `out`, otherwise (m, l, o) partials go to
+// the workspace.
 template <typename ST, int D, int BS, int G>
-__global__ __launch_bounds__(kThreads) void decode_kernel(const typename ST::elem* __restrict__ q,
-                                                          const typename ST::elem* __restrict__ kc,
-                                                          const typename ST::elem* __restrict__ vc,
-                                                          const int32_t* __restrict__ tables, int max_blocks,
-                                                          const int32_t* __restrict__ ctx_lens, int max_context,
-                                                          int num_blocks, int num_kv_heads, float scale_log2,
-                                                          int part_tokens,
-                                                          int max_parts, typename ST::elem* __restrict__ out,
-                                                          float* __restrict__ ws_ml, float* __restrict__ ws_o) {
+__device__ __forceinline__ void decode_item(DecodeLds<G, D, BS>& sh, const DecodeParams& P, int s, int kvh,
+                                            int part, int L) {
   using S = DecodeShape<ST, D, BS, G>;
   constexpr int VEC = S::VEC, LPR = S::LPR, RPI = S::RPI, NI = S::NI, NV = S::NV, NRED = S::NRED,
                 CPD = S::CPD;
   using elem = typename ST::elem;
-
-  __shared__ float red_acc[kWaves][G][D];
-  __shared__ float red_m[kWaves][G];
-  __shared__ float red_l[kWaves][G];
-  __shared__ __attribute__((aligned(16))) float p_lds[kWaves][G][BS];
-
-  const int part = blockIdx.x;
-  const int kvh = blockIdx.y;
-  const int s = blockIdx.z;
+  const elem* __restrict__ q = static_cast<const elem*>(P.q);
+  const elem* __restrict__ kc = static_cast<const elem*>(P.kc);
+  const elem* __restrict__ vc = static_cast<const elem*>(P.vc);
+  elem* __restrict__ out = static_cast<elem*>(P.out);
+  const int num_kv_heads = P.num_kv_heads;
   const int num_q_heads = num_kv_heads * G;
+  const int part_tokens = P.part_tokens;
+  const float scale_log2 = P.scale_log2;
+
   const int tid = threadIdx.x;
   const int lane = lane_id();
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -186,9 +221,6 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const typename ST::ele
   const int row = lane / LPR;  // K row within a load instruction
   const int tg = lane % CPD;   // V token group: tokens tg*VEC .. tg*VEC+VEC-1
 
-  // device lengths are clamped to the host bound (which the table also holds)
-  int L = ctx_lens[s];
-  L = L < 0 ? 0 : (L > max_context ? max_context : L);
   const int nparts = (L + part_tokens - 1) / part_tokens;
   if (L == 0) {
     if (part == 0) {
@@ -227,26 +259,18 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const typename ST::ele
   }
   float l_own = 0.f;
 
-  const int32_t* trow = tables + static_cast<int64_t>(s) * max_blocks + blk_begin;
+  const int32_t* trow = P.tables + static_cast<int64_t>(s) * P.max_blocks + blk_begin;
   const int64_t head_off = static_cast<int64_t>(kvh) * BS * D;
   const int64_t blk_stride = static_cast<int64_t>(num_kv_heads) * BS * D;
   const int lane_off = lane * VEC;
+  const int num_blocks = P.num_blocks;
 
   const int my_blocks = nb > wave ? (nb - wave + kWaves - 1) / kWaves : 0;
-  int tbl_base = -64;
-  int tbl_v = 0;
-  auto block_id = [&](int j) -> int {
-    if (j - tbl_base >= 64) {
-      tbl_base = j;
-      const int jj = j + lane;
-      tbl_v = jj < my_blocks ? trow[wave + jj * kWaves] : 0;
-    }
-    const int b = __builtin_amdgcn_readlane(tbl_v, j - tbl_base);
-    return (b >= 0 && b < num_blocks) ? b : 0;  // never dereference out of range
-  };
 
-  auto load_tile = [&](int j, u32x4* kr, u32x4* vr) {
-    const int64_t base = static_cast<int64_t>(block_id(j)) * blk_stride + head_off + lane_off;
+  // address of a tile from its physical block id (never dereferenced out of range)
+  auto load_tile = [&](int b, u32x4* kr, u32x4* vr) {
+    b = (b >= 0 && b < num_blocks) ? b : 0;
+    const int64_t base = static_cast<int64_t>(b) * blk_stride + head_off + lane_off;
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       kr[i] = load16_nt(kc + base + i * 64 * VEC);
@@ -254,7 +278,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const typename ST::ele
     }
   };
 
-  float* pw = &p_lds[wave][0][0];
+  float* pw = &sh.p_lds[wave][0][0];
 
   auto process = [&](int j, const u32x4* kr, const u32x4* vr) {
     const int blk = blk_begin + wave + j * kWaves;
@@ -331,24 +355,36 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const typename ST::ele
     wave_lds_sync();  // the next tile's probabilities overwrite pw
   };
 
-  if (my_blocks > 0) {
-    if constexpr (S::PREFETCH) {
-      u32x4 ka[NI], va[NI], kb[NI], vb[NI];
-      load_tile(0, ka, va);
-      int j = 0;
-      while (true) {
-        if (j + 1 < my_blocks) load_tile(j + 1, kb, vb);
-        process(j, ka, va);
-        if (++j >= my_blocks) break;
-        if (j + 1 < my_blocks) load_tile(j + 1, ka, va);
-        process(j, kb, vb);
-        if (++j >= my_blocks) break;
+  // The wave's tiles in chunks of 64: one vector load brings the chunk's
+  // block-table entries into a VGPR (read back with v_readlane), then a
+  // software pipeline over NBUF register buffers keeps the loads of tile
+  // j + NBUF - 1 in flight while tile j is processed.  In the steady state
+  // every prefetched tile exists, so no load is conditional and each wait
+  // covers only the tile about to be used; the last tiles of a chunk run in
+  // an unrolled tail.
+  for (int c0 = 0; c0 < my_blocks; c0 += 64) {
+    const int cn = min(64, my_blocks - c0);
+    const int tv = lane < cn ? trow[wave + (c0 + lane) * kWaves] : 0;
+    auto block_id = [&](int j) -> int { return __builtin_amdgcn_readlane(tv, j); };
+    constexpr int NB = S::NBUF;
+    u32x4 kb[NB][NI], vb[NB][NI];
+#pragma unroll
+    for (int b = 0; b < NB - 1; ++b)
+      if (b < cn) load_tile(block_id(b), kb[b], vb[b]);
+    int j0 = 0;
+    for (; j0 + 2 * NB - 2 < cn; j0 += NB) {
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        load_tile(block_id(j0 + b + NB - 1), kb[(b + NB - 1) % NB], vb[(b + NB - 1) % NB]);
+        process(c0 + j0 + b, kb[b], vb[b]);
       }
-    } else {
-      for (int j = 0; j < my_blocks; ++j) {
-        u32x4 ka[NI], va[NI];
-        load_tile(j, ka, va);
-        process(j, ka, va);
+    }
+#pragma unroll
+    for (int b = 0; b < 2 * NB - 1; ++b) {
+      const int j = j0 + b;
+      if (j < cn) {
+        if (j + NB - 1 < cn) load_tile(block_id(j + NB - 1), kb[(b + NB - 1) % NB], vb[(b + NB - 1) % NB]);
+        process(c0 + j, kb[b % NB], vb[b % NB]);
       }
     }
   }
@@ -371,13 +407,13 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const typename ST::ele
 #pragma unroll
     for (int h = 0; h < G; ++h)
 #pragma unroll
-      for (int i = 0; i < NI; ++i) red_acc[wave][h][(i * 64 + lane) / CPD] = acc[h][i];
+      for (int i = 0; i < NI; ++i) sh.red_acc[wave][h][(i * 64 + lane) / CPD] = acc[h][i];
   }
   if (lane == 0) {
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      red_m[wave][h] = m[h];
-      red_l[wave][h] = lh[h];
+      sh.red_m[wave][h] = m[h];
+      sh.red_l[wave][h] = lh[h];
     }
   }
   __syncthreads();
@@ -388,28 +424,106 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const typename ST::ele
     float M = -INFINITY;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w)
-      if (red_l[w][h] > 0.f) M = fmaxf(M, red_m[w][h]);
+      if (sh.red_l[w][h] > 0.f) M = fmaxf(M, sh.red_m[w][h]);
     float num = 0.f, den = 0.f;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) {
-      if (red_l[w][h] > 0.f) {
-        const float sc = __builtin_amdgcn_exp2f(red_m[w][h] - M);
-        num = __builtin_fmaf(red_acc[w][h][d], sc, num);
-        den = __builtin_fmaf(red_l[w][h], sc, den);
+      if (sh.red_l[w][h] > 0.f) {
+        const float sc = __builtin_amdgcn_exp2f(sh.red_m[w][h] - M);
+        num = __builtin_fmaf(sh.red_acc[w][h][d], sc, num);
+        den = __builtin_fmaf(sh.red_l[w][h], sc, den);
       }
     }
     const int64_t qh = static_cast<int64_t>(s) * num_q_heads + kvh * G + h;
     if (nparts == 1) {
       out[qh * D + d] = narrow<ST>(num / den);
     } else {
-      const int64_t pidx = qh * max_parts + part;
-      ws_o[pidx * D + d] = num / den;
+      const int64_t pidx = qh * P.max_parts + part;
+      P.ws_o[pidx * D + d] = num / den;
       if (d == 0) {
-        ws_ml[2 * pidx] = M;
-        ws_ml[2 * pidx + 1] = den;
+        P.ws_ml[2 * pidx] = M;
+        P.ws_ml[2 * pidx + 1] = den;
       }
     }
   }
+}
+
+// Grid (partition, KV head, sequence): used when every sequence has a single
+// partition, so no workgroup is launched without work.
+template <typename ST, int D, int BS, int G>
+__global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams P) {
+  __shared__ DecodeLds<G, D, BS> sh;
+  const int s = blockIdx.z;
+  decode_item<ST, D, BS, G>(sh, P, s, blockIdx.y, blockIdx.x, clamp_len(P.ctx_lens[s], P.max_context));
+}
+
+// Persistent variant for split contexts.  A grid the size of the chip walks
+// the compact list of (sequence, partition) pairs written by
+// decode_plan_kernel, times the KV heads: sequences shorter than the longest
+// one cost nothing for the partitions they do not have.  Consecutive items
+// are the KV heads of one (sequence, partition), which read neighbouring
+// tiles of the same blocks.
+template <typename ST, int D, int BS, int G>
+__global__ __launch_bounds__(kThreads) void decode_persistent_kernel(DecodeParams P) {
+  __shared__ DecodeLds<G, D, BS> sh;
+  const int hk = P.num_kv_heads;
+  const int n = __builtin_amdgcn_readfirstlane(*P.n_items) * hk;
+  for (int it = blockIdx.x; it < n; it += gridDim.x) {
+    const int item = it / hk;
+    const int kvh = it - item * hk;
+    const int s = __builtin_amdgcn_readfirstlane(P.items[2 * item]);
+    const int part = __builtin_amdgcn_readfirstlane(P.items[2 * item + 1]);
+    const int L = clamp_len(P.ctx_lens[s], P.max_context);
+    __syncthreads();  // the previous item's LDS merge is complete
+    decode_item<ST, D, BS, G>(sh, P, s, kvh, part, L);
+  }
+}
+
+// Work list of the persistent kernel: every (sequence, partition) pair with
+// tokens in it, in sequence order (a sequence of length 0 gets one pair, whose
+// item writes its zero output).  One workgroup scans the lengths 1024 at a
+// time.
+constexpr int kPlanThreads = 1024;
+
+__global__ __launch_bounds__(kPlanThreads) void decode_plan_kernel(const int32_t* __restrict__ ctx_lens, int num_seqs,
+                                                                   int max_context, int part_tokens,
+                                                                   int32_t* __restrict__ items,
+                                                                   int32_t* __restrict__ n_items) {
+  __shared__ int wave_tot[kPlanThreads / 64];
+  const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
+  int carry = 0;
+  for (int base = 0; base < num_seqs; base += kPlanThreads) {
+    const int s = base + tid;
+    int np = 0;
+    if (s < num_seqs) {
+      const int L = clamp_len(ctx_lens[s], max_context);
+      np = L == 0 ? 1 : (L + part_tokens - 1) / part_tokens;
+    }
+    // inclusive scan over the wavefront, then over the wavefront totals
+    int x = np;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(x, o, 64);
+      if (lane >= o) x += y;
+    }
+    if (lane == 63) wave_tot[wave] = x;
+    __syncthreads();
+    int before = carry, total = 0;
+#pragma unroll
+    for (int w = 0; w < kPlanThreads / 64; ++w) {
+      const int t = wave_tot[w];
+      before += w < wave ? t : 0;
+      total += t;
+    }
+    const int first = before + x - np;
+    for (int p = 0; p < np; ++p) {
+      items[2 * (first + p)] = s;
+      items[2 * (first + p) + 1] = p;
+    }
+    carry += total;
+    __syncthreads();  // wave_tot is rewritten by the next round
+  }
+  if (tid == 0) *n_items = carry;
 }
 
 // Log-sum-exp merge of the partitions of one (sequence, q head).
@@ -422,8 +536,7 @@ __global__ __launch_bounds__(D) void decode_reduce_kernel(const float* __restric
   extern __shared__ float w_sh[];  // [max_parts]
   __shared__ float M_sh;
   const int h = blockIdx.x, s = blockIdx.y, d = threadIdx.x;
-  int L = ctx_lens[s];
-  L = L < 0 ? 0 : (L > max_context ? max_context : L);
+  const int L = clamp_len(ctx_lens[s], max_context);
   const int np = (L + part_tokens - 1) / part_tokens;
   if (np <= 1) return;  // written directly by the decode kernel
   const int64_t qh = static_cast<int64_t>(s) * num_q_heads + h;
@@ -447,21 +560,66 @@ __global__ __launch_bounds__(D) void decode_reduce_kernel(const float* __restric
   out[qh * D + d] = narrow<ST>(num / den);
 }
 
+// Workgroups of the persistent kernel: as many as fit on the device at once
+// (queried once per kernel instance and device).
+template <typename ST, int D, int BS, int G>
+int persistent_grid() {
+  constexpr int kMaxDev = 64;
+  static std::atomic<int> cached[kMaxDev];  // 0 = not yet queried; racing writers store the same value
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) dev = 0;
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    int cus = 0, per_cu = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &per_cu, reinterpret_cast<const void*>(&decode_persistent_kernel<ST, D, BS, G>), kThreads, 0) !=
+            hipSuccess ||
+        per_cu <= 0)
+      per_cu = 2;
+    n = cus * per_cu;
+    cached[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
 template <typename ST, int D, int BS, int G>
 hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t st) {
-  dim3 grid(a.num_parts, a.num_kv_heads, a.num_seqs);
-  using elem = typename ST::elem;
-  hipLaunchKernelGGL((decode_kernel<ST, D, BS, G>), grid, dim3(kThreads), 0, st,
-                     static_cast<const elem*>(a.q), static_cast<const elem*>(a.k_cache),
-                     static_cast<const elem*>(a.v_cache), a.block_tables, a.max_blocks_per_seq, a.context_lens,
-                     a.max_context_len, a.num_blocks, a.num_kv_heads, a.scale * kLog2e, a.part_tokens, a.num_parts,
-                     static_cast<elem*>(a.out), a.ws_ml, a.ws_o);
+  DecodeParams P{};
+  P.q = a.q;
+  P.kc = a.k_cache;
+  P.vc = a.v_cache;
+  P.tables = a.block_tables;
+  P.ctx_lens = a.context_lens;
+  P.items = a.ws_items;
+  P.n_items = a.ws_count;
+  P.out = a.out;
+  P.ws_ml = a.ws_ml;
+  P.ws_o = a.ws_o;
+  P.scale_log2 = a.scale * kLog2e;
+  P.max_blocks = a.max_blocks_per_seq;
+  P.max_context = a.max_context_len;
+  P.num_blocks = a.num_blocks;
+  P.num_kv_heads = a.num_kv_heads;
+  P.part_tokens = a.part_tokens;
+  P.max_parts = a.num_parts;
+  if (a.num_parts <= 1) {
+    hipLaunchKernelGGL((decode_kernel<ST, D, BS, G>), dim3(1, a.num_kv_heads, a.num_seqs), dim3(kThreads), 0, st, P);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL(decode_plan_kernel, dim3(1), dim3(kPlanThreads), 0, st, a.context_lens, a.num_seqs,
+                     a.max_context_len, a.part_tokens, a.ws_items, a.ws_count);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || a.num_parts <= 1) return e;
+  if (e != hipSuccess) return e;
+  const int64_t upper = static_cast<int64_t>(a.num_seqs) * a.num_parts * a.num_kv_heads;
+  const int grid = static_cast<int>(std::min<int64_t>(upper, persistent_grid<ST, D, BS, G>()));
+  hipLaunchKernelGGL((decode_persistent_kernel<ST, D, BS, G>), dim3(grid), dim3(kThreads), 0, st, P);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
   const int num_q_heads = a.num_kv_heads * G;
   hipLaunchKernelGGL((decode_reduce_kernel<ST, D>), dim3(num_q_heads, a.num_seqs), dim3(D),
                      a.num_parts * sizeof(float), st, a.ws_ml, a.ws_o, a.context_lens,
-                     a.max_context_len, a.part_tokens, a.num_parts, num_q_heads, static_cast<elem*>(a.out));
+                     a.max_context_len, a.part_tokens, a.num_parts, num_q_heads, static_cast<typename ST::elem*>(a.out));
   return hipGetLastError();
 }
 

@@ -16,6 +16,8 @@ struct DecodeArgs {
   const int32_t* context_lens;
   float* ws_ml;  // [S][Hq][num_parts][2]  (max in log2 units, sum of weights)
   float* ws_o;   // [S][Hq][num_parts][D]  normalised partial outputs
+  int32_t* ws_items;  // [S * num_parts][2]  (sequence, partition) work list
+  int32_t* ws_count;  // [1]  entries in ws_items
   float scale;
   int32_t dtype, head_dim, block_size, group;
   int32_t num_seqs, num_kv_heads, num_blocks, max_blocks_per_seq;

@@ -125,7 +125,7 @@ def test_append_and_copy_validation():
 
 def test_workspace_size_formula():
     # partitions * (head_dim outputs + max + sum) fp32 per (sequence, q head)
-    assert P.pa_decode_workspace_bytes(4, 32, 128, 131072, 512) == 4 * 32 * 256 * 130 * 4
+    assert P.pa_decode_workspace_bytes(4, 32, 128, 131072, 512) == 4 * 32 * 256 * 130 * 4 + 4 * 256 * 8 + 16
     assert P.pa_decode_workspace_bytes(4, 32, 128, 512, 512) == 0  # one partition
     assert P.pa_decode_workspace_bytes(4, 32, 128, 1000, 0) == 0
     assert P.pa_decode_workspace_bytes(4, 32, 128, 1000, -1) >= P.pa_decode_workspace_bytes(4, 32, 128, 1000, 512)
