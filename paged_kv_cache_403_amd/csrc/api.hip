@@ -197,6 +197,9 @@ int pa_prefill_chunk(const pa_cache* cache, const void* q, void* out, const int3
   if (static_cast<int64_t>(max_context_len) > static_cast<int64_t>(max_blocks_per_seq) * cache->block_size)
     return PA_EINVAL;
   if (num_seqs > kMaxGridYZ) return PA_EUNSUPPORTED;
+  // the block-table entries of the longest context are staged in LDS
+  if (pa::prefill_lds_bytes(cache->dtype, cache->head_dim, max_context_len) > pa::kPrefillMaxLds)
+    return PA_EUNSUPPORTED;
   if (num_seqs == 0 || total_q == 0 || max_q_len == 0) return PA_OK;
   if (!q || !out || !cu_q_lens || !context_lens || !block_tables) return PA_EINVAL;
   pa::PrefillArgs a{};

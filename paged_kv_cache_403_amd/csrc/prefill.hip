@@ -7,23 +7,32 @@
 // Prefill is bound by the matrix units ("性能关键路径与瓶颈"), so both
 // contractions run as v_mfma_f32_32x32x16_{bf16,f16}:
 //
-//  * one workgroup = (sequence, KV head, tile of 128 rows); a row is a (token,
+//  * one workgroup = (sequence, KV head, tile of 256 rows); a row is a (token,
 //    q head of the group) pair, so the G q heads sharing a KV head share every
-//    K/V tile; four wavefronts own 32 rows each;
-//  * keys come in tiles of 64 gathered through the block table (64/BS
-//    blocks), staged in LDS with double buffering: K as [key][dim], V as
-//    [dim][key] -- the pool keeps V transposed inside each block, so the PV
-//    operand is read with 16-byte LDS loads and no transposition;
+//    K/V tile; eight wavefronts (two per SIMD, so one's softmax overlaps the
+//    other's matrix work) own 32 rows each;
+//  * the sequence's block-table entries are staged in LDS once; keys come in
+//    tiles of 64 gathered through them (64/BS blocks), double buffered in
+//    LDS: K as [key][dim], V as [dim][key] -- the pool keeps V transposed
+//    inside each block, so the PV operand is read with 16-byte LDS loads;
 //  * S^T = K Q^T with Q held in registers as the B operand; K rows are fed to
 //    the A operand in the order that makes each lane's accumulator hold 8
 //    consecutive keys of its own row per 16-key step, which is exactly the
 //    B-operand layout of O^T = V^T P^T -- probabilities never leave the lane;
-//  * online softmax per row in the exp2 domain (fp32 state), causal masking
-//    only on tiles that cross a row's diagonal, fully masked tiles skipped;
-//  * P enters the PV contraction as two 16-bit parts (nearest value and
-//    remainder), two MFMAs per step, so the probabilities carry ~16
-//    significant bits: with bf16 outputs the output rounding then dominates
-//    the error budget.
+//  * online softmax per row in the exp2 domain (fp32 state).  The reference
+//    max only moves when a score exceeds it by 2^8 (probabilities stay below
+//    256), so rescaling the accumulators is rare and skipped by whole
+//    wavefronts when no row needs it;
+//  * causal masking only on tiles that cross a row's diagonal; a wavefront
+//    skips tiles that lie wholly above its rows' diagonals;
+//  * P enters PV rounded to the storage type.  On a sequence's first key
+//    tile -- where rows with only a few keys can give outputs of large
+//    magnitude -- it enters as two 16-bit parts (nearest value and
+//    remainder, two MFMAs), so such rows keep only their output rounding;
+//  * workgroup ids are mapped so that all row tiles of one (sequence, KV
+//    head) run on the same XCD and share its L2.
+#include <algorithm>
+
 #include "common.h"
 #include "launch.h"
 
@@ -31,11 +40,14 @@ namespace pa {
 
 namespace {
 
-constexpr int kWaves = 4;
+constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kRows = 32 * kWaves;  // rows per workgroup
 constexpr int kKeys = 64;           // keys per tile
+constexpr int kXcds = 8;            // MI355X: workgroups go round robin over 8 XCDs
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLazy = 8.f;  // log2 units the running max may lag the true max
+constexpr int kSortMax = 4096;  // items per XCD ordered longest first (more keep index order)
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -66,6 +78,19 @@ __device__ __forceinline__ uint32_t pack2<F16>(float a, float b) {
   return __builtin_bit_cast(uint32_t, f16x2{static_cast<_Float16>(a), static_cast<_Float16>(b)});
 }
 
+// Max / sum of x over lanes l and l ^ 32.  v_permlane32_swap exchanges the
+// two 32-lane halves between its two operands; with x in both, every lane
+// ends up holding its own value in one result and its partner's in the
+// other (which one depends on the half), so both reductions are symmetric.
+__device__ __forceinline__ float halves_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float halves_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // A-operand row m of a 32-key subtile holds key perm(m): bits 2 and 3 swapped.
 __device__ __forceinline__ int key_perm(int m) { return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1); }
 
@@ -83,24 +108,66 @@ struct PrefillShape {
   static constexpr int TOK = kRows / G;              // tokens per workgroup tile
   static constexpr int KSTEPS = D / 16;
   static constexpr int DSUB = D / 32;
-  static_assert(PER_THREAD * kThreads == CHUNKS, "tile chunks");
+  static_assert(PER_THREAD >= 1 && PER_THREAD * kThreads == CHUNKS, "tile chunks");
   static_assert(BLOCKS * BS == kKeys, "blocks per tile");
 };
 
 template <typename ST, int D, int BS, int G>
-__global__ __launch_bounds__(kThreads, 2) void prefill_kernel(
+__global__ __launch_bounds__(kThreads, 1) void prefill_kernel(
     const typename ST::elem* __restrict__ q, const typename ST::elem* __restrict__ kc,
     const typename ST::elem* __restrict__ vc, const int32_t* __restrict__ tables, int max_blocks,
     const int32_t* __restrict__ ctx_lens, const int32_t* __restrict__ cu_q, int num_blocks, int num_kv_heads,
-    float scale_log2, typename ST::elem* __restrict__ out) {
+    int num_units, int row_tiles, int max_context, float scale_log2, typename ST::elem* __restrict__ out) {
   using S = PrefillShape<ST, D, BS, G>;
   using elem = typename ST::elem;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
   elem* smem = reinterpret_cast<elem*>(smem_raw);
+  int32_t* tbl = reinterpret_cast<int32_t*>(smem + 2 * S::STAGE);
 
-  const int g = blockIdx.y;
-  const int s = blockIdx.z;
   const int tid = threadIdx.x;
+  // Workgroup -> (unit = sequence * KV heads + head, row tile).  Workgroup w
+  // runs on XCD w % 8 as slot w / 8; the XCD owns units x, x + 8, ..., so
+  // all row tiles of a unit share one L2.  Within an XCD the slots take the
+  // items in decreasing number of key tiles (ties by index): the dispatcher
+  // hands slots to compute units in order, so this is longest-first
+  // scheduling of the uneven contexts.
+  const int xcd = blockIdx.x % kXcds;
+  const int slot = blockIdx.x / kXcds;
+  const int xunits = num_units > xcd ? (num_units - xcd + kXcds - 1) / kXcds : 0;
+  const int nitems = xunits * row_tiles;
+  if (slot >= nitems) return;
+  int item = slot;
+  if (nitems <= kSortMax) {
+    int* cost = reinterpret_cast<int*>(tbl);  // the table area is free until the item is known
+    __shared__ int chosen;
+    for (int e = tid; e < nitems; e += kThreads) {
+      const int u = xcd + kXcds * (e / row_tiles);
+      const int su = u / num_kv_heads;
+      const int nu = cu_q[su + 1] - cu_q[su];
+      const int Lu = min(ctx_lens[su], max_context);
+      const int t0 = (e % row_tiles) * S::TOK;
+      // key tiles the item reads (0: no rows)
+      cost[e] = (nu <= 0 || t0 >= nu || Lu < nu) ? 0 : (Lu - nu + min(nu, t0 + S::TOK) - 1) / kKeys + 1;
+    }
+    __syncthreads();
+    for (int e = tid; e < nitems; e += kThreads) {
+      const int c = cost[e];
+      int rank = 0;
+      for (int f = 0; f < nitems; ++f) {
+        const int cf = cost[f];
+        rank += (cf > c || (cf == c && f < e)) ? 1 : 0;
+      }
+      if (rank == slot) chosen = e;
+    }
+    __syncthreads();
+    item = chosen;
+    __syncthreads();  // cost[] is overwritten by the block table below
+  }
+  const int unit = xcd + kXcds * (item / row_tiles);
+  const int s = unit / num_kv_heads;
+  const int g = unit - s * num_kv_heads;
+  const int tile = item % row_tiles;
+
   const int lane = lane_id();
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int half = lane >> 5;  // which 8 of 16 along the contraction
@@ -109,9 +176,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(
   const int q0 = cu_q[s];
   const int n = cu_q[s + 1] - q0;
   int L = ctx_lens[s];
-  L = L > max_blocks * BS ? max_blocks * BS : L;
-  // heavier tiles (later tokens see more keys) are dispatched first
-  const int tile = gridDim.x - 1 - blockIdx.x;
+  L = L > max_context ? max_context : L;
   const int tok0 = tile * S::TOK;
   if (n <= 0 || tok0 >= n || L < n) return;
   const int num_q_heads = num_kv_heads * G;
@@ -122,6 +187,24 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(
   const int hq = g * G + r % G;
   const bool row_ok = tok < n;
   const int pos = L - n + (row_ok ? tok : n - 1);  // last key this row sees
+  // last key any row of this wavefront sees (rows past the chunk see n - 1)
+  const int wave_pos = L - n + min(n - 1, tok0 + (wave * 32 + 31) / G);
+
+  const int tok_last = min(n, tok0 + S::TOK) - 1;
+  const int kmax = L - n + tok_last;  // last key any row of the tile sees
+  const int ntiles = kmax / kKeys + 1;
+  const int diag0 = L - n + tok0;  // keys above this may be masked for some row
+  const int nblk_valid = (L + BS - 1) / BS;
+
+  // block-table entries of every tile, out-of-range ids replaced by block 0
+  {
+    const int32_t* trow = tables + static_cast<int64_t>(s) * max_blocks;
+    const int nt = ntiles * S::BLOCKS;
+    for (int i = tid; i < nt; i += kThreads) {
+      int b = i < nblk_valid ? trow[i] : 0;
+      tbl[i] = (b >= 0 && b < num_blocks) ? b : 0;
+    }
+  }
 
   // Q as the B operand of S^T = K Q^T: lane holds q[row][16 kk + 8 half .. +8]
   u32x4 qb[S::KSTEPS];
@@ -131,13 +214,6 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(
     for (int kk = 0; kk < S::KSTEPS; ++kk) qb[kk] = row_ok ? load16(qp + kk * 16) : u32x4{0, 0, 0, 0};
   }
 
-  const int tok_last = min(n, tok0 + S::TOK) - 1;
-  const int kmax = L - n + tok_last;  // last key any row of the tile sees
-  const int ntiles = kmax / kKeys + 1;
-  const int diag0 = L - n + tok0;  // keys above this may be masked for some row
-  const int nblk_valid = (L + BS - 1) / BS;
-
-  const int32_t* trow = tables + static_cast<int64_t>(s) * max_blocks;
   const int64_t head_k = static_cast<int64_t>(g) * BS * D;
   const int64_t blk_stride = static_cast<int64_t>(num_kv_heads) * BS * D;
 
@@ -150,17 +226,10 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(
       const int c = tid + i * kThreads;
       const int b = c / S::CPB;  // block within the tile
       const int cc = c % S::CPB;
-      const int kb = t * S::BLOCKS + b;
-      if (kb < nblk_valid) {
-        int blk = trow[kb];
-        blk = (blk >= 0 && blk < num_blocks) ? blk : 0;
-        const int64_t base = static_cast<int64_t>(blk) * blk_stride + head_k + static_cast<int64_t>(cc) * 8;
-        kst[i] = load16(kc + base);
-        vst[i] = load16(vc + base);
-      } else {
-        kst[i] = u32x4{0, 0, 0, 0};
-        vst[i] = u32x4{0, 0, 0, 0};
-      }
+      const int blk = tbl[t * S::BLOCKS + b];
+      const int64_t base = static_cast<int64_t>(blk) * blk_stride + head_k + static_cast<int64_t>(cc) * 8;
+      kst[i] = load16(kc + base);
+      vst[i] = load16(vc + base);
     }
   };
   // registers -> LDS stage; keys at or past L are zeroed in V (and K)
@@ -202,6 +271,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(
 #pragma unroll
   for (int ds = 0; ds < S::DSUB; ++ds) o_acc[ds] = f32x16{};
 
+  __syncthreads();  // block table in LDS
   fetch(0);
   stage(0, 0);
   __syncthreads();
@@ -213,80 +283,90 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(
     const elem* kl = smem + buf * S::STAGE;
     const elem* vl = kl + S::K_ELEMS;
 
-    // S^T for the two 32-key subtiles
-    f32x16 sacc[2] = {f32x16{}, f32x16{}};
+    if (t * kKeys <= wave_pos) {  // some row of this wavefront sees a key of this tile
+      // S^T for the two 32-key subtiles
+      f32x16 sacc[2] = {f32x16{}, f32x16{}};
 #pragma unroll
-    for (int kk = 0; kk < S::KSTEPS; ++kk) {
+      for (int kk = 0; kk < S::KSTEPS; ++kk) {
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const u32x4 a = *reinterpret_cast<const u32x4*>(kl + (ks * 32 + arow) * S::KPAD + kk * 16 + half * 8);
-        sacc[ks] = mfma32<ST>(a, qb[kk], sacc[ks]);
+        for (int ks = 0; ks < 2; ++ks) {
+          const u32x4 a = *reinterpret_cast<const u32x4*>(kl + (ks * 32 + arow) * S::KPAD + kk * 16 + half * 8);
+          sacc[ks] = mfma32<ST>(a, qb[kk], sacc[ks]);
+        }
       }
-    }
-    // lane value j of subtile ks is key t*64 + 32 ks + 16 (j/8) + 8 half + j%8
-    const int kbase = t * kKeys + half * 8;
-    if (t * kKeys + kKeys - 1 > diag0) {
+      // lane value j of subtile ks is key t*64 + 32 ks + 16 (j/8) + 8 half + j%8
+      const int kbase = t * kKeys + half * 8;
+      if (t * kKeys + kKeys - 1 > diag0) {
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+          for (int jj = 0; jj < 16; ++jj) {
+            const int key = kbase + ks * 32 + (jj >> 3) * 16 + (jj & 7);
+            sacc[ks][jj] = key <= pos ? sacc[ks][jj] : -INFINITY;
+          }
+      }
+      float mx = -INFINITY;
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          const int key = kbase + ks * 32 + (j >> 3) * 16 + (j & 7);
-          sacc[ks][j] = key <= pos ? sacc[ks][j] : -INFINITY;
+        for (int jj = 0; jj < 16; ++jj) mx = fmaxf(mx, sacc[ks][jj]);
+      mx = halves_max(mx) * scale_log2;
+      // the reference max moves only when the tile's max passes it by kLazy
+      const bool move = mx > m_run + kLazy;
+      const bool rescale = move && m_run > -INFINITY;  // accumulators hold earlier keys
+      const float m_new = move ? mx : m_run;
+      const float alpha = move ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
+      m_run = m_new;
+      float psum = 0.f;
+      // P^T as B operand, one per 16-key step
+      u32x4 pb[4], pl[4];
+      const bool split = t == 0;  // first tile: probabilities as two 16-bit parts
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int a8 = 0; a8 < 2; ++a8) {
+          float p[8];
+#pragma unroll
+          for (int u = 0; u < 8; ++u) {
+            p[u] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[ks][a8 * 8 + u], scale_log2, -m_new));
+            psum += p[u];
+          }
+          uint32_t hi[4];
+#pragma unroll
+          for (int w2 = 0; w2 < 4; ++w2) hi[w2] = pack2<ST>(p[2 * w2], p[2 * w2 + 1]);
+          pb[ks * 2 + a8] = u32x4{hi[0], hi[1], hi[2], hi[3]};
+          if (split) {
+            uint32_t lo[4];
+#pragma unroll
+            for (int w2 = 0; w2 < 4; ++w2) {
+              float h0, h1;
+              widen2<ST>(hi[w2], h0, h1);
+              lo[w2] = pack2<ST>(p[2 * w2] - h0, p[2 * w2 + 1] - h1);
+            }
+            pl[ks * 2 + a8] = u32x4{lo[0], lo[1], lo[2], lo[3]};
+          }
         }
-    }
-    float mx = -INFINITY;
+      l_run = l_run * alpha + psum;
+      if (__builtin_amdgcn_ballot_w64(rescale) != 0) {
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-      for (int j = 0; j < 16; ++j) mx = fmaxf(mx, sacc[ks][j]);
-    mx = fmaxf(mx, xor_lane<32>(mx));
-    const float m_new = fmaxf(m_run, mx * scale_log2);
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-    m_run = m_new;
-    float psum = 0.f;
-    // P^T as B operand, one per 16-key step: the 16-bit value nearest p and
-    // the 16-bit value nearest the remainder, so P V keeps fp32-like accuracy
-    // and the output's own rounding is the only visible error
-    u32x4 pb[4], pl[4];
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-      for (int a8 = 0; a8 < 2; ++a8) {
-        float p[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          p[u] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[ks][a8 * 8 + u], scale_log2, -m_new));
-          psum += p[u];
-        }
-        uint32_t hi[4], lo[4];
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          hi[w] = pack2<ST>(p[2 * w], p[2 * w + 1]);
-          float h0, h1;
-          widen2<ST>(hi[w], h0, h1);
-          lo[w] = pack2<ST>(p[2 * w] - h0, p[2 * w + 1] - h1);
-        }
-        pb[ks * 2 + a8] = u32x4{hi[0], hi[1], hi[2], hi[3]};
-        pl[ks * 2 + a8] = u32x4{lo[0], lo[1], lo[2], lo[3]};
+        for (int ds = 0; ds < S::DSUB; ++ds) o_acc[ds] *= alpha;
       }
-    l_run = l_run * alpha + psum;
+      // O^T += V^T P^T
 #pragma unroll
-    for (int ds = 0; ds < S::DSUB; ++ds) o_acc[ds] *= alpha;
-    // O^T += V^T P^T
+      for (int kk2 = 0; kk2 < 4; ++kk2) {
 #pragma unroll
-    for (int kk2 = 0; kk2 < 4; ++kk2) {
-#pragma unroll
-      for (int ds = 0; ds < S::DSUB; ++ds) {
-        const u32x4 a = *reinterpret_cast<const u32x4*>(vl + (ds * 32 + nl) * S::VPAD + kk2 * 16 + half * 8);
-        o_acc[ds] = mfma32<ST>(a, pb[kk2], o_acc[ds]);
-        o_acc[ds] = mfma32<ST>(a, pl[kk2], o_acc[ds]);
+        for (int ds = 0; ds < S::DSUB; ++ds) {
+          const u32x4 a = *reinterpret_cast<const u32x4*>(vl + (ds * 32 + nl) * S::VPAD + kk2 * 16 + half * 8);
+          o_acc[ds] = mfma32<ST>(a, pb[kk2], o_acc[ds]);
+          if (split) o_acc[ds] = mfma32<ST>(a, pl[kk2], o_acc[ds]);
+        }
       }
     }
     if (t + 1 < ntiles) stage(t + 1, buf ^ 1);
     __syncthreads();
   }
 
-  const float l_tot = l_run + xor_lane<32>(l_run);  // both halves of the row (all lanes active)
+  const float l_tot = halves_sum(l_run);  // both halves of the row
   if (!row_ok) return;
   const float inv = 1.f / l_tot;
   elem* op = out + (static_cast<int64_t>(q0 + tok) * num_q_heads + hq) * D;
@@ -296,10 +376,10 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(
 #pragma unroll
     for (int j4 = 0; j4 < 4; ++j4) {
       const int d0 = ds * 32 + j4 * 8 + half * 4;
-      uint2 w;
-      w.x = pack2<ST>(o_acc[ds][j4 * 4 + 0] * inv, o_acc[ds][j4 * 4 + 1] * inv);
-      w.y = pack2<ST>(o_acc[ds][j4 * 4 + 2] * inv, o_acc[ds][j4 * 4 + 3] * inv);
-      *reinterpret_cast<uint2*>(op + d0) = w;
+      uint2 wv;
+      wv.x = pack2<ST>(o_acc[ds][j4 * 4 + 0] * inv, o_acc[ds][j4 * 4 + 1] * inv);
+      wv.y = pack2<ST>(o_acc[ds][j4 * 4 + 2] * inv, o_acc[ds][j4 * 4 + 3] * inv);
+      *reinterpret_cast<uint2*>(op + d0) = wv;
     }
 }
 
@@ -307,21 +387,29 @@ template <typename ST, int D, int BS, int G>
 hipError_t launch_t(const PrefillArgs& a, hipStream_t st) {
   using S = PrefillShape<ST, D, BS, G>;
   using elem = typename ST::elem;
-  const int tiles = (a.max_q_len + S::TOK - 1) / S::TOK;
-  if (tiles == 0 || a.num_seqs == 0) return hipSuccess;
-  const size_t lds = 2 * S::STAGE * sizeof(elem);
+  const int row_tiles = (a.max_q_len + S::TOK - 1) / S::TOK;
+  if (row_tiles == 0 || a.num_seqs == 0) return hipSuccess;
+  const int units = a.num_seqs * a.num_kv_heads;
+  const int64_t grid = static_cast<int64_t>((units + kXcds - 1) / kXcds) * kXcds * row_tiles;
+  if (grid > 0x7fffffff) return hipErrorInvalidValue;
+  const int max_tiles = (a.max_context_len + kKeys - 1) / kKeys;
+  const int per_xcd = (units + kXcds - 1) / kXcds * row_tiles;
+  const size_t tbl_entries = std::max<size_t>(static_cast<size_t>(max_tiles) * S::BLOCKS,
+                                              per_xcd <= kSortMax ? static_cast<size_t>(per_xcd) : 0);
+  const size_t lds = 2 * S::STAGE * sizeof(elem) + tbl_entries * sizeof(int32_t);
+  if (lds > kPrefillMaxLds) return hipErrorInvalidValue;
   static bool lds_attr_set = false;  // above 64 KiB of dynamic LDS must be allowed explicitly
   if (!lds_attr_set) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_kernel<ST, D, BS, G>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(kPrefillMaxLds));
     if (e != hipSuccess) return e;
     lds_attr_set = true;
   }
-  dim3 grid(tiles, a.num_kv_heads, a.num_seqs);
-  hipLaunchKernelGGL((prefill_kernel<ST, D, BS, G>), grid, dim3(kThreads), lds, st,
+  hipLaunchKernelGGL((prefill_kernel<ST, D, BS, G>), dim3(static_cast<unsigned>(grid)), dim3(kThreads), lds, st,
                      static_cast<const elem*>(a.q), static_cast<const elem*>(a.k_cache),
                      static_cast<const elem*>(a.v_cache), a.block_tables, a.max_blocks_per_seq, a.context_lens,
-                     a.cu_q_lens, a.num_blocks, a.num_kv_heads, a.scale * kLog2e, static_cast<elem*>(a.out));
+                     a.cu_q_lens, a.num_blocks, a.num_kv_heads, units, row_tiles, a.max_context_len,
+                     a.scale * kLog2e, static_cast<elem*>(a.out));
   return hipGetLastError();
 }
 
@@ -355,6 +443,15 @@ hipError_t by_dim(const PrefillArgs& a, hipStream_t st) {
 }
 
 }  // namespace
+
+size_t prefill_lds_bytes(int32_t dtype, int32_t head_dim, int32_t max_context_len) {
+  (void)dtype;  // both matrix-core types are 16-bit
+  const size_t stage = static_cast<size_t>(kKeys) * (head_dim + 8) + static_cast<size_t>(head_dim) * (kKeys + 8);
+  const size_t max_tiles = (static_cast<size_t>(max_context_len) + kKeys - 1) / kKeys;
+  // table entries (64 keys per tile over blocks of at least 16 tokens), or
+  // the item costs of the longest-first ordering if more
+  return 2 * stage * 2 + std::max<size_t>(max_tiles * (kKeys / 16), kSortMax) * sizeof(int32_t);
+}
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st) {
   switch (a.dtype) {
