@@ -59,6 +59,20 @@ def attend(qv, K, V, scale):
     return p @ V, m + np.log(l), p
 
 
+def attention_rows(q_rows, K, V, positions, scale, dtype):
+    """Rows of one (sequence, q head) against that head's K/V in logical
+    order (K, V [L][D] storage values): row i sees keys 0..positions[i].
+    The same definition as `paged_attention`, for a few sampled rows of a
+    long sequence.  Returns out [n][D] fp64."""
+    q = to_f64(np.asarray(q_rows), dtype)
+    Kf = to_f64(np.asarray(K), dtype)
+    Vf = to_f64(np.asarray(V), dtype)
+    out = np.zeros((len(positions), Kf.shape[1]))
+    for i, a in enumerate(positions):
+        out[i], _, _ = attend(q[i], Kf[: int(a) + 1], Vf[: int(a) + 1], scale)
+    return out
+
+
 def paged_attention(q, pool_k, pool_v, tables, context_lens, q_lens, scale, dtype):
     """q: [sum n][Hq][D] storage values, rows in sequence order.
 

@@ -61,15 +61,18 @@ class StepState:
     setup_slots: np.ndarray  # int64, all pre-step appends in issue order
 
 
-def run_workload(wl, fill_bits=None) -> StepState:
+def run_workload(wl, fill_bits=None, with_pool=True) -> StepState:
     """Replay setup and step operations of a `workloads.Workload`.
 
     The pool starts filled with `fill_bits` (a sentinel in unused slots), the
     pre-step cache is built, then the step's block-manager calls run and the
-    step's copies and appends are applied, in that order."""
+    step's copies and appends are applied, in that order.  with_pool=False
+    replays only the bookkeeping (slots, copy pairs, tables, lengths) and
+    leaves `pool` None -- for workloads too large to hold twice in host
+    memory."""
     sp = wl.spec
     bm = BlockManager(sp.num_blocks, sp.block_size, wl.free_order)
-    pool = Pool(sp.num_blocks, sp.num_kv_heads, sp.block_size, sp.head_dim, sp.dtype, fill_bits)
+    pool = Pool(sp.num_blocks, sp.num_kv_heads, sp.block_size, sp.head_dim, sp.dtype, fill_bits) if with_pool else None
     setup_slots = []
     for op in wl.setup_ops():
         if op.kind == "add":
@@ -78,17 +81,19 @@ def run_workload(wl, fill_bits=None) -> StepState:
             bm.fork(op.parent, op.seq, op.keep)
         else:
             slots, pairs = bm.append(op.seq, op.n)
-            pool.copy(pairs)
-            pool.write(slots, op.k, op.v)
+            if pool is not None:
+                pool.copy(pairs)
+                pool.write(slots, op.k, op.v)
             setup_slots.extend(slots)
     step_slots, step_pairs = [], []
     for op in wl.step_ops():
         slots, pairs = bm.append(op.seq, op.n)
         step_slots.extend(slots)
         step_pairs.extend(pairs)
-    k_new, v_new = wl.step_kv()
-    pool.copy(step_pairs)
-    pool.write(step_slots, k_new, v_new)
+    if pool is not None:
+        k_new, v_new = wl.step_kv()
+        pool.copy(step_pairs)
+        pool.write(step_slots, k_new, v_new)
     batch = wl.batch
     maxb = max(len(bm.tables[p.seq_id]) for p in batch)
     tables = np.full((len(batch), max(maxb, 1)), sp.poison_block, dtype=np.int32)

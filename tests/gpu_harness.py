@@ -24,10 +24,11 @@ class ProductResult:
     tables: np.ndarray
     lens: np.ndarray
     setup_slots: np.ndarray
+    cache: object = None  # the device PagedKVCache when asked for
 
 
 def run_step(wl, fill=SENTINEL, free_order=None, partition_size=0, device="cuda", keep_pool=True,
-             prefill_all=False):
+             prefill_all=False, return_cache=False):
     """One step of `wl`: setup appends, the step's copies and appends, then
     decode for one-token sequences and chunked prefill for the others (or
     prefill for all when prefill_all)."""
@@ -75,12 +76,17 @@ def run_step(wl, fill=SENTINEL, free_order=None, partition_size=0, device="cuda"
                            int(n_new[idx].max()), int(plan.host_lens[idx].max()), sp.scale)
         out_all[rows] = to_host(out)
     torch.cuda.synchronize()
+    if return_cache:
+        res_cache = cache
+    else:
+        res_cache = None
     return ProductResult(
         out=out_all,
         k_pool=to_host(cache.k) if keep_pool else None,
         v_pool=to_host(cache.v) if keep_pool else None,
         slots=plan.host_slots, pairs=plan.host_pairs, tables=plan.host_tables, lens=plan.host_lens,
         setup_slots=setup_slots,
+        cache=res_cache,
     )
 
 

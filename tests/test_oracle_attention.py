@@ -185,3 +185,28 @@ def test_workload_generation_is_deterministic():
     x = workloads.normal_values((1, 2, 3), (5, 1 << 20), "f16", threads=1)
     y = workloads.normal_values((1, 2, 3), (5, 1 << 20), "f16", threads=8)
     assert (x == y).all()
+
+
+@pytest.mark.parametrize("name", ["mha_decode_7b", "gqa_shared_prefix", "mixed_chunked_prefill"])
+def test_sampled_rows_match_batched_reference(name):
+    """attention_rows on a sequence's logical K/V (the sampled form the
+    full-size GPU tests use) reproduces paged_attention's rows, and the
+    bookkeeping-only replay matches the full one."""
+    wl, st = _state(name)
+    sp = wl.spec
+    ref, _ = A.paged_attention(wl.step_q(), st.pool.k, st.pool.v, st.tables, st.context_lens, st.q_lens,
+                               sp.scale, sp.dtype)
+    light = run_workload(wl, with_pool=False)
+    assert light.pool is None
+    for a, b in [(light.slot_mapping, st.slot_mapping), (light.cow_pairs, st.cow_pairs), (light.tables, st.tables),
+                 (light.context_lens, st.context_lens), (light.setup_slots, st.setup_slots)]:
+        assert np.array_equal(a, b)
+    G = sp.num_q_heads // sp.num_kv_heads
+    row = 0
+    for p in wl.batch:
+        K, V = wl.logical_kv(p.seq_id)
+        for h in (0, sp.num_q_heads - 1):
+            pos = p.context_len - p.n_new + np.arange(p.n_new)
+            got = A.attention_rows(wl.q[p.seq_id][:, h], K[:, h // G], V[:, h // G], pos, sp.scale, sp.dtype)
+            assert np.abs(got - ref[row:row + p.n_new, h]).max() <= 1e-12
+        row += p.n_new
