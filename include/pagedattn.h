@@ -142,7 +142,10 @@ int32_t pa_decode_choose_partition(const pa_cache* cache, int32_t num_seqs, int3
  *   cu_q_lens     device int32 [num_seqs + 1], cu_q_lens[0] = 0,
  *                 cu_q_lens[num_seqs] = total_q
  *   context_lens  device int32 [num_seqs]
- *   max_q_len, max_context_len  host bounds of n_s and context_lens */
+ *   max_q_len, max_context_len  host bounds of n_s and context_lens
+ * A workgroup stages its sequence's block-table entries in LDS, so contexts
+ * whose table does not fit (about 360k tokens at block_size 16, head_dim
+ * 128) return PA_EUNSUPPORTED. */
 int pa_prefill_chunk(const pa_cache* cache, const void* q, void* out, const int32_t* cu_q_lens,
                      const int32_t* context_lens, int32_t num_seqs, int32_t total_q, int32_t num_q_heads,
                      const int32_t* block_tables, int32_t max_blocks_per_seq, int32_t max_q_len,
