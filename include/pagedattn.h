@@ -132,6 +132,41 @@ int pa_decode(const pa_cache* cache, const void* q, void* out, int32_t num_seqs,
 int32_t pa_decode_choose_partition(const pa_cache* cache, int32_t num_seqs, int32_t num_q_heads,
                                    int32_t max_context_len);
 
+/* Bytes of device workspace pa_decode_grouped needs (partition_size as
+ * passed to it; 0 = the default). */
+size_t pa_decode_grouped_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                                         int32_t max_context_len, int32_t partition_size);
+
+/* Prefix-grouped decode: the same result as pa_decode, but blocks that
+ * several sequences of the batch share (forks of one prompt keep its blocks
+ * read-only until copy-on-write: lshu.cn/news/11644, "收益分析") are read
+ * once for all of them -- prefix caching within the batch, which the same
+ * page counts among the decode-side savings ("性能关键路径与瓶颈").
+ * Arguments as for pa_decode, f16 or bf16 caches, plus:
+ *   group_start     device int32 [num_groups + 1]: sequences
+ *                   group_start[g] .. group_start[g+1]-1 are likely to share
+ *                   a prefix (e.g. forks of one prompt).  A hint only: the
+ *                   library cuts the batch into runs at these starts, splits
+ *                   runs into chunks of at most 32 / (num_q_heads /
+ *                   num_kv_heads) sequences, and measures on the block
+ *                   tables how many leading full blocks each sequence has in
+ *                   common with its chunk's longest sequence; any grouping
+ *                   (NULL with num_groups 0 included) gives the same result
+ *   partition_size  0 = 256; else a multiple of 32 and of block_size, at
+ *                   most 64 blocks: tokens per partition of both the shared
+ *                   prefix and each sequence's own suffix
+ *   workspace       device scratch of at least
+ *                   pa_decode_grouped_workspace_bytes(); rewritten by each
+ *                   call, so calls sharing it must be ordered on one stream
+ * num_seqs is limited to 4096 (PA_EUNSUPPORTED above).  Runs four kernels
+ * on `stream`: a one-workgroup planner, the shared-prefix kernel (matrix
+ * cores, one chunk's rows per workgroup), the suffix partitions of the split
+ * decode kernel, and the log-sum-exp merge. */
+int pa_decode_grouped(const pa_cache* cache, const void* q, void* out, int32_t num_seqs, int32_t num_q_heads,
+                      const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
+                      int32_t max_context_len, float scale, const int32_t* group_start, int32_t num_groups,
+                      int32_t partition_size, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Chunked-prefill attention (5x10.cn/post/462, "分块预填充"; lshu.cn/news/11644,
  * "整体架构": long prompts are split into chunks over several iterations and
  * batched with decode tokens).  Sequence s has n_s = cu_q_lens[s+1] -

@@ -54,6 +54,9 @@ _SIGNATURES = {
     "pa_decode": (ctypes.c_int, [_cp, _vp, _vp, _i32, _i32, _vp, _i32, _vp, _i32, ctypes.c_float, _i32, _vp,
                                  ctypes.c_size_t, _vp]),
     "pa_decode_choose_partition": (_i32, [_cp, _i32, _i32, _i32]),
+    "pa_decode_grouped_workspace_bytes": (ctypes.c_size_t, [_i32, _i32, _i32, _i32, _i32]),
+    "pa_decode_grouped": (ctypes.c_int, [_cp, _vp, _vp, _i32, _i32, _vp, _i32, _vp, _i32, ctypes.c_float, _vp, _i32,
+                                         _i32, _vp, ctypes.c_size_t, _vp]),
     "pa_prefill_chunk": (ctypes.c_int, [_cp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp, _i32, _i32, _i32,
                                         ctypes.c_float, _vp]),
     "pa_status_str": (ctypes.c_char_p, [ctypes.c_int]),
@@ -186,6 +189,25 @@ def pa_decode(cache: pa_cache, q, out, block_tables, context_lens, max_context_l
                          _dev_ptr(context_lens, "context_lens"), int(max_context_len), float(scale),
                          int(partition_size), _dev_ptr(workspace, "workspace"), ws_bytes, _stream(stream, q))
     _check(rc, "pa_decode")
+
+
+def pa_decode_grouped_workspace_bytes(num_seqs, num_q_heads, head_dim, max_context_len, partition_size=0) -> int:
+    return int(lib().pa_decode_grouped_workspace_bytes(num_seqs, num_q_heads, head_dim, max_context_len,
+                                                       partition_size))
+
+
+def pa_decode_grouped(cache: pa_cache, q, out, block_tables, context_lens, max_context_len, scale, group_start,
+                      partition_size=0, workspace=None, stream=None):
+    """group_start: device int32 [num_groups + 1] (or None for no grouping hint)."""
+    num_seqs, num_q_heads = int(q.shape[0]), int(q.shape[1])
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    num_groups = 0 if group_start is None else max(int(group_start.shape[0]) - 1, 0)
+    rc = lib().pa_decode_grouped(ctypes.byref(cache), _dev_ptr(q, "q"), _dev_ptr(out, "out"), num_seqs, num_q_heads,
+                                 _dev_ptr(block_tables, "block_tables"), int(block_tables.shape[1]),
+                                 _dev_ptr(context_lens, "context_lens"), int(max_context_len), float(scale),
+                                 _dev_ptr(group_start, "group_start"), num_groups, int(partition_size),
+                                 _dev_ptr(workspace, "workspace"), ws_bytes, _stream(stream, q))
+    _check(rc, "pa_decode_grouped")
 
 
 def pa_prefill_chunk(cache: pa_cache, q, out, cu_q_lens, context_lens, block_tables, max_q_len, max_context_len,

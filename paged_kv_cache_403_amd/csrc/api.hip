@@ -1,6 +1,7 @@
 // C ABI of the paged KV-cache attention library: argument validation, launch
 // configuration, workspace sizing and error mapping.  Every check that needs
 // only host-visible values runs before anything is enqueued.
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 
@@ -59,6 +60,42 @@ size_t workspace_for(int64_t num_seqs, int64_t num_q_heads, int64_t head_dim, in
   return static_cast<size_t>(num_seqs * num_q_heads * num_parts * (head_dim + 2) * sizeof(float) +
                              num_seqs * num_parts * 2 * sizeof(int32_t) + 16);
 }
+
+// Prefix-grouped decode: partitions of `part` tokens, 2 * ceil(C / part)
+// slots per row (prefix slots of the chunk, then the sequence's own).
+constexpr int32_t kGroupedDefaultPartition = 256;
+
+struct GroupedLayout {
+  int64_t parts, slots;
+  size_t ml, o, suf_items, pre_items, seq_start, slot_base, nslots, counts, total;  // byte offsets
+};
+
+size_t align16(size_t x) { return (x + 15) / 16 * 16; }
+
+GroupedLayout grouped_layout(int64_t num_seqs, int64_t num_q_heads, int64_t head_dim, int64_t max_context_len,
+                             int64_t part) {
+  GroupedLayout g{};
+  g.parts = std::max<int64_t>(1, (max_context_len + part - 1) / part);
+  g.slots = 2 * g.parts;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off = align16(off + bytes);
+    return at;
+  };
+  g.ml = take(num_seqs * num_q_heads * g.slots * 2 * sizeof(float));
+  g.o = take(num_seqs * num_q_heads * g.slots * head_dim * sizeof(float));
+  g.suf_items = take(num_seqs * g.parts * 2 * sizeof(int32_t));
+  g.pre_items = take(num_seqs * g.parts * 4 * sizeof(int32_t));
+  g.seq_start = take(num_seqs * sizeof(int32_t));
+  g.slot_base = take(num_seqs * sizeof(int32_t));
+  g.nslots = take(num_seqs * sizeof(int32_t));
+  g.counts = take(2 * sizeof(int32_t));
+  g.total = off;
+  return g;
+}
+
+int32_t grouped_partition(int32_t requested) { return requested == 0 ? kGroupedDefaultPartition : requested; }
 
 }  // namespace
 
@@ -223,6 +260,73 @@ int pa_prefill_chunk(const pa_cache* cache, const void* q, void* out, const int3
   a.max_q_len = max_q_len;
   a.max_context_len = max_context_len;
   return hip_status(pa::launch_prefill(a, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"
+
+extern "C" {
+
+size_t pa_decode_grouped_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                                         int32_t max_context_len, int32_t partition_size) {
+  const int32_t part = grouped_partition(partition_size);
+  if (num_seqs <= 0 || num_q_heads <= 0 || head_dim <= 0 || max_context_len < 0 || part <= 0) return 0;
+  return grouped_layout(num_seqs, num_q_heads, head_dim, max_context_len, part).total;
+}
+
+int pa_decode_grouped(const pa_cache* cache, const void* q, void* out, int32_t num_seqs, int32_t num_q_heads,
+                      const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
+                      int32_t max_context_len, float scale, const int32_t* group_start, int32_t num_groups,
+                      int32_t partition_size, void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = check_cache(cache);
+  if (rc != PA_OK) return rc;
+  if (cache->dtype == PA_F32) return PA_EUNSUPPORTED;
+  int32_t group = 0;
+  if ((rc = check_group(cache, num_q_heads, &group)) != PA_OK) return rc;
+  if ((rc = check_scale(scale)) != PA_OK) return rc;
+  if (num_seqs < 0 || num_groups < 0 || max_blocks_per_seq <= 0 || max_context_len < 0) return PA_EINVAL;
+  if (static_cast<int64_t>(max_context_len) > static_cast<int64_t>(max_blocks_per_seq) * cache->block_size)
+    return PA_EINVAL;
+  const int32_t part = grouped_partition(partition_size);
+  if (part <= 0 || part % 32 != 0 || part % cache->block_size != 0 || part / cache->block_size > 64) return PA_EINVAL;
+  if (num_seqs > pa::kGroupedMaxSeqs) return PA_EUNSUPPORTED;
+  if (num_seqs == 0) return PA_OK;
+  if (!q || !out || !block_tables || !context_lens || (num_groups > 0 && !group_start)) return PA_EINVAL;
+  const GroupedLayout L = grouped_layout(num_seqs, num_q_heads, cache->head_dim, max_context_len, part);
+  if (!workspace || workspace_bytes < L.total) return PA_EWORKSPACE;
+  char* ws = static_cast<char*>(workspace);
+
+  pa::GroupedArgs g{};
+  pa::DecodeArgs& a = g.d;
+  a.q = q;
+  a.out = out;
+  a.k_cache = cache->k_cache;
+  a.v_cache = cache->v_cache;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.ws_ml = reinterpret_cast<float*>(ws + L.ml);
+  a.ws_o = reinterpret_cast<float*>(ws + L.o);
+  a.ws_items = reinterpret_cast<int32_t*>(ws + L.suf_items);
+  a.ws_count = reinterpret_cast<int32_t*>(ws + L.counts);
+  a.scale = scale;
+  a.dtype = cache->dtype;
+  a.head_dim = cache->head_dim;
+  a.block_size = cache->block_size;
+  a.group = group;
+  a.num_seqs = num_seqs;
+  a.num_kv_heads = cache->num_kv_heads;
+  a.num_blocks = cache->num_blocks;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.max_context_len = max_context_len;
+  a.part_tokens = part;
+  a.num_parts = static_cast<int32_t>(L.slots);
+  g.group_start = num_groups > 0 ? group_start : nullptr;
+  g.num_groups = num_groups;
+  g.seq_start = reinterpret_cast<int32_t*>(ws + L.seq_start);
+  g.slot_base = reinterpret_cast<int32_t*>(ws + L.slot_base);
+  g.nslots = reinterpret_cast<int32_t*>(ws + L.nslots);
+  g.pre_items = reinterpret_cast<int32_t*>(ws + L.pre_items);
+  g.pre_count = a.ws_count + 1;
+  return hip_status(pa::launch_decode_grouped(g, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

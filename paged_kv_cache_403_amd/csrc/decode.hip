@@ -174,6 +174,8 @@ struct DecodeParams {
   const int32_t* ctx_lens;
   const int32_t* items;    // persistent kernel: (sequence, partition) pairs
   const int32_t* n_items;  // persistent kernel: number of pairs
+  const int32_t* seq_start;  // grouped decode: first token of each sequence's own part (else null)
+  const int32_t* slot_base;  // grouped decode: workspace slot of each sequence's first own partition
   void* out;
   float* ws_ml;
   float* ws_o;
@@ -197,10 +199,12 @@ __device__ __forceinline__ int clamp_len(int L, int max_context) {
 // tokens of partition `part` (the whole context when it is the only one).
 // L is the sequence's clamped context length.  With one partition the
 // normalised rows are written to `out`, otherwise (m, l, o) partials go to
-// the workspace.
+// the workspace.  Grouped decode (start > 0 or `partial`): the partitions
+// cover tokens start..L-1 and always leave partials, at slot
+// slot0 + part, for the merge with the shared prefix's partials.
 template <typename ST, int D, int BS, int G>
 __device__ __forceinline__ void decode_item(DecodeLds<G, D, BS>& sh, const DecodeParams& P, int s, int kvh,
-                                            int part, int L) {
+                                            int part, int L, int start = 0, int slot0 = 0, bool partial = false) {
   using S = DecodeShape<ST, D, BS, G>;
   constexpr int VEC = S::VEC, LPR = S::LPR, RPI = S::RPI, NI = S::NI, NV = S::NV, NRED = S::NRED,
                 CPD = S::CPD;
@@ -221,8 +225,8 @@ __device__ __forceinline__ void decode_item(DecodeLds<G, D, BS>& sh, const Decod
   const int row = lane / LPR;  // K row within a load instruction
   const int tg = lane % CPD;   // V token group: tokens tg*VEC .. tg*VEC+VEC-1
 
-  const int nparts = (L + part_tokens - 1) / part_tokens;
-  if (L == 0) {
+  const int nparts = L > start ? (L - start + part_tokens - 1) / part_tokens : 0;
+  if (L == 0 && !partial) {
     if (part == 0) {
       for (int e = tid; e < G * D; e += kThreads)
         out[(static_cast<int64_t>(s) * num_q_heads + kvh * G) * D + e] = narrow<ST>(0.f);
@@ -231,8 +235,9 @@ __device__ __forceinline__ void decode_item(DecodeLds<G, D, BS>& sh, const Decod
   }
   if (part >= nparts) return;
 
-  const int tok_end = min(L, (part + 1) * part_tokens);
-  const int blk_begin = part * (part_tokens / BS);
+  const int tok_begin = start + part * part_tokens;  // a multiple of BS
+  const int tok_end = min(L, tok_begin + part_tokens);
+  const int blk_begin = tok_begin / BS;
   const int nb = (tok_end + BS - 1) / BS - blk_begin;  // blocks in this partition
 
   // where this lane's reduced scores sit: head h_own, tokens i*RPI + row
@@ -435,10 +440,10 @@ __device__ __forceinline__ void decode_item(DecodeLds<G, D, BS>& sh, const Decod
       }
     }
     const int64_t qh = static_cast<int64_t>(s) * num_q_heads + kvh * G + h;
-    if (nparts == 1) {
+    if (nparts == 1 && !partial) {
       out[qh * D + d] = narrow<ST>(num / den);
     } else {
-      const int64_t pidx = qh * P.max_parts + part;
+      const int64_t pidx = qh * P.max_parts + slot0 + part;
       P.ws_o[pidx * D + d] = num / den;
       if (d == 0) {
         P.ws_ml[2 * pidx] = M;
@@ -475,7 +480,10 @@ __global__ __launch_bounds__(kThreads) void decode_persistent_kernel(DecodeParam
     const int part = __builtin_amdgcn_readfirstlane(P.items[2 * item + 1]);
     const int L = clamp_len(P.ctx_lens[s], P.max_context);
     __syncthreads();  // the previous item's LDS merge is complete
-    decode_item<ST, D, BS, G>(sh, P, s, kvh, part, L);
+    const bool grouped = P.seq_start != nullptr;
+    const int start = grouped ? __builtin_amdgcn_readfirstlane(P.seq_start[s]) : 0;
+    const int slot0 = grouped ? __builtin_amdgcn_readfirstlane(P.slot_base[s]) : 0;
+    decode_item<ST, D, BS, G>(sh, P, s, kvh, part, L, start, slot0, grouped);
   }
 }
 
@@ -526,38 +534,53 @@ __global__ __launch_bounds__(kPlanThreads) void decode_plan_kernel(const int32_t
   if (tid == 0) *n_items = carry;
 }
 
-// Log-sum-exp merge of the partitions of one (sequence, q head).
+// Log-sum-exp merge of the partitions of one (sequence, q head).  nslots:
+// grouped decode's per-sequence slot count (null: the partitions of the
+// context, and single-partition rows were written directly).  Slots with no
+// keys (l = 0) carry no weight; a row with none is written as zeros.
 template <typename ST, int D>
 __global__ __launch_bounds__(D) void decode_reduce_kernel(const float* __restrict__ ws_ml,
                                                           const float* __restrict__ ws_o,
                                                           const int32_t* __restrict__ ctx_lens, int max_context,
                                                           int part_tokens, int max_parts, int num_q_heads,
+                                                          const int32_t* __restrict__ nslots,
                                                           typename ST::elem* __restrict__ out) {
   extern __shared__ float w_sh[];  // [max_parts]
   __shared__ float M_sh;
   const int h = blockIdx.x, s = blockIdx.y, d = threadIdx.x;
-  const int L = clamp_len(ctx_lens[s], max_context);
-  const int np = (L + part_tokens - 1) / part_tokens;
-  if (np <= 1) return;  // written directly by the decode kernel
+  int np;
+  if (nslots) {
+    np = min(max(nslots[s], 0), max_parts);
+  } else {
+    const int L = clamp_len(ctx_lens[s], max_context);
+    np = (L + part_tokens - 1) / part_tokens;
+    if (np <= 1) return;  // written directly by the decode kernel
+  }
   const int64_t qh = static_cast<int64_t>(s) * num_q_heads + h;
   const float* ml = ws_ml + 2 * qh * max_parts;
   if (d == 0) {
     float M = -INFINITY;
-    for (int p = 0; p < np; ++p) M = fmaxf(M, ml[2 * p]);
+    for (int p = 0; p < np; ++p)
+      if (ml[2 * p + 1] > 0.f) M = fmaxf(M, ml[2 * p]);
     M_sh = M;
   }
   __syncthreads();
   const float M = M_sh;
-  for (int p = d; p < np; p += D) w_sh[p] = ml[2 * p + 1] * __builtin_amdgcn_exp2f(ml[2 * p] - M);
+  for (int p = d; p < np; p += D) {
+    const float l = ml[2 * p + 1];
+    w_sh[p] = l > 0.f ? l * __builtin_amdgcn_exp2f(ml[2 * p] - M) : 0.f;
+  }
   __syncthreads();
   const float* o = ws_o + qh * max_parts * D + d;
   float num = 0.f, den = 0.f;
   for (int p = 0; p < np; ++p) {
     const float w = w_sh[p];
-    num = __builtin_fmaf(w, o[static_cast<int64_t>(p) * D], num);
-    den += w;
+    if (w > 0.f) {
+      num = __builtin_fmaf(w, o[static_cast<int64_t>(p) * D], num);
+      den += w;
+    }
   }
-  out[qh * D + d] = narrow<ST>(num / den);
+  out[qh * D + d] = narrow<ST>(den > 0.f ? num / den : 0.f);
 }
 
 // Workgroups of the persistent kernel: as many as fit on the device at once
@@ -603,14 +626,20 @@ hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t st) {
   P.num_kv_heads = a.num_kv_heads;
   P.part_tokens = a.part_tokens;
   P.max_parts = a.num_parts;
-  if (a.num_parts <= 1) {
+  P.seq_start = a.seq_start;
+  P.slot_base = a.slot_base;
+  const bool grouped = a.seq_start != nullptr;
+  if (a.num_parts <= 1 && !grouped) {
     hipLaunchKernelGGL((decode_kernel<ST, D, BS, G>), dim3(1, a.num_kv_heads, a.num_seqs), dim3(kThreads), 0, st, P);
     return hipGetLastError();
   }
-  hipLaunchKernelGGL(decode_plan_kernel, dim3(1), dim3(kPlanThreads), 0, st, a.context_lens, a.num_seqs,
-                     a.max_context_len, a.part_tokens, a.ws_items, a.ws_count);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  hipError_t e = hipSuccess;
+  if (!grouped) {
+    hipLaunchKernelGGL(decode_plan_kernel, dim3(1), dim3(kPlanThreads), 0, st, a.context_lens, a.num_seqs,
+                       a.max_context_len, a.part_tokens, a.ws_items, a.ws_count);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   const int64_t upper = static_cast<int64_t>(a.num_seqs) * a.num_parts * a.num_kv_heads;
   const int grid = static_cast<int>(std::min<int64_t>(upper, persistent_grid<ST, D, BS, G>()));
   hipLaunchKernelGGL((decode_persistent_kernel<ST, D, BS, G>), dim3(grid), dim3(kThreads), 0, st, P);
@@ -619,7 +648,8 @@ hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t st) {
   const int num_q_heads = a.num_kv_heads * G;
   hipLaunchKernelGGL((decode_reduce_kernel<ST, D>), dim3(num_q_heads, a.num_seqs), dim3(D),
                      a.num_parts * sizeof(float), st, a.ws_ml, a.ws_o, a.context_lens,
-                     a.max_context_len, a.part_tokens, a.num_parts, num_q_heads, static_cast<typename ST::elem*>(a.out));
+                     a.max_context_len, a.part_tokens, a.num_parts, num_q_heads, a.nslots,
+                     static_cast<typename ST::elem*>(a.out));
   return hipGetLastError();
 }
 

@@ -1,0 +1,550 @@
+// Prefix-grouped decode: sequences of one batch that share the physical
+// blocks of a prompt prefix read those blocks once for all of them.
+//
+// Within a batch, requests forked from one prompt keep the prompt's blocks
+// by reference and only copy a block on their first write to it
+// (lshu.cn/news/11644, "收益分析"); the same page names prefix caching
+// within the batch as one of the few decode-side savings, decode being
+// bound by the KV bytes it reads ("性能关键路径与瓶颈").  Plain decode still
+// reads the shared blocks once per sequence.  Here the decode of a step is
+// split by keys, which attention allows because partial results over
+// disjoint key sets combine exactly through their log-sum-exp (the same
+// merge as split-K decode):
+//
+//  * a planner (one workgroup) cuts the batch into chunks of consecutive
+//    sequences -- the caller's groups, split so that a chunk's q rows
+//    (members x q heads per KV head) fit one 32-row matrix tile -- and
+//    measures on the block tables themselves how many leading full blocks
+//    each member has in common with the chunk's longest sequence (its
+//    reference).  The caller's grouping is only a hint: a sequence that
+//    shares nothing gets a shared length of 0 and is decoded alone;
+//  * the shared-prefix kernel takes one (chunk, KV head, partition) per
+//    workgroup and runs all of the chunk's rows over the reference's
+//    blocks on the matrix cores: S^T = K Q^T and O^T = V^T P^T with
+//    v_mfma_f32_32x32x16, each row masked at its own shared length;
+//  * the suffix of every sequence (its tokens from the shared length on) is
+//    decoded by the split decode kernel, and one merge combines prefix and
+//    suffix partials per (sequence, q head).
+//
+// The result equals plain decode over each sequence's own table: a member
+// reads only blocks whose table entries equal its own.
+#include <algorithm>
+#include <atomic>
+
+#include "common.h"
+#include "launch.h"
+#include "mfma.h"
+
+namespace pa {
+
+namespace {
+
+constexpr int kPlanThreads = 1024;
+constexpr int kPlanWaves = kPlanThreads / 64;
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kTile = 32;  // keys per matrix tile
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ int clamp_len(int L, int max_context) { return L < 0 ? 0 : (L > max_context ? max_context : L); }
+
+// Inclusive scan of x over the workgroup (kPlanThreads threads) under the
+// associative `op`; `total` receives the reduction over all threads.
+template <typename T, typename Op>
+__device__ __forceinline__ T block_scan(T x, T ident, Op op, T* wave_tot, T& total) {
+  const int lane = lane_id(), wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const T y = __shfl_up(x, o, 64);
+    if (lane >= o) x = op(x, y);
+  }
+  if (lane == 63) wave_tot[wave] = x;
+  __syncthreads();
+  T before = ident, all = ident;
+#pragma unroll
+  for (int w = 0; w < kPlanWaves; ++w) {
+    const T t = wave_tot[w];
+    if (w < wave) before = op(before, t);
+    all = op(all, t);
+  }
+  __syncthreads();  // wave_tot is rewritten by the next scan
+  total = all;
+  return op(before, x);
+}
+
+struct PlanParams {
+  const int32_t* group_start;
+  const int32_t* tables;
+  const int32_t* ctx_lens;
+  int32_t* seq_start;
+  int32_t* slot_base;
+  int32_t* nslots;
+  int32_t* pre_items;
+  int32_t* pre_count;
+  int32_t* suf_items;
+  int32_t* suf_count;
+  int num_groups, num_seqs, max_context, max_blocks, block_size, part_tokens, chunk_max;
+};
+
+__global__ __launch_bounds__(kPlanThreads) void grouped_plan_kernel(PlanParams P) {
+  __shared__ int ref_of[kGroupedMaxSeqs];  // chunk start, then the chunk's reference
+  __shared__ int share[kGroupedMaxSeqs];   // shared tokens (block multiple); a reference holds its chunk's max
+  __shared__ int len[kGroupedMaxSeqs];     // clamped context lengths
+  __shared__ int wtot_i[kPlanWaves];
+  __shared__ long long wtot_l[kPlanWaves];
+  const int S = P.num_seqs, tid = threadIdx.x, BS = P.block_size;
+
+  // 1. run starts: sequence 0 and every in-range group start
+  for (int s = tid; s < S; s += kPlanThreads) {
+    ref_of[s] = s == 0;
+    len[s] = clamp_len(P.ctx_lens[s], P.max_context);
+  }
+  __syncthreads();
+  for (int g = tid; g < P.num_groups; g += kPlanThreads) {
+    const int st = P.group_start[g];
+    if (st > 0 && st < S) ref_of[st] = 1;
+  }
+  __syncthreads();
+
+  // 2. run start of each sequence (running max of flagged indices), then
+  //    runs cut into chunks of at most chunk_max members
+  int carry = 0;
+  for (int base = 0; base < S; base += kPlanThreads) {
+    const int s = base + tid;
+    const int v = (s < S && ref_of[s]) ? s : 0;
+    int pass_max = 0;
+    const int run = max(carry, block_scan(v, 0, [](int a, int b) { return max(a, b); }, wtot_i, pass_max));
+    if (s < S) ref_of[s] = run + ((s - run) / P.chunk_max) * P.chunk_max;
+    carry = max(carry, pass_max);
+  }
+  __syncthreads();
+
+  // 3. each chunk's reference: its longest member (the first of equals),
+  //    found by the chunk's first sequence and parked in `share` (not yet
+  //    in use), then copied to every member
+  for (int s = tid; s < S; s += kPlanThreads) {
+    if (ref_of[s] != s) continue;
+    int n = 1, best = s;
+    while (n < P.chunk_max && s + n < S && ref_of[s + n] == s) {
+      if (len[s + n] > len[best]) best = s + n;
+      ++n;
+    }
+    share[s] = best;
+  }
+  __syncthreads();
+  for (int s = tid; s < S; s += kPlanThreads) ref_of[s] = share[ref_of[s]];
+  __syncthreads();
+
+  // 4. leading full blocks each member has in common with its reference
+  for (int s = tid; s < S; s += kPlanThreads) {
+    const int ref = ref_of[s];
+    int common = 0;
+    if (ref != s) {
+      const int lim = min(len[s], len[ref]) / BS;
+      const int32_t* a = P.tables + static_cast<int64_t>(s) * P.max_blocks;
+      const int32_t* b = P.tables + static_cast<int64_t>(ref) * P.max_blocks;
+      while (common < lim) {
+        int diff = 8;
+#pragma unroll
+        for (int e = 7; e >= 0; --e) {
+          const int j = common + e;
+          if (j >= lim || a[j] != b[j]) diff = e;
+        }
+        common += diff;
+        if (diff < 8) break;
+      }
+    }
+    share[s] = common * BS;
+  }
+  __syncthreads();
+  for (int s = tid; s < S; s += kPlanThreads) {
+    const int ref = ref_of[s];
+    if (ref != s && share[s] > 0) atomicMax(&share[ref], share[s]);
+  }
+  __syncthreads();
+
+  // 5. work lists.  Prefix items (first member, members, partition,
+  //    reference) for each chunk with a shared prefix, emitted by the
+  //    chunk's first sequence; suffix items (sequence, partition) over each
+  //    sequence's own tokens.  Both counts are scanned at once as the two
+  //    halves of a 64-bit value.
+  long long carry2 = 0;
+  const int PT = P.part_tokens;
+  for (int base = 0; base < S; base += kPlanThreads) {
+    const int s = base + tid;
+    int own_pre = 0, np = 0, sh = 0, sb = 0, ref = 0;
+    if (s < S) {
+      ref = ref_of[s];
+      sh = share[s];
+      sb = (share[ref] + PT - 1) / PT;
+      if (s == 0 || ref_of[s - 1] != ref) own_pre = sb;  // first of its chunk
+      np = len[s] > sh ? (len[s] - sh + PT - 1) / PT : 0;
+    }
+    const long long packed = static_cast<long long>(own_pre) | (static_cast<long long>(np) << 32);
+    long long total = 0;
+    const long long incl = block_scan(packed, 0LL, [](long long a, long long b) { return a + b; }, wtot_l, total);
+    const long long excl = carry2 + incl - packed;
+    const int pfirst = static_cast<int>(excl & 0xffffffffLL);
+    const int sfirst = static_cast<int>(excl >> 32);
+    if (s < S) {
+      P.seq_start[s] = sh;
+      P.slot_base[s] = sb;
+      P.nslots[s] = sb + np;
+      if (own_pre > 0) {
+        int n = 1;
+        while (n < P.chunk_max && s + n < S && ref_of[s + n] == ref) ++n;
+        for (int p = 0; p < own_pre; ++p) {
+          int32_t* it = P.pre_items + 4 * (pfirst + p);
+          it[0] = s;
+          it[1] = n;
+          it[2] = p;
+          it[3] = ref;
+        }
+      }
+      for (int p = 0; p < np; ++p) {
+        P.suf_items[2 * (sfirst + p)] = s;
+        P.suf_items[2 * (sfirst + p) + 1] = p;
+      }
+    }
+    carry2 += total;
+  }
+  if (tid == 0) {
+    *P.pre_count = static_cast<int>(carry2 & 0xffffffffLL);
+    *P.suf_count = static_cast<int>(carry2 >> 32);
+  }
+}
+
+struct PrefixParams {
+  const void* q;
+  const void* kc;
+  const void* vc;
+  const int32_t* tables;
+  const int32_t* shares;  // per sequence; a reference holds its chunk's maximum
+  // items: (first member, members, partition, reference)
+  const int32_t* items;
+  const int32_t* n_items;
+  float* ws_ml;
+  float* ws_o;
+  float scale_log2;
+  int32_t max_blocks, num_blocks, num_kv_heads, part_tokens, max_parts;
+};
+
+template <int D>
+struct PrefixLds {
+  float o[kWaves][32][D + 4];  // per-wave unnormalised O rows
+  float m[kWaves][32];
+  float l[kWaves][32];
+  float c[kWaves][32];  // merge weights
+  float inv[32];
+};
+
+// One (chunk, KV head, partition) per iteration, keys read through the
+// reference's table.  Rows r = member * G + h; wave w takes key tiles
+// w, w + 4, ... of the partition.
+template <typename ST, int D, int BS, int G>
+__global__ __launch_bounds__(kThreads, 2) void grouped_prefix_kernel(PrefixParams P) {
+  static_assert(D % 32 == 0 && D >= 64, "head_dim");
+  static_assert(BS == 16 || BS == 32, "block size");
+  constexpr int KS = D / 16;  // contraction steps of S^T = K Q^T
+  constexpr int DT = D / 32;  // 32-wide column tiles of O^T
+  constexpr int TB = kTile / BS;  // blocks per key tile
+  using elem = typename ST::elem;
+  __shared__ PrefixLds<D> sh;
+
+  const elem* __restrict__ q = static_cast<const elem*>(P.q);
+  const elem* __restrict__ kc = static_cast<const elem*>(P.kc);
+  const elem* __restrict__ vc = static_cast<const elem*>(P.vc);
+  const int hk = P.num_kv_heads, hq = hk * G;
+  const int lane = lane_id();
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r = lane & 31;  // row of this lane (B operand column / accumulator column)
+  const int hf = lane >> 5;  // half: k-elements 8*hf.. of each step
+  const int64_t blk_stride = static_cast<int64_t>(hk) * BS * D;
+  const int n_work = *P.n_items * hk;
+
+  for (int it = blockIdx.x; it < n_work; it += gridDim.x) {
+    const int item = it / hk, kvh = it - item * hk;
+    const int first = __builtin_amdgcn_readfirstlane(P.items[4 * item]);
+    const int members = __builtin_amdgcn_readfirstlane(P.items[4 * item + 1]);
+    const int part = __builtin_amdgcn_readfirstlane(P.items[4 * item + 2]);
+    const int ref = __builtin_amdgcn_readfirstlane(P.items[4 * item + 3]);
+    const int share_max = __builtin_amdgcn_readfirstlane(P.shares[ref]);
+    const int tok0 = part * P.part_tokens;
+    const int tok1 = min(share_max, tok0 + P.part_tokens);
+    const int ntiles = (tok1 - tok0 + kTile - 1) / kTile;
+    const int mem = r / G, hh = r - mem * G;
+    const bool row_ok = mem < members;
+    const int row_lim = row_ok ? P.shares[first + mem] : 0;
+
+    // Q^T as the B operand: row r, dims 8 * (2k + hf) ..
+    u32x4 qb[KS];
+    const elem* qrow = q + (static_cast<int64_t>(first + (row_ok ? mem : 0)) * hq + kvh * G + hh) * D + 8 * hf;
+#pragma unroll
+    for (int k = 0; k < KS; ++k) qb[k] = row_ok ? load16(qrow + 16 * k) : u32x4{0, 0, 0, 0};
+
+    // the partition's block ids, one per lane (64 * BS >= part_tokens)
+    const int32_t* trow = P.tables + static_cast<int64_t>(ref) * P.max_blocks + tok0 / BS;
+    const int nblk = (tok1 - tok0 + BS - 1) / BS;
+    int bid = lane < nblk ? trow[lane] : 0;
+    bid = (bid >= 0 && bid < P.num_blocks) ? bid : 0;
+
+    f32x16 o[DT];
+#pragma unroll
+    for (int t = 0; t < DT; ++t) o[t] = f32x16{};
+    float m_run = -INFINITY, l_run = 0.f;
+
+    // K rows in A-operand order (key_perm) and V^T rows for the PV steps
+    const int kkey = key_perm(r);
+    auto load_tile = [&](int t, u32x4* kr, u32x4* vr) __attribute__((always_inline)) {
+      const int kb = __shfl(bid, t * TB + kkey / BS, 64);
+      const elem* kp = kc + static_cast<int64_t>(kb) * blk_stride + (static_cast<int64_t>(kvh) * BS + kkey % BS) * D +
+                       8 * hf;
+#pragma unroll
+      for (int k = 0; k < KS; ++k) kr[k] = load16_nt(kp + 16 * k);
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const int key = 16 * k + 8 * hf;  // first of this lane's 8 keys in the step
+        const int vb = __shfl(bid, t * TB + key / BS, 64);
+        const elem* vp = vc + static_cast<int64_t>(vb) * blk_stride + (static_cast<int64_t>(kvh) * D + r) * BS + key % BS;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) vr[dt * 2 + k] = load16_nt(vp + dt * 32 * BS);
+      }
+    };
+
+    // One key tile: scores, online softmax, PV.  P enters the PV products as
+    // two 16-bit parts (nearest value and remainder), so the weights keep
+    // about 16 bits: rows with only a few shared keys can have outputs as
+    // large as single V entries, where one 16-bit rounding of P would show.
+    auto compute = [&](int t, const u32x4* kr, const u32x4* vr) __attribute__((always_inline)) {
+      f32x16 s = f32x16{};
+#pragma unroll
+      for (int k = 0; k < KS; ++k) s = mfma32<ST>(kr[k], qb[k], s);
+
+      const int key0 = tok0 + t * kTile;
+      float x[16];
+      float tmax = -INFINITY;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int key = key0 + key_perm(8 * (e >> 2) + 4 * hf + (e & 3));
+        x[e] = key < row_lim ? s[e] * P.scale_log2 : -INFINITY;
+        tmax = fmaxf(tmax, x[e]);
+      }
+      tmax = halves_max(tmax);
+      const float m_new = fmaxf(m_run, tmax);
+      const float m_use = m_new == -INFINITY ? 0.f : m_new;
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+      float psum = 0.f;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        x[e] = __builtin_amdgcn_exp2f(x[e] - m_use);
+        psum += x[e];
+      }
+      l_run = l_run * alpha + psum;
+      m_run = m_new;
+      u32x4 hi[2], lo[2];
+#pragma unroll
+      for (int k = 0; k < 2; ++k)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const float a0 = x[8 * k + 2 * c], a1 = x[8 * k + 2 * c + 1];
+          const uint32_t h = pack2<ST>(a0, a1);
+          float h0, h1;
+          widen2<ST>(h, h0, h1);
+          hi[k][c] = h;
+          lo[k][c] = pack2<ST>(a0 - h0, a1 - h1);
+        }
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        o[dt] *= alpha;
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+          o[dt] = mfma32<ST>(vr[dt * 2 + k], hi[k], o[dt]);
+          o[dt] = mfma32<ST>(vr[dt * 2 + k], lo[k], o[dt]);
+        }
+      }
+    };
+
+    // wave w takes tiles w, w + 4, ...; two register buffers alternate, the
+    // next tile's loads in flight while the current one is computed (at the
+    // end the last tile is requested again: a cache hit)
+    const int my_tiles = ntiles > wave ? (ntiles - wave + kWaves - 1) / kWaves : 0;
+    const int last = wave + (my_tiles - 1) * kWaves;
+    u32x4 k0[KS], v0[2 * DT], k1[KS], v1[2 * DT];
+    if (my_tiles > 0) load_tile(wave, k0, v0);
+    for (int i = 0; i < my_tiles; i += 2) {
+      const int t = wave + i * kWaves;
+      load_tile(min(t + kWaves, last), k1, v1);
+      compute(t, k0, v0);
+      if (i + 1 < my_tiles) {
+        load_tile(min(t + 2 * kWaves, last), k0, v0);
+        compute(t + kWaves, k1, v1);
+      }
+    }
+
+    // merge the four wavefronts' states of each row
+    const float l_tot = halves_sum(l_run);
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        float4 v4 = {o[dt][4 * j], o[dt][4 * j + 1], o[dt][4 * j + 2], o[dt][4 * j + 3]};
+        *reinterpret_cast<float4*>(&sh.o[wave][r][dt * 32 + 8 * j + 4 * hf]) = v4;
+      }
+    if (hf == 0) {
+      sh.m[wave][r] = m_run;
+      sh.l[wave][r] = l_tot;
+    }
+    __syncthreads();
+    const int tid = threadIdx.x;
+    if (tid < 32) {
+      float M = -INFINITY;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w)
+        if (sh.l[w][tid] > 0.f) M = fmaxf(M, sh.m[w][tid]);
+      float L = 0.f;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        const float c = sh.l[w][tid] > 0.f ? __builtin_amdgcn_exp2f(sh.m[w][tid] - M) : 0.f;
+        sh.c[w][tid] = c;
+        L += c * sh.l[w][tid];
+      }
+      sh.inv[tid] = L > 0.f ? 1.f / L : 0.f;
+      const int mm = tid / G;
+      if (mm < members) {
+        const int64_t pidx = (static_cast<int64_t>(first + mm) * hq + kvh * G + tid % G) * P.max_parts + part;
+        P.ws_ml[2 * pidx] = M;
+        P.ws_ml[2 * pidx + 1] = L;
+      }
+    }
+    __syncthreads();
+    for (int e = tid; e < 32 * D; e += kThreads) {
+      const int row = e / D, d = e - row * D;
+      const int mm = row / G;
+      if (mm >= members) continue;
+      float acc = 0.f;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) acc = __builtin_fmaf(sh.c[w][row], sh.o[w][row][d], acc);
+      const int64_t pidx = (static_cast<int64_t>(first + mm) * hq + kvh * G + row % G) * P.max_parts + part;
+      P.ws_o[pidx * D + d] = acc * sh.inv[row];
+    }
+    __syncthreads();  // LDS is reused by the next item
+  }
+}
+
+// Workgroups of the prefix kernel that fit on the device at once.
+template <typename ST, int D, int BS, int G>
+int prefix_grid() {
+  constexpr int kMaxDev = 64;
+  static std::atomic<int> cached[kMaxDev];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) dev = 0;
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    int cus = 0, per_cu = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &per_cu, reinterpret_cast<const void*>(&grouped_prefix_kernel<ST, D, BS, G>), kThreads, 0) !=
+            hipSuccess ||
+        per_cu <= 0)
+      per_cu = 1;
+    n = cus * per_cu;
+    cached[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
+template <typename ST, int D, int BS, int G>
+hipError_t launch_t(const GroupedArgs& g, hipStream_t st) {
+  const DecodeArgs& a = g.d;
+  PlanParams pp{};
+  pp.group_start = g.group_start;
+  pp.tables = a.block_tables;
+  pp.ctx_lens = a.context_lens;
+  pp.seq_start = g.seq_start;
+  pp.slot_base = g.slot_base;
+  pp.nslots = g.nslots;
+  pp.pre_items = g.pre_items;
+  pp.pre_count = g.pre_count;
+  pp.suf_items = a.ws_items;
+  pp.suf_count = a.ws_count;
+  pp.num_groups = g.num_groups;
+  pp.num_seqs = a.num_seqs;
+  pp.max_context = a.max_context_len;
+  pp.max_blocks = a.max_blocks_per_seq;
+  pp.block_size = BS;
+  pp.part_tokens = a.part_tokens;
+  pp.chunk_max = 32 / G;
+  hipLaunchKernelGGL(grouped_plan_kernel, dim3(1), dim3(kPlanThreads), 0, st, pp);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+
+  PrefixParams P{};
+  P.q = a.q;
+  P.kc = a.k_cache;
+  P.vc = a.v_cache;
+  P.tables = a.block_tables;
+  P.shares = g.seq_start;
+  P.items = g.pre_items;
+  P.n_items = g.pre_count;
+  P.ws_ml = a.ws_ml;
+  P.ws_o = a.ws_o;
+  P.scale_log2 = a.scale * kLog2e;
+  P.max_blocks = a.max_blocks_per_seq;
+  P.num_blocks = a.num_blocks;
+  P.num_kv_heads = a.num_kv_heads;
+  P.part_tokens = a.part_tokens;
+  P.max_parts = a.num_parts;
+  const int64_t parts = (static_cast<int64_t>(a.max_context_len) + a.part_tokens - 1) / a.part_tokens;
+  const int64_t upper = std::max<int64_t>(1, (a.num_seqs / 2) * parts * a.num_kv_heads);
+  const int grid = static_cast<int>(std::min<int64_t>(upper, prefix_grid<ST, D, BS, G>()));
+  hipLaunchKernelGGL((grouped_prefix_kernel<ST, D, BS, G>), dim3(grid), dim3(kThreads), 0, st, P);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+
+  DecodeArgs d = a;
+  d.seq_start = g.seq_start;
+  d.slot_base = g.slot_base;
+  d.nslots = g.nslots;
+  return launch_decode(d, st);
+}
+
+template <typename ST, int D, int BS>
+hipError_t by_group(const GroupedArgs& a, hipStream_t st) {
+  switch (a.d.group) {
+    case 1: return launch_t<ST, D, BS, 1>(a, st);
+    case 2: return launch_t<ST, D, BS, 2>(a, st);
+    case 4: return launch_t<ST, D, BS, 4>(a, st);
+    case 8: return launch_t<ST, D, BS, 8>(a, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <typename ST, int D>
+hipError_t by_block(const GroupedArgs& a, hipStream_t st) {
+  switch (a.d.block_size) {
+    case 16: return by_group<ST, D, 16>(a, st);
+    case 32: return by_group<ST, D, 32>(a, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <typename ST>
+hipError_t by_dim(const GroupedArgs& a, hipStream_t st) {
+  switch (a.d.head_dim) {
+    case 64: return by_block<ST, 64>(a, st);
+    case 128: return by_block<ST, 128>(a, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_decode_grouped(const GroupedArgs& a, hipStream_t st) {
+  switch (a.d.dtype) {
+    case 1: return by_dim<F16>(a, st);
+    case 2: return by_dim<BF16>(a, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace pa

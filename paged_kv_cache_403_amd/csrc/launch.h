@@ -23,8 +23,32 @@ struct DecodeArgs {
   int32_t num_seqs, num_kv_heads, num_blocks, max_blocks_per_seq;
   int32_t max_context_len;  // host bound; device lengths are clamped to it
   int32_t part_tokens;  // tokens per partition (multiple of block_size)
-  int32_t num_parts;    // ceil(max_context_len / part_tokens)
+  int32_t num_parts;    // ceil(max_context_len / part_tokens); grouped: workspace slots per row
+  // Grouped decode (all null otherwise): each sequence's own tokens start at
+  // seq_start[s]; its partials go to slots slot_base[s].. and the merge reads
+  // nslots[s] slots.  ws_items / ws_count then come from the grouped planner.
+  const int32_t* seq_start;
+  const int32_t* slot_base;
+  const int32_t* nslots;
 };
+
+// Prefix-grouped decode: the planner and shared-prefix kernel (grouped.hip)
+// followed by the suffix partitions and merge of launch_decode.
+struct GroupedArgs {
+  DecodeArgs d;                // num_parts = slots per row, ws_* as below
+  const int32_t* group_start;  // [num_groups + 1] hint: runs of sequences that may share a prefix
+  int32_t num_groups;
+  int32_t* seq_start;   // [S]  shared tokens of each sequence (its own part starts there)
+  int32_t* slot_base;   // [S]  prefix slots of its chunk
+  int32_t* nslots;      // [S]
+  int32_t* pre_items;   // [S * ceil(max_context / part)][4]  (first member, members, partition, reference)
+  int32_t* pre_count;   // [1]
+};
+
+// Sequences one grouped-decode planner workgroup can hold in LDS.
+constexpr int32_t kGroupedMaxSeqs = 4096;
+
+hipError_t launch_decode_grouped(const GroupedArgs& a, hipStream_t st);
 
 struct PrefillArgs {
   const void* q;

@@ -28,10 +28,12 @@ class ProductResult:
 
 
 def run_step(wl, fill=SENTINEL, free_order=None, partition_size=0, device="cuda", keep_pool=True,
-             prefill_all=False, return_cache=False):
+             prefill_all=False, return_cache=False, grouped=False, group_start=None):
     """One step of `wl`: setup appends, the step's copies and appends, then
     decode for one-token sequences and chunked prefill for the others (or
-    prefill for all when prefill_all)."""
+    prefill for all when prefill_all).  grouped: decode through the
+    prefix-grouped entry point with the hint `group_start` (int32 starts
+    over the decode sequences, None for no hint)."""
     sp = wl.spec
     order = wl.free_order if free_order is None else free_order
     cache = PagedKVCache(sp.num_blocks, sp.num_kv_heads, sp.block_size, sp.head_dim, sp.dtype, device, order,
@@ -58,9 +60,16 @@ def run_step(wl, fill=SENTINEL, free_order=None, partition_size=0, device="cuda"
         tables = plan.block_tables[torch.from_numpy(idx).to(device)].contiguous()
         lens = plan.context_lens[torch.from_numpy(idx).to(device)].contiguous()
         max_ctx = int(plan.host_lens[idx].max())
-        ws_bytes = P.pa_decode_workspace_bytes(len(idx), sp.num_q_heads, sp.head_dim, max_ctx, partition_size)
-        ws = torch.empty(max(ws_bytes, 4), dtype=torch.uint8, device=device) if ws_bytes else None
-        P.pa_decode(cache.desc, q, out, tables, lens, max_ctx, sp.scale, partition_size, ws)
+        if grouped:
+            ws_bytes = P.pa_decode_grouped_workspace_bytes(len(idx), sp.num_q_heads, sp.head_dim, max_ctx,
+                                                           partition_size)
+            ws = torch.empty(max(ws_bytes, 4), dtype=torch.uint8, device=device)
+            gs = None if group_start is None else torch.as_tensor(np.asarray(group_start, np.int32)).to(device)
+            P.pa_decode_grouped(cache.desc, q, out, tables, lens, max_ctx, sp.scale, gs, partition_size, ws)
+        else:
+            ws_bytes = P.pa_decode_workspace_bytes(len(idx), sp.num_q_heads, sp.head_dim, max_ctx, partition_size)
+            ws = torch.empty(max(ws_bytes, 4), dtype=torch.uint8, device=device) if ws_bytes else None
+            P.pa_decode(cache.desc, q, out, tables, lens, max_ctx, sp.scale, partition_size, ws)
         o = to_host(out)
         for j, i in enumerate(dec):
             out_all[starts[i]] = o[j]

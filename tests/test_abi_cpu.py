@@ -131,6 +131,51 @@ def test_workspace_size_formula():
     assert P.pa_decode_workspace_bytes(4, 32, 128, 1000, -1) >= P.pa_decode_workspace_bytes(4, 32, 128, 1000, 512)
 
 
+def _grouped(cache, num_seqs=4, num_q_heads=32, max_blocks=8, max_ctx=100, scale=0.1, groups=FAKE, num_groups=2,
+             part=0, ws=FAKE, ws_bytes=1 << 30, q=FAKE):
+    return P.lib().pa_decode_grouped(ctypes.byref(cache), q, FAKE, num_seqs, num_q_heads, FAKE, max_blocks, FAKE,
+                                     max_ctx, scale, groups, num_groups, part, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(num_q_heads=24), P.PA_EUNSUPPORTED),
+    (dict(scale=0.0), P.PA_EINVAL),
+    (dict(num_seqs=-1), P.PA_EINVAL),
+    (dict(num_seqs=4097), P.PA_EUNSUPPORTED),   # the planner holds at most 4096 sequences
+    (dict(num_groups=-1), P.PA_EINVAL),
+    (dict(groups=0, num_groups=3), P.PA_EINVAL),  # groups announced, none given
+    (dict(max_ctx=8 * 16 + 1), P.PA_EINVAL),
+    (dict(part=48), P.PA_EINVAL),                 # not a multiple of 32
+    (dict(part=-32), P.PA_EINVAL),
+    (dict(part=64 * 16 + 32), P.PA_EINVAL),       # more than 64 blocks per partition
+    (dict(q=0), P.PA_EINVAL),
+    (dict(ws=0), P.PA_EWORKSPACE),
+    (dict(ws_bytes=64), P.PA_EWORKSPACE),
+])
+def test_grouped_decode_validation(kw, code):
+    assert _grouped(_cache(), **kw) == code
+
+
+def test_grouped_decode_rejects_fp32_and_accepts_empty_batch():
+    assert _grouped(_cache(dtype=P.PA_F32)) == P.PA_EUNSUPPORTED
+    assert _grouped(_cache(), num_seqs=0) == P.PA_OK
+
+
+def test_grouped_workspace_size_formula():
+    # slots per row = 2 * ceil(C / part): states + outputs per (sequence, q
+    # head, slot), then suffix items [S*parts][2], prefix items [S*parts][4],
+    # three per-sequence arrays and two counters, each 16-byte aligned
+    def a16(x):
+        return (x + 15) // 16 * 16
+    S, hq, d, C, part = 256, 32, 128, 8192, 256
+    parts = C // part
+    want = (a16(S * hq * 2 * parts * 2 * 4) + a16(S * hq * 2 * parts * d * 4) + a16(S * parts * 2 * 4)
+            + a16(S * parts * 4 * 4) + 3 * a16(S * 4) + a16(8))
+    assert P.pa_decode_grouped_workspace_bytes(S, hq, d, C, part) == want
+    assert P.pa_decode_grouped_workspace_bytes(S, hq, d, C, 0) == want  # 0 = 256 tokens
+    assert P.pa_decode_grouped_workspace_bytes(0, hq, d, C, 0) == 0
+
+
 # ---- block manager parity with the oracle ---------------------------------------------
 
 def test_page_example_through_the_library():

@@ -359,3 +359,52 @@ def custom(num_q_heads, num_kv_heads, head_dim, block_size, dtype, ctx_lens, n_n
                 num_blocks=sized_pool(plans, block_size, num_blocks), partition_size=partition_size)
     return synthesize(spec, plans, (99, seed, num_q_heads, num_kv_heads, head_dim, block_size,
                                     ["f32", "f16", "bf16"].index(dtype)))
+
+
+def custom_shared(num_q_heads, num_kv_heads, head_dim, block_size, dtype, groups, seed=0, holder_in_batch=False,
+                  name="custom_shared") -> Workload:
+    """Decode sequences in groups that fork one prefix holder each (tests).
+
+    groups: list of (prefix_len, [context lengths of the members]).  A member
+    keeps min(L - 1, prefix_len) tokens of its holder's prefix, as in the
+    shared-prefix configuration; prefix_len 0 makes the members fresh
+    sequences.  holder_in_batch: the holder decodes in the step too, just
+    before its members (context prefix_len + 1)."""
+    plans = []
+    n_batch = sum(len(m) for _, m in groups) + (sum(1 for p, _ in groups if p > 0) if holder_in_batch else 0)
+    sid, hid = 0, n_batch
+    for prefix, members in groups:
+        parent = -1
+        if prefix > 0:
+            if holder_in_batch:
+                plans.append(SeqPlan(sid, -1, 0, prefix, 1, True))
+                parent, sid = sid, sid + 1
+            else:
+                plans.append(SeqPlan(hid, -1, 0, prefix, 0, False))
+                parent, hid = hid, hid + 1
+        for L in members:
+            if parent >= 0:
+                plans.append(SeqPlan(sid, parent, min(int(L) - 1, prefix), int(L) - 1, 1, True))
+            else:
+                plans.append(SeqPlan(sid, -1, 0, int(L) - 1, 1, True))
+            sid += 1
+    spec = Spec(name, num_q_heads, num_kv_heads, head_dim, block_size, dtype,
+                num_blocks=sized_pool(plans, block_size))
+    return synthesize(spec, plans, (98, seed, num_q_heads, num_kv_heads, head_dim, block_size,
+                                    ["f32", "f16", "bf16"].index(dtype), 1 if holder_in_batch else 0))
+
+
+def group_starts(wl: Workload):
+    """Runs of consecutive batch sequences forked from one holder (or the
+    holder followed by its forks), as the [num_groups + 1] start list a
+    grouped decode takes as its hint."""
+    batch = wl.batch
+    root = []
+    for p in batch:
+        root.append(p.parent if p.parent >= 0 else p.seq_id)
+    starts = [0]
+    for i in range(1, len(batch)):
+        if root[i] != root[i - 1]:
+            starts.append(i)
+    starts.append(len(batch))
+    return np.array(starts, dtype=np.int32)
