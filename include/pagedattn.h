@@ -158,7 +158,10 @@ size_t pa_decode_grouped_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, 
  *   workspace       device scratch of at least
  *                   pa_decode_grouped_workspace_bytes(); rewritten by each
  *                   call, so calls sharing it must be ordered on one stream
- * num_seqs is limited to 4096 (PA_EUNSUPPORTED above).  Runs four kernels
+ * PA_EUNSUPPORTED above 4096 sequences, or when (num_q_heads /
+ * num_kv_heads) * 2 * ceil(max_context_len / partition) exceeds 16384 (the
+ * merge's per-head slot weights live in 64 KiB of LDS; with 256-token
+ * partitions that is 262144 tokens of context at 8 q heads per KV head).  Runs four kernels
  * on `stream`: a one-workgroup planner, the shared-prefix kernel (matrix
  * cores, one chunk's rows per workgroup), the suffix partitions of the split
  * decode kernel, and the log-sum-exp merge. */

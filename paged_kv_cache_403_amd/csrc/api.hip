@@ -64,6 +64,7 @@ size_t workspace_for(int64_t num_seqs, int64_t num_q_heads, int64_t head_dim, in
 // Prefix-grouped decode: partitions of `part` tokens, 2 * ceil(C / part)
 // slots per row (prefix slots of the chunk, then the sequence's own).
 constexpr int32_t kGroupedDefaultPartition = 256;
+constexpr int64_t kGroupedMergeLds = 64 * 1024;
 
 struct GroupedLayout {
   int64_t parts, slots;
@@ -292,6 +293,8 @@ int pa_decode_grouped(const pa_cache* cache, const void* q, void* out, int32_t n
   if (num_seqs == 0) return PA_OK;
   if (!q || !out || !block_tables || !context_lens || (num_groups > 0 && !group_start)) return PA_EINVAL;
   const GroupedLayout L = grouped_layout(num_seqs, num_q_heads, cache->head_dim, max_context_len, part);
+  // the merge keeps the slot weights of one KV head's q heads in LDS
+  if (static_cast<int64_t>(group) * L.slots * sizeof(float) > kGroupedMergeLds) return PA_EUNSUPPORTED;
   if (!workspace || workspace_bytes < L.total) return PA_EWORKSPACE;
   char* ws = static_cast<char*>(workspace);
 

@@ -33,425 +33,12 @@
 #include <atomic>
 
 #include "common.h"
+#include "decode_item.h"
 #include "launch.h"
 
 namespace pa {
 
 namespace {
-
-constexpr int kWaves = 4;
-constexpr int kThreads = 64 * kWaves;
-constexpr float kLog2e = 1.4426950408889634f;
-#ifndef PA_DECODE_NBUF16
-#define PA_DECODE_NBUF16 2
-#endif
-#ifndef PA_DECODE_NBUF32
-#define PA_DECODE_NBUF32 1
-#endif
-
-template <typename ST, int D, int BS, int G>
-struct DecodeShape {
-  static constexpr int VEC = 16 / ST::bytes;  // elements per 16-byte chunk
-  static constexpr int LPR = D / VEC;         // lanes covering one K row
-  static constexpr int RPI = 64 / LPR;        // K rows per load instruction
-  static constexpr int NI = BS / RPI;         // load instructions per tile (K and V alike)
-  static constexpr int NV = G * NI;           // partial dot products per lane per tile
-  static constexpr int NRED = NV > LPR ? NV / LPR : 1;  // scores per lane after the transpose
-  static constexpr int HALV = ilog2(NV / NRED);         // halving steps of the transpose
-  static constexpr int LOG_G = ilog2(G);
-  static constexpr int CPD = BS / VEC;  // V chunks per head_dim row
-  // register buffers of the tile pipeline (each NI 16-byte chunks of K and V)
-  static constexpr int NBUF = NI <= 4 ? PA_DECODE_NBUF16 : PA_DECODE_NBUF32;
-  static_assert(LPR >= 8 && LPR <= 32 && (LPR & (LPR - 1)) == 0, "row lanes");
-  static_assert(NI >= 1 && RPI * NI == BS, "tile rows");
-  static_assert(NRED <= NI, "a lane's scores share one head");
-  static_assert(HALV >= LOG_G, "head bits");
-  static_assert(CPD >= 2 && CPD <= 8, "token groups");
-};
-
-// ---- transposing butterfly over the lanes of one K row -----------------------
-// Step T exchanges with lane ^ (LPR >> (T+1)).  While a lane holds more than
-// one value it keeps half (the lower half if its mask bit is clear) and adds
-// the partner's copy of that half; after that it adds the partner's value.
-template <int NV, int LPR, int T>
-struct RowReduce {
-  static constexpr int M = LPR >> (T + 1);
-  static constexpr int N = (NV >> T) > 0 ? (NV >> T) : 1;
-  static __device__ __forceinline__ void run(float* v, int seg) {
-    if constexpr (M >= 1) {
-      if constexpr (N > 1) {
-        const bool upper = (seg & M) != 0;
-#pragma unroll
-        for (int j = 0; j < N / 2; ++j) {
-          const float keep = upper ? v[N / 2 + j] : v[j];
-          const float send = upper ? v[j] : v[N / 2 + j];
-          v[j] = keep + xor_lane<M>(send);
-        }
-      } else {
-        v[0] += xor_lane<M>(v[0]);
-      }
-      RowReduce<NV, LPR, T + 1>::run(v, seg);
-    }
-  }
-};
-
-// Inverse of halving steps T..0: each lane's N values become 2^(T+1) N values
-// in index order, gathered from its partners.
-template <int NV, int LPR, int T>
-struct RowBroadcast {
-  static constexpr int M = LPR >> (T + 1);
-  static constexpr int N = NV >> (T + 1);
-  static __device__ __forceinline__ void run(float* v, int seg) {
-    const bool upper = (seg & M) != 0;
-#pragma unroll
-    for (int j = 0; j < N; ++j) {
-      const float other = xor_lane<M>(v[j]);
-      const float mine = v[j];
-      v[j] = upper ? other : mine;
-      v[N + j] = upper ? mine : other;
-    }
-    if constexpr (T > 0) RowBroadcast<NV, LPR, T - 1>::run(v, seg);
-  }
-};
-
-// max over the lanes that hold other tokens of the same head: the halving
-// steps LOG_G..HALV-1 (token bits inside a row) ...
-template <int LPR, int T, int END>
-__device__ __forceinline__ float max_steps(float x) {
-  if constexpr (T < END) {
-    x = fmaxf(x, xor_lane<(LPR >> (T + 1))>(x));
-    return max_steps<LPR, T + 1, END>(x);
-  }
-  return x;
-}
-template <int LPR, int T, int END>
-__device__ __forceinline__ float sum_steps(float x) {
-  if constexpr (T < END) {
-    x += xor_lane<(LPR >> (T + 1))>(x);
-    return sum_steps<LPR, T + 1, END>(x);
-  }
-  return x;
-}
-// ... and the rows of the wavefront (masks LPR .. 32)
-template <int M>
-__device__ __forceinline__ float rows_max(float x) {
-  if constexpr (M <= 32) {
-    x = fmaxf(x, xor_lane<(M <= 32 ? M : 32)>(x));
-    return rows_max<M * 2>(x);
-  }
-  return x;
-}
-template <int M>
-__device__ __forceinline__ float rows_sum(float x) {
-  if constexpr (M <= 32) {
-    x += xor_lane<(M <= 32 ? M : 32)>(x);
-    return rows_sum<M * 2>(x);
-  }
-  return x;
-}
-// sum over the lanes of one V row's token groups (masks 1 .. CPD/2)
-template <int M, int CPD>
-__device__ __forceinline__ float groups_sum(float x) {
-  if constexpr (M < CPD) {
-    x += xor_lane<M>(x);
-    return groups_sum<M * 2, CPD>(x);
-  }
-  return x;
-}
-
-__device__ __forceinline__ void wave_lds_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
-// Arguments shared by the decode kernels.
-struct DecodeParams {
-  const void* q;
-  const void* kc;
-  const void* vc;
-  const int32_t* tables;
-  const int32_t* ctx_lens;
-  const int32_t* items;    // persistent kernel: (sequence, partition) pairs
-  const int32_t* n_items;  // persistent kernel: number of pairs
-  const int32_t* seq_start;  // grouped decode: first token of each sequence's own part (else null)
-  const int32_t* slot_base;  // grouped decode: workspace slot of each sequence's first own partition
-  void* out;
-  float* ws_ml;
-  float* ws_o;
-  float scale_log2;
-  int32_t max_blocks, max_context, num_blocks, num_kv_heads, part_tokens, max_parts;
-};
-
-template <int G, int D, int BS>
-struct DecodeLds {
-  float red_acc[kWaves][G][D];
-  float red_m[kWaves][G];
-  float red_l[kWaves][G];
-  __attribute__((aligned(16))) float p_lds[kWaves][G][BS];
-};
-
-__device__ __forceinline__ int clamp_len(int L, int max_context) {
-  return L < 0 ? 0 : (L > max_context ? max_context : L);
-}
-
-// One work item: the G q heads of KV head `kvh` of sequence `s` over the
-// tokens of partition `part` (the whole context when it is the only one).
-// L is the sequence's clamped context length.  With one partition the
-// normalised rows are written to `out`, otherwise (m, l, o) partials go to
-// the workspace.  Grouped decode (start > 0 or `partial`): the partitions
-// cover tokens start..L-1 and always leave partials, at slot
-// slot0 + part, for the merge with the shared prefix's partials.
-template <typename ST, int D, int BS, int G>
-__device__ __forceinline__ void decode_item(DecodeLds<G, D, BS>& sh, const DecodeParams& P, int s, int kvh,
-                                            int part, int L, int start = 0, int slot0 = 0, bool partial = false) {
-  using S = DecodeShape<ST, D, BS, G>;
-  constexpr int VEC = S::VEC, LPR = S::LPR, RPI = S::RPI, NI = S::NI, NV = S::NV, NRED = S::NRED,
-                CPD = S::CPD;
-  using elem = typename ST::elem;
-  const elem* __restrict__ q = static_cast<const elem*>(P.q);
-  const elem* __restrict__ kc = static_cast<const elem*>(P.kc);
-  const elem* __restrict__ vc = static_cast<const elem*>(P.vc);
-  elem* __restrict__ out = static_cast<elem*>(P.out);
-  const int num_kv_heads = P.num_kv_heads;
-  const int num_q_heads = num_kv_heads * G;
-  const int part_tokens = P.part_tokens;
-  const float scale_log2 = P.scale_log2;
-
-  const int tid = threadIdx.x;
-  const int lane = lane_id();
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int seg = lane % LPR;  // 16-byte chunk of a K row
-  const int row = lane / LPR;  // K row within a load instruction
-  const int tg = lane % CPD;   // V token group: tokens tg*VEC .. tg*VEC+VEC-1
-
-  const int nparts = L > start ? (L - start + part_tokens - 1) / part_tokens : 0;
-  if (L == 0 && !partial) {
-    if (part == 0) {
-      for (int e = tid; e < G * D; e += kThreads)
-        out[(static_cast<int64_t>(s) * num_q_heads + kvh * G) * D + e] = narrow<ST>(0.f);
-    }
-    return;
-  }
-  if (part >= nparts) return;
-
-  const int tok_begin = start + part * part_tokens;  // a multiple of BS
-  const int tok_end = min(L, tok_begin + part_tokens);
-  const int blk_begin = tok_begin / BS;
-  const int nb = (tok_end + BS - 1) / BS - blk_begin;  // blocks in this partition
-
-  // where this lane's reduced scores sit: head h_own, tokens i*RPI + row
-  int off = 0;
-#pragma unroll
-  for (int t = 0; t < S::HALV; ++t) off += (seg & (LPR >> (t + 1))) ? (NV >> (t + 1)) : 0;
-  const int h_own = off / NI;
-  const int i_own = off % NI;
-  bool owner = true;  // one lane per distinct reduced value counts it in l
-#pragma unroll
-  for (int t = S::HALV; t < ilog2(LPR); ++t) owner = owner && !(seg & (LPR >> (t + 1)));
-
-  u32x4 qv[G];
-  const elem* qrow = q + (static_cast<int64_t>(s) * num_q_heads + kvh * G) * D + seg * VEC;
-#pragma unroll
-  for (int h = 0; h < G; ++h) qv[h] = load16(qrow + h * D);
-
-  float m[G], acc[G][NI];
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    m[h] = -INFINITY;
-#pragma unroll
-    for (int i = 0; i < NI; ++i) acc[h][i] = 0.f;
-  }
-  float l_own = 0.f;
-
-  const int32_t* trow = P.tables + static_cast<int64_t>(s) * P.max_blocks + blk_begin;
-  const int64_t head_off = static_cast<int64_t>(kvh) * BS * D;
-  const int64_t blk_stride = static_cast<int64_t>(num_kv_heads) * BS * D;
-  const int lane_off = lane * VEC;
-  const int num_blocks = P.num_blocks;
-
-  const int my_blocks = nb > wave ? (nb - wave + kWaves - 1) / kWaves : 0;
-
-  // address of a tile from its physical block id (never dereferenced out of range)
-  auto load_tile = [&](int b, u32x4* kr, u32x4* vr) {
-    b = (b >= 0 && b < num_blocks) ? b : 0;
-    const int64_t base = static_cast<int64_t>(b) * blk_stride + head_off + lane_off;
-#pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      kr[i] = load16_nt(kc + base + i * 64 * VEC);
-      vr[i] = load16_nt(vc + base + i * 64 * VEC);
-    }
-  };
-
-  float* pw = &sh.p_lds[wave][0][0];
-
-  auto process = [&](int j, const u32x4* kr, const u32x4* vr) {
-    const int blk = blk_begin + wave + j * kWaves;
-    const bool partial = blk * BS + BS > tok_end;
-    // QK partial dot products, index h*NI + i
-    float v[NV];
-#pragma unroll
-    for (int h = 0; h < G; ++h)
-#pragma unroll
-      for (int i = 0; i < NI; ++i) v[h * NI + i] = dot16<ST>(qv[h], kr[i], 0.f);
-    RowReduce<NV, LPR, 0>::run(v, seg);
-    float bm = -INFINITY;
-#pragma unroll
-    for (int j2 = 0; j2 < NRED; ++j2) {
-      float x = v[j2] * scale_log2;
-      if (partial) x = (blk * BS + (i_own + j2) * RPI + row < tok_end) ? x : -INFINITY;
-      v[j2] = x;
-      bm = fmaxf(bm, x);
-    }
-    // block max of each head, known to every lane
-    bm = max_steps<LPR, S::LOG_G, S::HALV>(bm);
-    bm = rows_max<LPR>(bm);
-    float bmh[G];
-    bmh[0] = bm;
-    if constexpr (S::LOG_G > 0) RowBroadcast<G, LPR, S::LOG_G - 1>::run(bmh, seg);
-    float alpha[G];
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const float mn = fmaxf(m[h], bmh[h]);
-      alpha[h] = __builtin_amdgcn_exp2f(m[h] - mn);
-      m[h] = mn;
-    }
-    // probabilities of this lane's scores, shared through LDS
-    float ps = 0.f;
-#pragma unroll
-    for (int j2 = 0; j2 < NRED; ++j2) {
-      const float p = __builtin_amdgcn_exp2f(v[j2] - m[h_own]);
-      ps += p;
-      pw[h_own * BS + (i_own + j2) * RPI + row] = p;
-    }
-    l_own = l_own * alpha[h_own] + (owner ? ps : 0.f);
-    wave_lds_sync();
-
-    float vt[NI][VEC];
-#pragma unroll
-    for (int i = 0; i < NI; ++i) widen16<ST>(vr[i], vt[i]);
-    if (partial) {
-#pragma unroll
-      for (int c = 0; c < VEC; ++c) {
-        const bool ok = blk * BS + tg * VEC + c < tok_end;
-#pragma unroll
-        for (int i = 0; i < NI; ++i) vt[i][c] = ok ? vt[i][c] : 0.f;
-      }
-    }
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      float p[VEC];
-#pragma unroll
-      for (int c = 0; c < VEC; c += 4) {
-        const float4 x = *reinterpret_cast<const float4*>(pw + h * BS + tg * VEC + c);
-        p[c] = x.x;
-        p[c + 1] = x.y;
-        p[c + 2] = x.z;
-        p[c + 3] = x.w;
-      }
-#pragma unroll
-      for (int i = 0; i < NI; ++i) {
-        float a = acc[h][i] * alpha[h];
-#pragma unroll
-        for (int c = 0; c < VEC; ++c) a = __builtin_fmaf(p[c], vt[i][c], a);
-        acc[h][i] = a;
-      }
-    }
-    wave_lds_sync();  // the next tile's probabilities overwrite pw
-  };
-
-  // The wave's tiles in chunks of 64: one vector load brings the chunk's
-  // block-table entries into a VGPR (read back with v_readlane), then a
-  // software pipeline over NBUF register buffers keeps the loads of tile
-  // j + NBUF - 1 in flight while tile j is processed.  In the steady state
-  // every prefetched tile exists, so no load is conditional and each wait
-  // covers only the tile about to be used; the last tiles of a chunk run in
-  // an unrolled tail.
-  for (int c0 = 0; c0 < my_blocks; c0 += 64) {
-    const int cn = min(64, my_blocks - c0);
-    const int tv = lane < cn ? trow[wave + (c0 + lane) * kWaves] : 0;
-    auto block_id = [&](int j) -> int { return __builtin_amdgcn_readlane(tv, j); };
-    constexpr int NB = S::NBUF;
-    u32x4 kb[NB][NI], vb[NB][NI];
-#pragma unroll
-    for (int b = 0; b < NB - 1; ++b)
-      if (b < cn) load_tile(block_id(b), kb[b], vb[b]);
-    int j0 = 0;
-    for (; j0 + 2 * NB - 2 < cn; j0 += NB) {
-#pragma unroll
-      for (int b = 0; b < NB; ++b) {
-        load_tile(block_id(j0 + b + NB - 1), kb[(b + NB - 1) % NB], vb[(b + NB - 1) % NB]);
-        process(c0 + j0 + b, kb[b], vb[b]);
-      }
-    }
-#pragma unroll
-    for (int b = 0; b < 2 * NB - 1; ++b) {
-      const int j = j0 + b;
-      if (j < cn) {
-        if (j + NB - 1 < cn) load_tile(block_id(j + NB - 1), kb[(b + NB - 1) % NB], vb[(b + NB - 1) % NB]);
-        process(c0 + j, kb[b % NB], vb[b % NB]);
-      }
-    }
-  }
-
-  // l of every head: sum over the lanes holding that head's tokens, then
-  // gather the G heads
-  float lh[G];
-  {
-    float x = sum_steps<LPR, S::LOG_G, ilog2(LPR)>(l_own);
-    x = rows_sum<LPR>(x);
-    lh[0] = x;
-    if constexpr (S::LOG_G > 0) RowBroadcast<G, LPR, S::LOG_G - 1>::run(lh, seg);
-  }
-  // PV partial sums: combine the token groups of each V row
-#pragma unroll
-  for (int h = 0; h < G; ++h)
-#pragma unroll
-    for (int i = 0; i < NI; ++i) acc[h][i] = groups_sum<1, CPD>(acc[h][i]);
-  if (tg == 0) {
-#pragma unroll
-    for (int h = 0; h < G; ++h)
-#pragma unroll
-      for (int i = 0; i < NI; ++i) sh.red_acc[wave][h][(i * 64 + lane) / CPD] = acc[h][i];
-  }
-  if (lane == 0) {
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      sh.red_m[wave][h] = m[h];
-      sh.red_l[wave][h] = lh[h];
-    }
-  }
-  __syncthreads();
-
-  // combine the four wavefronts
-  for (int e = tid; e < G * D; e += kThreads) {
-    const int h = e / D, d = e % D;
-    float M = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w)
-      if (sh.red_l[w][h] > 0.f) M = fmaxf(M, sh.red_m[w][h]);
-    float num = 0.f, den = 0.f;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      if (sh.red_l[w][h] > 0.f) {
-        const float sc = __builtin_amdgcn_exp2f(sh.red_m[w][h] - M);
-        num = __builtin_fmaf(sh.red_acc[w][h][d], sc, num);
-        den = __builtin_fmaf(sh.red_l[w][h], sc, den);
-      }
-    }
-    const int64_t qh = static_cast<int64_t>(s) * num_q_heads + kvh * G + h;
-    if (nparts == 1 && !partial) {
-      out[qh * D + d] = narrow<ST>(num / den);
-    } else {
-      const int64_t pidx = qh * P.max_parts + slot0 + part;
-      P.ws_o[pidx * D + d] = num / den;
-      if (d == 0) {
-        P.ws_ml[2 * pidx] = M;
-        P.ws_ml[2 * pidx + 1] = den;
-      }
-    }
-  }
-}
 
 // Grid (partition, KV head, sequence): used when every sequence has a single
 // partition, so no workgroup is launched without work.
@@ -480,10 +67,7 @@ __global__ __launch_bounds__(kThreads) void decode_persistent_kernel(DecodeParam
     const int part = __builtin_amdgcn_readfirstlane(P.items[2 * item + 1]);
     const int L = clamp_len(P.ctx_lens[s], P.max_context);
     __syncthreads();  // the previous item's LDS merge is complete
-    const bool grouped = P.seq_start != nullptr;
-    const int start = grouped ? __builtin_amdgcn_readfirstlane(P.seq_start[s]) : 0;
-    const int slot0 = grouped ? __builtin_amdgcn_readfirstlane(P.slot_base[s]) : 0;
-    decode_item<ST, D, BS, G>(sh, P, s, kvh, part, L, start, slot0, grouped);
+    decode_item<ST, D, BS, G>(sh, P, s, kvh, part, L);
   }
 }
 
@@ -534,53 +118,38 @@ __global__ __launch_bounds__(kPlanThreads) void decode_plan_kernel(const int32_t
   if (tid == 0) *n_items = carry;
 }
 
-// Log-sum-exp merge of the partitions of one (sequence, q head).  nslots:
-// grouped decode's per-sequence slot count (null: the partitions of the
-// context, and single-partition rows were written directly).  Slots with no
-// keys (l = 0) carry no weight; a row with none is written as zeros.
+// Log-sum-exp merge of the partitions of one (sequence, q head).
 template <typename ST, int D>
 __global__ __launch_bounds__(D) void decode_reduce_kernel(const float* __restrict__ ws_ml,
                                                           const float* __restrict__ ws_o,
                                                           const int32_t* __restrict__ ctx_lens, int max_context,
                                                           int part_tokens, int max_parts, int num_q_heads,
-                                                          const int32_t* __restrict__ nslots,
                                                           typename ST::elem* __restrict__ out) {
   extern __shared__ float w_sh[];  // [max_parts]
   __shared__ float M_sh;
   const int h = blockIdx.x, s = blockIdx.y, d = threadIdx.x;
-  int np;
-  if (nslots) {
-    np = min(max(nslots[s], 0), max_parts);
-  } else {
-    const int L = clamp_len(ctx_lens[s], max_context);
-    np = (L + part_tokens - 1) / part_tokens;
-    if (np <= 1) return;  // written directly by the decode kernel
-  }
+  const int L = clamp_len(ctx_lens[s], max_context);
+  const int np = (L + part_tokens - 1) / part_tokens;
+  if (np <= 1) return;  // written directly by the decode kernel
   const int64_t qh = static_cast<int64_t>(s) * num_q_heads + h;
   const float* ml = ws_ml + 2 * qh * max_parts;
   if (d == 0) {
     float M = -INFINITY;
-    for (int p = 0; p < np; ++p)
-      if (ml[2 * p + 1] > 0.f) M = fmaxf(M, ml[2 * p]);
+    for (int p = 0; p < np; ++p) M = fmaxf(M, ml[2 * p]);
     M_sh = M;
   }
   __syncthreads();
   const float M = M_sh;
-  for (int p = d; p < np; p += D) {
-    const float l = ml[2 * p + 1];
-    w_sh[p] = l > 0.f ? l * __builtin_amdgcn_exp2f(ml[2 * p] - M) : 0.f;
-  }
+  for (int p = d; p < np; p += D) w_sh[p] = ml[2 * p + 1] * __builtin_amdgcn_exp2f(ml[2 * p] - M);
   __syncthreads();
   const float* o = ws_o + qh * max_parts * D + d;
   float num = 0.f, den = 0.f;
   for (int p = 0; p < np; ++p) {
     const float w = w_sh[p];
-    if (w > 0.f) {
-      num = __builtin_fmaf(w, o[static_cast<int64_t>(p) * D], num);
-      den += w;
-    }
+    num = __builtin_fmaf(w, o[static_cast<int64_t>(p) * D], num);
+    den += w;
   }
-  out[qh * D + d] = narrow<ST>(den > 0.f ? num / den : 0.f);
+  out[qh * D + d] = narrow<ST>(num / den);
 }
 
 // Workgroups of the persistent kernel: as many as fit on the device at once
@@ -626,20 +195,14 @@ hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t st) {
   P.num_kv_heads = a.num_kv_heads;
   P.part_tokens = a.part_tokens;
   P.max_parts = a.num_parts;
-  P.seq_start = a.seq_start;
-  P.slot_base = a.slot_base;
-  const bool grouped = a.seq_start != nullptr;
-  if (a.num_parts <= 1 && !grouped) {
+  if (a.num_parts <= 1) {
     hipLaunchKernelGGL((decode_kernel<ST, D, BS, G>), dim3(1, a.num_kv_heads, a.num_seqs), dim3(kThreads), 0, st, P);
     return hipGetLastError();
   }
-  hipError_t e = hipSuccess;
-  if (!grouped) {
-    hipLaunchKernelGGL(decode_plan_kernel, dim3(1), dim3(kPlanThreads), 0, st, a.context_lens, a.num_seqs,
-                       a.max_context_len, a.part_tokens, a.ws_items, a.ws_count);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
+  hipLaunchKernelGGL(decode_plan_kernel, dim3(1), dim3(kPlanThreads), 0, st, a.context_lens, a.num_seqs,
+                     a.max_context_len, a.part_tokens, a.ws_items, a.ws_count);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
   const int64_t upper = static_cast<int64_t>(a.num_seqs) * a.num_parts * a.num_kv_heads;
   const int grid = static_cast<int>(std::min<int64_t>(upper, persistent_grid<ST, D, BS, G>()));
   hipLaunchKernelGGL((decode_persistent_kernel<ST, D, BS, G>), dim3(grid), dim3(kThreads), 0, st, P);
@@ -648,7 +211,7 @@ hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t st) {
   const int num_q_heads = a.num_kv_heads * G;
   hipLaunchKernelGGL((decode_reduce_kernel<ST, D>), dim3(num_q_heads, a.num_seqs), dim3(D),
                      a.num_parts * sizeof(float), st, a.ws_ml, a.ws_o, a.context_lens,
-                     a.max_context_len, a.part_tokens, a.num_parts, num_q_heads, a.nslots,
+                     a.max_context_len, a.part_tokens, a.num_parts, num_q_heads,
                      static_cast<typename ST::elem*>(a.out));
   return hipGetLastError();
 }

@@ -18,20 +18,31 @@
 //    each member has in common with the chunk's longest sequence (its
 //    reference).  The caller's grouping is only a hint: a sequence that
 //    shares nothing gets a shared length of 0 and is decoded alone;
-//  * the shared-prefix kernel takes one (chunk, KV head, partition) per
-//    workgroup and runs all of the chunk's rows over the reference's
-//    blocks on the matrix cores: S^T = K Q^T and O^T = V^T P^T with
-//    v_mfma_f32_32x32x16, each row masked at its own shared length;
-//  * the suffix of every sequence (its tokens from the shared length on) is
-//    decoded by the split decode kernel, and one merge combines prefix and
-//    suffix partials per (sequence, q head).
+//  * one persistent kernel then walks two work lists.  A shared-prefix item
+//    is a (chunk, KV head, partition): all of the chunk's rows run over the
+//    reference's blocks on the matrix cores, S^T = K Q^T and O^T = V^T P^T
+//    with v_mfma_f32_32x32x16, each row masked at its own shared length.  A
+//    suffix item is a (sequence, KV head, partition) of the sequence's own
+//    tokens, decoded like split decode.  Prefix items come first (they are
+//    the longest), so suffix items fill in behind them;
+//  * private tails of at most 64 keys are not items of their own: the last
+//    prefix partition of the chunk takes them as extra masked tiles (most
+//    forks diverge only a few tokens before the step);
+//  * every item leaves (max, sum, output) partials in workspace slots (a
+//    sequence whose only slot is one suffix partition writes its output
+//    directly); a merge kernel combines each sequence's slots by
+//    log-sum-exp.  Merging inside the persistent kernel instead, by the
+//    last item of each sequence, needs device-scope release fences (an L2
+//    write-back per item on this chip) and measured many times slower.
 //
 // The result equals plain decode over each sequence's own table: a member
 // reads only blocks whose table entries equal its own.
 #include <algorithm>
 #include <atomic>
+#include <climits>
 
 #include "common.h"
+#include "decode_item.h"
 #include "launch.h"
 #include "mfma.h"
 
@@ -41,12 +52,8 @@ namespace {
 
 constexpr int kPlanThreads = 1024;
 constexpr int kPlanWaves = kPlanThreads / 64;
-constexpr int kWaves = 4;
-constexpr int kThreads = 64 * kWaves;
 constexpr int kTile = 32;  // keys per matrix tile
-constexpr float kLog2e = 1.4426950408889634f;
-
-__device__ __forceinline__ int clamp_len(int L, int max_context) { return L < 0 ? 0 : (L > max_context ? max_context : L); }
+constexpr int kFoldTail = 64;  // private tails up to this many keys ride along with the shared prefix
 
 // Inclusive scan of x over the workgroup (kPlanThreads threads) under the
 // associative `op`; `total` receives the reduction over all threads.
@@ -135,26 +142,33 @@ __global__ __launch_bounds__(kPlanThreads) void grouped_plan_kernel(PlanParams P
   for (int s = tid; s < S; s += kPlanThreads) ref_of[s] = share[ref_of[s]];
   __syncthreads();
 
-  // 4. leading full blocks each member has in common with its reference
-  for (int s = tid; s < S; s += kPlanThreads) {
-    const int ref = ref_of[s];
+  // 4. leading full blocks each member has in common with its reference.
+  //    `lpm` adjacent lanes share a sequence (as many as the batch leaves
+  //    room for) and compare 8 entries each per step, interleaved.
+  int lpm = 1;
+  while (lpm < 64 && S * lpm * 2 <= kPlanThreads) lpm *= 2;
+  for (int base = 0; base < S * lpm; base += kPlanThreads) {
+    const int v = base + tid, s = v / lpm, sub = v % lpm;
+    const int ref = s < S ? ref_of[s] : 0;
+    const int lim = (s < S && ref != s) ? min(len[s], len[ref]) / BS : 0;
+    const int32_t* a = P.tables + static_cast<int64_t>(s < S ? s : 0) * P.max_blocks;
+    const int32_t* b = P.tables + static_cast<int64_t>(ref) * P.max_blocks;
     int common = 0;
-    if (ref != s) {
-      const int lim = min(len[s], len[ref]) / BS;
-      const int32_t* a = P.tables + static_cast<int64_t>(s) * P.max_blocks;
-      const int32_t* b = P.tables + static_cast<int64_t>(ref) * P.max_blocks;
-      while (common < lim) {
-        int diff = 8;
+    while (common < lim) {  // the same trip count for the lpm lanes of a sequence
+      int first = INT_MAX;
 #pragma unroll
-        for (int e = 7; e >= 0; --e) {
-          const int j = common + e;
-          if (j >= lim || a[j] != b[j]) diff = e;
-        }
-        common += diff;
-        if (diff < 8) break;
+      for (int e = 0; e < 8; ++e) {
+        const int j = common + sub + lpm * e;
+        if (j < lim && a[j] != b[j]) first = min(first, j);
       }
+      for (int o = 1; o < lpm; o <<= 1) first = min(first, __shfl_xor(first, o, 64));
+      if (first != INT_MAX) {
+        common = first;
+        break;
+      }
+      common += 8 * lpm;
     }
-    share[s] = common * BS;
+    if (s < S && sub == 0) share[s] = min(common, lim) * BS;
   }
   __syncthreads();
   for (int s = tid; s < S; s += kPlanThreads) {
@@ -178,7 +192,8 @@ __global__ __launch_bounds__(kPlanThreads) void grouped_plan_kernel(PlanParams P
       sh = share[s];
       sb = (share[ref] + PT - 1) / PT;
       if (s == 0 || ref_of[s - 1] != ref) own_pre = sb;  // first of its chunk
-      np = len[s] > sh ? (len[s] - sh + PT - 1) / PT : 0;
+      const int tail = len[s] - sh;
+      np = tail <= 0 || (sb > 0 && tail <= kFoldTail) ? 0 : (tail + PT - 1) / PT;
     }
     const long long packed = static_cast<long long>(own_pre) | (static_cast<long long>(np) << 32);
     long long total = 0;
@@ -214,19 +229,13 @@ __global__ __launch_bounds__(kPlanThreads) void grouped_plan_kernel(PlanParams P
   }
 }
 
-struct PrefixParams {
-  const void* q;
-  const void* kc;
-  const void* vc;
-  const int32_t* tables;
-  const int32_t* shares;  // per sequence; a reference holds its chunk's maximum
-  // items: (first member, members, partition, reference)
-  const int32_t* items;
-  const int32_t* n_items;
-  float* ws_ml;
-  float* ws_o;
-  float scale_log2;
-  int32_t max_blocks, num_blocks, num_kv_heads, part_tokens, max_parts;
+struct GroupedParams {
+  DecodeParams dec;          // the suffix work list in items / n_items
+  const int32_t* seq_start;  // shared tokens per sequence; a reference holds its chunk's maximum
+  const int32_t* slot_base;
+  const int32_t* nslots;
+  const int32_t* pre_items;  // (first member, members, partition, reference)
+  const int32_t* pre_count;
 };
 
 template <int D>
@@ -238,204 +247,318 @@ struct PrefixLds {
   float inv[32];
 };
 
-// One (chunk, KV head, partition) per iteration, keys read through the
-// reference's table.  Rows r = member * G + h; wave w takes key tiles
-// w, w + 4, ... of the partition.
+template <int G, int D, int BS>
+union GroupedLds {
+  DecodeLds<G, D, BS> dec;
+  PrefixLds<D> pre;
+};
+
+// A shared-prefix item: the rows r = member * G + h of one chunk over one
+// partition of the shared prefix, keys read through the reference's table;
+// wave w takes key tiles w, w + 4, ...  Writes slot `part` of every member.
 template <typename ST, int D, int BS, int G>
-__global__ __launch_bounds__(kThreads, 2) void grouped_prefix_kernel(PrefixParams P) {
+__device__ __forceinline__ void prefix_item(PrefixLds<D>& sh, const GroupedParams& GP, int item, int kvh, int& first,
+                                            int& members) {
   static_assert(D % 32 == 0 && D >= 64, "head_dim");
   static_assert(BS == 16 || BS == 32, "block size");
-  constexpr int KS = D / 16;  // contraction steps of S^T = K Q^T
-  constexpr int DT = D / 32;  // 32-wide column tiles of O^T
+  constexpr int KS = D / 16;      // contraction steps of S^T = K Q^T
+  constexpr int DT = D / 32;      // 32-wide column tiles of O^T
   constexpr int TB = kTile / BS;  // blocks per key tile
   using elem = typename ST::elem;
-  __shared__ PrefixLds<D> sh;
-
+  const DecodeParams& P = GP.dec;
   const elem* __restrict__ q = static_cast<const elem*>(P.q);
   const elem* __restrict__ kc = static_cast<const elem*>(P.kc);
   const elem* __restrict__ vc = static_cast<const elem*>(P.vc);
   const int hk = P.num_kv_heads, hq = hk * G;
   const int lane = lane_id();
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int r = lane & 31;  // row of this lane (B operand column / accumulator column)
+  const int r = lane & 31;   // row of this lane (B operand column / accumulator column)
   const int hf = lane >> 5;  // half: k-elements 8*hf.. of each step
   const int64_t blk_stride = static_cast<int64_t>(hk) * BS * D;
-  const int n_work = *P.n_items * hk;
 
-  for (int it = blockIdx.x; it < n_work; it += gridDim.x) {
-    const int item = it / hk, kvh = it - item * hk;
-    const int first = __builtin_amdgcn_readfirstlane(P.items[4 * item]);
-    const int members = __builtin_amdgcn_readfirstlane(P.items[4 * item + 1]);
-    const int part = __builtin_amdgcn_readfirstlane(P.items[4 * item + 2]);
-    const int ref = __builtin_amdgcn_readfirstlane(P.items[4 * item + 3]);
-    const int share_max = __builtin_amdgcn_readfirstlane(P.shares[ref]);
-    const int tok0 = part * P.part_tokens;
-    const int tok1 = min(share_max, tok0 + P.part_tokens);
-    const int ntiles = (tok1 - tok0 + kTile - 1) / kTile;
-    const int mem = r / G, hh = r - mem * G;
-    const bool row_ok = mem < members;
-    const int row_lim = row_ok ? P.shares[first + mem] : 0;
+  first = __builtin_amdgcn_readfirstlane(GP.pre_items[4 * item]);
+  members = __builtin_amdgcn_readfirstlane(GP.pre_items[4 * item + 1]);
+  const int part = __builtin_amdgcn_readfirstlane(GP.pre_items[4 * item + 2]);
+  const int ref = __builtin_amdgcn_readfirstlane(GP.pre_items[4 * item + 3]);
+  const int share_max = __builtin_amdgcn_readfirstlane(GP.seq_start[ref]);
+  const int tok0 = part * P.part_tokens;
+  const int tok1 = min(share_max, tok0 + P.part_tokens);
+  const int ntiles = (tok1 - tok0 + kTile - 1) / kTile;
+  const int mem = r / G, hh = r - mem * G;
+  const bool row_ok = mem < members;
+  const int row_lim = row_ok ? GP.seq_start[first + mem] : 0;
 
-    // Q^T as the B operand: row r, dims 8 * (2k + hf) ..
-    u32x4 qb[KS];
-    const elem* qrow = q + (static_cast<int64_t>(first + (row_ok ? mem : 0)) * hq + kvh * G + hh) * D + 8 * hf;
+  // Q^T as the B operand: row r, dims 8 * (2k + hf) ..
+  u32x4 qb[KS];
+  const elem* qrow = q + (static_cast<int64_t>(first + (row_ok ? mem : 0)) * hq + kvh * G + hh) * D + 8 * hf;
 #pragma unroll
-    for (int k = 0; k < KS; ++k) qb[k] = row_ok ? load16(qrow + 16 * k) : u32x4{0, 0, 0, 0};
+  for (int k = 0; k < KS; ++k) qb[k] = row_ok ? load16(qrow + 16 * k) : u32x4{0, 0, 0, 0};
 
-    // the partition's block ids, one per lane (64 * BS >= part_tokens)
-    const int32_t* trow = P.tables + static_cast<int64_t>(ref) * P.max_blocks + tok0 / BS;
-    const int nblk = (tok1 - tok0 + BS - 1) / BS;
-    int bid = lane < nblk ? trow[lane] : 0;
-    bid = (bid >= 0 && bid < P.num_blocks) ? bid : 0;
+  // the partition's block ids, one per lane (64 * BS >= part_tokens)
+  const int32_t* trow = P.tables + static_cast<int64_t>(ref) * P.max_blocks + tok0 / BS;
+  const int nblk = (tok1 - tok0 + BS - 1) / BS;
+  int bid = lane < nblk ? trow[lane] : 0;
+  bid = (bid >= 0 && bid < P.num_blocks) ? bid : 0;
 
-    f32x16 o[DT];
+  f32x16 o[DT];
 #pragma unroll
-    for (int t = 0; t < DT; ++t) o[t] = f32x16{};
-    float m_run = -INFINITY, l_run = 0.f;
+  for (int t = 0; t < DT; ++t) o[t] = f32x16{};
+  float m_run = -INFINITY, l_run = 0.f;
 
-    // K rows in A-operand order (key_perm) and V^T rows for the PV steps
-    const int kkey = key_perm(r);
-    auto load_tile = [&](int t, u32x4* kr, u32x4* vr) __attribute__((always_inline)) {
-      const int kb = __shfl(bid, t * TB + kkey / BS, 64);
-      const elem* kp = kc + static_cast<int64_t>(kb) * blk_stride + (static_cast<int64_t>(kvh) * BS + kkey % BS) * D +
-                       8 * hf;
+  // K rows in A-operand order (key_perm) and V^T rows for the PV steps
+  const int kkey = key_perm(r);
+  auto load_tile = [&](int t, u32x4* kr, u32x4* vr) __attribute__((always_inline)) {
+    const int kb = __shfl(bid, t * TB + kkey / BS, 64);
+    const elem* kp =
+        kc + static_cast<int64_t>(kb) * blk_stride + (static_cast<int64_t>(kvh) * BS + kkey % BS) * D + 8 * hf;
 #pragma unroll
-      for (int k = 0; k < KS; ++k) kr[k] = load16_nt(kp + 16 * k);
+    for (int k = 0; k < KS; ++k) kr[k] = load16_nt(kp + 16 * k);
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int key = 16 * k + 8 * hf;  // first of this lane's 8 keys in the step
+      const int vb = __shfl(bid, t * TB + key / BS, 64);
+      const elem* vp = vc + static_cast<int64_t>(vb) * blk_stride + (static_cast<int64_t>(kvh) * D + r) * BS + key % BS;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) vr[dt * 2 + k] = load16_nt(vp + dt * 32 * BS);
+    }
+  };
+
+  // One key tile: scores, online softmax, PV.  P enters the PV products as
+  // two 16-bit parts (nearest value and remainder), so the weights keep
+  // about 16 bits: rows with only a few shared keys can have outputs as
+  // large as single V entries, where one 16-bit rounding of P would show.
+  auto compute = [&](int key0, int lim, const u32x4* kr, const u32x4* vr) __attribute__((always_inline)) {
+    f32x16 s = f32x16{};
+#pragma unroll
+    for (int k = 0; k < KS; ++k) s = mfma32<ST>(kr[k], qb[k], s);
+
+    float x[16];
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int key = key0 + key_perm(8 * (e >> 2) + 4 * hf + (e & 3));
+      x[e] = key < lim ? s[e] * P.scale_log2 : -INFINITY;
+      tmax = fmaxf(tmax, x[e]);
+    }
+    tmax = halves_max(tmax);
+    const float m_new = fmaxf(m_run, tmax);
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+    float psum = 0.f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      x[e] = __builtin_amdgcn_exp2f(x[e] - m_use);
+      psum += x[e];
+    }
+    l_run = l_run * alpha + psum;
+    m_run = m_new;
+    u32x4 hi[2], lo[2];
+#pragma unroll
+    for (int k = 0; k < 2; ++k)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const float a0 = x[8 * k + 2 * c], a1 = x[8 * k + 2 * c + 1];
+        const uint32_t h = pack2<ST>(a0, a1);
+        float h0, h1;
+        widen2<ST>(h, h0, h1);
+        hi[k][c] = h;
+        lo[k][c] = pack2<ST>(a0 - h0, a1 - h1);
+      }
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      o[dt] *= alpha;
 #pragma unroll
       for (int k = 0; k < 2; ++k) {
-        const int key = 16 * k + 8 * hf;  // first of this lane's 8 keys in the step
-        const int vb = __shfl(bid, t * TB + key / BS, 64);
-        const elem* vp = vc + static_cast<int64_t>(vb) * blk_stride + (static_cast<int64_t>(kvh) * D + r) * BS + key % BS;
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) vr[dt * 2 + k] = load16_nt(vp + dt * 32 * BS);
+        o[dt] = mfma32<ST>(vr[dt * 2 + k], hi[k], o[dt]);
+        o[dt] = mfma32<ST>(vr[dt * 2 + k], lo[k], o[dt]);
       }
-    };
+    }
+  };
 
-    // One key tile: scores, online softmax, PV.  P enters the PV products as
-    // two 16-bit parts (nearest value and remainder), so the weights keep
-    // about 16 bits: rows with only a few shared keys can have outputs as
-    // large as single V entries, where one 16-bit rounding of P would show.
-    auto compute = [&](int t, const u32x4* kr, const u32x4* vr) __attribute__((always_inline)) {
-      f32x16 s = f32x16{};
-#pragma unroll
-      for (int k = 0; k < KS; ++k) s = mfma32<ST>(kr[k], qb[k], s);
+  // two register buffers alternate, the next tile's loads in flight while
+  // the current one is computed (at the end the last tile is requested
+  // again: a cache hit)
+  const int my_tiles = ntiles > wave ? (ntiles - wave + kWaves - 1) / kWaves : 0;
+  const int last = wave + (my_tiles - 1) * kWaves;
+  u32x4 k0[KS], v0[2 * DT], k1[KS], v1[2 * DT];
+  if (my_tiles > 0) load_tile(wave, k0, v0);
+  for (int i = 0; i < my_tiles; i += 2) {
+    const int t = wave + i * kWaves;
+    load_tile(min(t + kWaves, last), k1, v1);
+    compute(tok0 + t * kTile, row_lim, k0, v0);
+    if (i + 1 < my_tiles) {
+      load_tile(min(t + 2 * kWaves, last), k0, v0);
+      compute(tok0 + (t + kWaves) * kTile, row_lim, k1, v1);
+    }
+  }
 
-      const int key0 = tok0 + t * kTile;
-      float x[16];
-      float tmax = -INFINITY;
+  // The last partition also takes the members' short private tails (keys
+  // share..L-1 read through the member's own table, at most kFoldTail of
+  // them): one tile per 32 keys, scored for all rows but kept only for the
+  // member's own.  Tiles go round robin over the waves.
+  if (part == (share_max + P.part_tokens - 1) / P.part_tokens - 1) {
+    int g = 0;  // running tile index over the members
+    for (int m = 0; m < members; ++m) {
+      const int sm = first + m;
+      const int t0 = __builtin_amdgcn_readfirstlane(GP.seq_start[sm]);
+      const int Lm = clamp_len(__builtin_amdgcn_readfirstlane(P.ctx_lens[sm]), P.max_context);
+      const int tail = Lm - t0;
+      if (tail <= 0 || tail > kFoldTail) continue;
+      const int32_t* mrow = P.tables + static_cast<int64_t>(sm) * P.max_blocks;
+      for (int key0 = t0; key0 < Lm; key0 += kTile, ++g) {
+        if (g % kWaves != wave) continue;
+        // keys past the tail read the tail's last block again (masked)
+        const int kb0 = mrow[min(key0 + kkey, Lm - 1) / BS];
+        const int kb = (kb0 >= 0 && kb0 < P.num_blocks) ? kb0 : 0;
+        const elem* kp =
+            kc + static_cast<int64_t>(kb) * blk_stride + (static_cast<int64_t>(kvh) * BS + (key0 + kkey) % BS) * D + 8 * hf;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int key = key0 + key_perm(8 * (e >> 2) + 4 * hf + (e & 3));
-        x[e] = key < row_lim ? s[e] * P.scale_log2 : -INFINITY;
-        tmax = fmaxf(tmax, x[e]);
-      }
-      tmax = halves_max(tmax);
-      const float m_new = fmaxf(m_run, tmax);
-      const float m_use = m_new == -INFINITY ? 0.f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-      float psum = 0.f;
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        x[e] = __builtin_amdgcn_exp2f(x[e] - m_use);
-        psum += x[e];
-      }
-      l_run = l_run * alpha + psum;
-      m_run = m_new;
-      u32x4 hi[2], lo[2];
-#pragma unroll
-      for (int k = 0; k < 2; ++k)
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const float a0 = x[8 * k + 2 * c], a1 = x[8 * k + 2 * c + 1];
-          const uint32_t h = pack2<ST>(a0, a1);
-          float h0, h1;
-          widen2<ST>(h, h0, h1);
-          hi[k][c] = h;
-          lo[k][c] = pack2<ST>(a0 - h0, a1 - h1);
-        }
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        o[dt] *= alpha;
+        for (int k = 0; k < KS; ++k) k0[k] = load16_nt(kp + 16 * k);
 #pragma unroll
         for (int k = 0; k < 2; ++k) {
-          o[dt] = mfma32<ST>(vr[dt * 2 + k], hi[k], o[dt]);
-          o[dt] = mfma32<ST>(vr[dt * 2 + k], lo[k], o[dt]);
+          const int key = key0 + 16 * k + 8 * hf;
+          const int vb0 = mrow[min(key, Lm - 1) / BS];
+          const int vb = (vb0 >= 0 && vb0 < P.num_blocks) ? vb0 : 0;
+          const elem* vp = vc + static_cast<int64_t>(vb) * blk_stride + (static_cast<int64_t>(kvh) * D + r) * BS + key % BS;
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt) v0[dt * 2 + k] = load16_nt(vp + dt * 32 * BS);
         }
+        compute(key0, mem == m ? Lm : 0, k0, v0);
       }
-    };
+    }
+  }
 
-    // wave w takes tiles w, w + 4, ...; two register buffers alternate, the
-    // next tile's loads in flight while the current one is computed (at the
-    // end the last tile is requested again: a cache hit)
-    const int my_tiles = ntiles > wave ? (ntiles - wave + kWaves - 1) / kWaves : 0;
-    const int last = wave + (my_tiles - 1) * kWaves;
-    u32x4 k0[KS], v0[2 * DT], k1[KS], v1[2 * DT];
-    if (my_tiles > 0) load_tile(wave, k0, v0);
-    for (int i = 0; i < my_tiles; i += 2) {
-      const int t = wave + i * kWaves;
-      load_tile(min(t + kWaves, last), k1, v1);
-      compute(t, k0, v0);
-      if (i + 1 < my_tiles) {
-        load_tile(min(t + 2 * kWaves, last), k0, v0);
-        compute(t + kWaves, k1, v1);
-      }
+  // merge the four wavefronts' states of each row into the members' slots
+  const float l_tot = halves_sum(l_run);
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      float4 v4 = {o[dt][4 * j], o[dt][4 * j + 1], o[dt][4 * j + 2], o[dt][4 * j + 3]};
+      *reinterpret_cast<float4*>(&sh.o[wave][r][dt * 32 + 8 * j + 4 * hf]) = v4;
     }
-
-    // merge the four wavefronts' states of each row
-    const float l_tot = halves_sum(l_run);
+  if (hf == 0) {
+    sh.m[wave][r] = m_run;
+    sh.l[wave][r] = l_tot;
+  }
+  __syncthreads();
+  const int tid = threadIdx.x;
+  if (tid < 32) {
+    float M = -INFINITY;
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
+    for (int w = 0; w < kWaves; ++w)
+      if (sh.l[w][tid] > 0.f) M = fmaxf(M, sh.m[w][tid]);
+    float L = 0.f;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        float4 v4 = {o[dt][4 * j], o[dt][4 * j + 1], o[dt][4 * j + 2], o[dt][4 * j + 3]};
-        *reinterpret_cast<float4*>(&sh.o[wave][r][dt * 32 + 8 * j + 4 * hf]) = v4;
-      }
-    if (hf == 0) {
-      sh.m[wave][r] = m_run;
-      sh.l[wave][r] = l_tot;
+    for (int w = 0; w < kWaves; ++w) {
+      const float c = sh.l[w][tid] > 0.f ? __builtin_amdgcn_exp2f(sh.m[w][tid] - M) : 0.f;
+      sh.c[w][tid] = c;
+      L += c * sh.l[w][tid];
     }
-    __syncthreads();
-    const int tid = threadIdx.x;
-    if (tid < 32) {
-      float M = -INFINITY;
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w)
-        if (sh.l[w][tid] > 0.f) M = fmaxf(M, sh.m[w][tid]);
-      float L = 0.f;
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
-        const float c = sh.l[w][tid] > 0.f ? __builtin_amdgcn_exp2f(sh.m[w][tid] - M) : 0.f;
-        sh.c[w][tid] = c;
-        L += c * sh.l[w][tid];
-      }
-      sh.inv[tid] = L > 0.f ? 1.f / L : 0.f;
-      const int mm = tid / G;
-      if (mm < members) {
-        const int64_t pidx = (static_cast<int64_t>(first + mm) * hq + kvh * G + tid % G) * P.max_parts + part;
-        P.ws_ml[2 * pidx] = M;
-        P.ws_ml[2 * pidx + 1] = L;
-      }
+    sh.inv[tid] = L > 0.f ? 1.f / L : 0.f;
+    const int mm = tid / G;
+    if (mm < members) {
+      const int64_t pidx = (static_cast<int64_t>(first + mm) * hq + kvh * G + tid % G) * P.max_parts + part;
+      P.ws_ml[2 * pidx] = M;
+      P.ws_ml[2 * pidx + 1] = L;
     }
-    __syncthreads();
-    for (int e = tid; e < 32 * D; e += kThreads) {
-      const int row = e / D, d = e - row * D;
-      const int mm = row / G;
-      if (mm >= members) continue;
-      float acc = 0.f;
+  }
+  __syncthreads();
+  for (int e = tid; e < 32 * D; e += kThreads) {
+    const int row = e / D, d = e - row * D;
+    const int mm = row / G;
+    if (mm >= members) continue;
+    float acc = 0.f;
 #pragma unroll
-      for (int w = 0; w < kWaves; ++w) acc = __builtin_fmaf(sh.c[w][row], sh.o[w][row][d], acc);
-      const int64_t pidx = (static_cast<int64_t>(first + mm) * hq + kvh * G + row % G) * P.max_parts + part;
-      P.ws_o[pidx * D + d] = acc * sh.inv[row];
-    }
-    __syncthreads();  // LDS is reused by the next item
+    for (int w = 0; w < kWaves; ++w) acc = __builtin_fmaf(sh.c[w][row], sh.o[w][row][d], acc);
+    const int64_t pidx = (static_cast<int64_t>(first + mm) * hq + kvh * G + row % G) * P.max_parts + part;
+    P.ws_o[pidx * D + d] = acc * sh.inv[row];
   }
 }
 
-// Workgroups of the prefix kernel that fit on the device at once.
+// The persistent kernel: prefix items, then suffix items, each times the KV
+// heads.  A suffix item that is its sequence's only slot writes the output
+// directly; every other item leaves partials for the merge kernel.
 template <typename ST, int D, int BS, int G>
-int prefix_grid() {
+__global__ __launch_bounds__(kThreads, 2) void grouped_decode_kernel(GroupedParams GP) {
+  __shared__ GroupedLds<G, D, BS> sh;
+  const DecodeParams& P = GP.dec;
+  const int hk = P.num_kv_heads;
+  const int n_pre = __builtin_amdgcn_readfirstlane(*GP.pre_count) * hk;
+  const int n_all = n_pre + __builtin_amdgcn_readfirstlane(*P.n_items) * hk;
+  for (int it = blockIdx.x; it < n_all; it += gridDim.x) {
+    __syncthreads();  // the previous item is done with LDS
+    if (it < n_pre) {
+      const int item = it / hk;
+      int first, members;
+      prefix_item<ST, D, BS, G>(sh.pre, GP, item, it - item * hk, first, members);
+    } else {
+      const int j = it - n_pre, item = j / hk;
+      const int s = __builtin_amdgcn_readfirstlane(P.items[2 * item]);
+      const int part = __builtin_amdgcn_readfirstlane(P.items[2 * item + 1]);
+      const int L = clamp_len(P.ctx_lens[s], P.max_context);
+      const bool only = __builtin_amdgcn_readfirstlane(GP.nslots[s]) == 1 &&
+                        __builtin_amdgcn_readfirstlane(GP.slot_base[s]) == 0;
+      decode_item<ST, D, BS, G>(sh.dec, P, s, j - item * hk, part, L, __builtin_amdgcn_readfirstlane(GP.seq_start[s]),
+                                __builtin_amdgcn_readfirstlane(GP.slot_base[s]), !only);
+    }
+  }
+}
+
+// Log-sum-exp merge of each (sequence, KV head)'s slots: grid (KV head,
+// sequence), G rows of D outputs.  The slot weights of the G rows go to LDS
+// first (G * max_parts floats of dynamic LDS), so the output loop's loads are
+// independent.  Slots without keys (sum 0) carry no weight; a row with none
+// (context 0) is written as zeros.  Rows written directly by the decode
+// kernel are skipped.
+template <typename ST, int D, int G>
+__global__ __launch_bounds__(kThreads) void grouped_merge_kernel(DecodeParams P, const int32_t* __restrict__ nslots,
+                                                                const int32_t* __restrict__ slot_base) {
+  extern __shared__ float w_sh[];  // [G][max_parts]
+  __shared__ float M_sh[G];
+  const int kvh = blockIdx.x, s = blockIdx.y, tid = threadIdx.x;
+  const int ns = min(nslots[s], P.max_parts);
+  if (ns == 1 && slot_base[s] == 0) return;
+  const int hq = P.num_kv_heads * G, mp = P.max_parts;
+  const int64_t qh0 = static_cast<int64_t>(s) * hq + kvh * G;
+  const float* ml = P.ws_ml + 2 * qh0 * mp;  // the G rows' slots are contiguous
+  for (int i = tid; i < G * ns; i += kThreads) {
+    const int h = i / ns, p = i - h * ns;
+    const float l = ml[2 * (h * mp + p) + 1];
+    w_sh[h * mp + p] = l > 0.f ? ml[2 * (h * mp + p)] : -INFINITY;
+  }
+  __syncthreads();
+  if (tid < G) {
+    float M = -INFINITY;
+    for (int p = 0; p < ns; ++p) M = fmaxf(M, w_sh[tid * mp + p]);
+    M_sh[tid] = M;
+  }
+  __syncthreads();
+  for (int i = tid; i < G * ns; i += kThreads) {
+    const int h = i / ns, p = i - h * ns;
+    const float m = w_sh[h * mp + p];
+    w_sh[h * mp + p] = m == -INFINITY ? 0.f : ml[2 * (h * mp + p) + 1] * __builtin_amdgcn_exp2f(m - M_sh[h]);
+  }
+  __syncthreads();
+  typename ST::elem* out = static_cast<typename ST::elem*>(P.out);
+  for (int e = tid; e < G * D; e += kThreads) {
+    const int h = e / D, d = e - h * D;
+    const float* o = P.ws_o + (qh0 + h) * mp * D + d;
+    const float* w = w_sh + h * mp;
+    float num = 0.f, den = 0.f;
+    for (int p = 0; p < ns; ++p) {
+      num = __builtin_fmaf(w[p], o[static_cast<int64_t>(p) * D], num);
+      den += w[p];
+    }
+    out[(qh0 + h) * D + d] = narrow<ST>(den > 0.f ? num / den : 0.f);
+  }
+}
+
+// Workgroups of the persistent kernel that fit on the device at once.
+template <typename ST, int D, int BS, int G>
+int grouped_grid() {
   constexpr int kMaxDev = 64;
-  static std::atomic<int> cached[kMaxDev];
+  static std::atomic<int> cached[kMaxDev];  // 0 = not yet queried; racing writers store the same value
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) dev = 0;
   int n = cached[dev].load(std::memory_order_relaxed);
@@ -443,7 +566,7 @@ int prefix_grid() {
     int cus = 0, per_cu = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &per_cu, reinterpret_cast<const void*>(&grouped_prefix_kernel<ST, D, BS, G>), kThreads, 0) !=
+            &per_cu, reinterpret_cast<const void*>(&grouped_decode_kernel<ST, D, BS, G>), kThreads, 0) !=
             hipSuccess ||
         per_cu <= 0)
       per_cu = 1;
@@ -478,34 +601,40 @@ hipError_t launch_t(const GroupedArgs& g, hipStream_t st) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
 
-  PrefixParams P{};
-  P.q = a.q;
-  P.kc = a.k_cache;
-  P.vc = a.v_cache;
-  P.tables = a.block_tables;
-  P.shares = g.seq_start;
-  P.items = g.pre_items;
-  P.n_items = g.pre_count;
-  P.ws_ml = a.ws_ml;
-  P.ws_o = a.ws_o;
-  P.scale_log2 = a.scale * kLog2e;
-  P.max_blocks = a.max_blocks_per_seq;
-  P.num_blocks = a.num_blocks;
-  P.num_kv_heads = a.num_kv_heads;
-  P.part_tokens = a.part_tokens;
-  P.max_parts = a.num_parts;
-  const int64_t parts = (static_cast<int64_t>(a.max_context_len) + a.part_tokens - 1) / a.part_tokens;
-  const int64_t upper = std::max<int64_t>(1, (a.num_seqs / 2) * parts * a.num_kv_heads);
-  const int grid = static_cast<int>(std::min<int64_t>(upper, prefix_grid<ST, D, BS, G>()));
-  hipLaunchKernelGGL((grouped_prefix_kernel<ST, D, BS, G>), dim3(grid), dim3(kThreads), 0, st, P);
+  GroupedParams P{};
+  P.dec.q = a.q;
+  P.dec.kc = a.k_cache;
+  P.dec.vc = a.v_cache;
+  P.dec.tables = a.block_tables;
+  P.dec.ctx_lens = a.context_lens;
+  P.dec.items = a.ws_items;
+  P.dec.n_items = a.ws_count;
+  P.dec.out = a.out;
+  P.dec.ws_ml = a.ws_ml;
+  P.dec.ws_o = a.ws_o;
+  P.dec.scale_log2 = a.scale * kLog2e;
+  P.dec.max_blocks = a.max_blocks_per_seq;
+  P.dec.max_context = a.max_context_len;
+  P.dec.num_blocks = a.num_blocks;
+  P.dec.num_kv_heads = a.num_kv_heads;
+  P.dec.part_tokens = a.part_tokens;
+  P.dec.max_parts = a.num_parts;
+  P.seq_start = g.seq_start;
+  P.slot_base = g.slot_base;
+  P.nslots = g.nslots;
+  P.pre_items = g.pre_items;
+  P.pre_count = g.pre_count;
+  // both item lists are bounded by sequences x partitions of the longest context
+  const int64_t parts =
+      std::max<int64_t>(1, (static_cast<int64_t>(a.max_context_len) + a.part_tokens - 1) / a.part_tokens);
+  const int64_t upper = (a.num_seqs / 2 + a.num_seqs) * parts * a.num_kv_heads;
+  const int grid = static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(upper, grouped_grid<ST, D, BS, G>())));
+  hipLaunchKernelGGL((grouped_decode_kernel<ST, D, BS, G>), dim3(grid), dim3(kThreads), 0, st, P);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-
-  DecodeArgs d = a;
-  d.seq_start = g.seq_start;
-  d.slot_base = g.slot_base;
-  d.nslots = g.nslots;
-  return launch_decode(d, st);
+  hipLaunchKernelGGL((grouped_merge_kernel<ST, D, G>), dim3(a.num_kv_heads, a.num_seqs), dim3(kThreads),
+                     static_cast<size_t>(G) * a.num_parts * sizeof(float), st, P.dec, g.nslots, g.slot_base);
+  return hipGetLastError();
 }
 
 template <typename ST, int D, int BS>

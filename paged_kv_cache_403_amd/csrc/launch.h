@@ -24,18 +24,12 @@ struct DecodeArgs {
   int32_t max_context_len;  // host bound; device lengths are clamped to it
   int32_t part_tokens;  // tokens per partition (multiple of block_size)
   int32_t num_parts;    // ceil(max_context_len / part_tokens); grouped: workspace slots per row
-  // Grouped decode (all null otherwise): each sequence's own tokens start at
-  // seq_start[s]; its partials go to slots slot_base[s].. and the merge reads
-  // nslots[s] slots.  ws_items / ws_count then come from the grouped planner.
-  const int32_t* seq_start;
-  const int32_t* slot_base;
-  const int32_t* nslots;
 };
 
-// Prefix-grouped decode: the planner and shared-prefix kernel (grouped.hip)
-// followed by the suffix partitions and merge of launch_decode.
+// Prefix-grouped decode (grouped.hip): a planner, one persistent kernel for
+// the shared-prefix and suffix items, and a merge kernel.
 struct GroupedArgs {
-  DecodeArgs d;                // num_parts = slots per row, ws_* as below
+  DecodeArgs d;                // num_parts = slots per row; ws_items / ws_count = suffix list
   const int32_t* group_start;  // [num_groups + 1] hint: runs of sequences that may share a prefix
   int32_t num_groups;
   int32_t* seq_start;   // [S]  shared tokens of each sequence (its own part starts there)

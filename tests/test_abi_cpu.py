@@ -151,6 +151,7 @@ def _grouped(cache, num_seqs=4, num_q_heads=32, max_blocks=8, max_ctx=100, scale
     (dict(q=0), P.PA_EINVAL),
     (dict(ws=0), P.PA_EWORKSPACE),
     (dict(ws_bytes=64), P.PA_EWORKSPACE),
+    (dict(num_q_heads=64, max_blocks=20000, max_ctx=300000), P.PA_EUNSUPPORTED),  # merge weights over 64 KiB
 ])
 def test_grouped_decode_validation(kw, code):
     assert _grouped(_cache(), **kw) == code
@@ -164,7 +165,7 @@ def test_grouped_decode_rejects_fp32_and_accepts_empty_batch():
 def test_grouped_workspace_size_formula():
     # slots per row = 2 * ceil(C / part): states + outputs per (sequence, q
     # head, slot), then suffix items [S*parts][2], prefix items [S*parts][4],
-    # three per-sequence arrays and two counters, each 16-byte aligned
+    # three per-sequence arrays and two list lengths, each 16-byte aligned
     def a16(x):
         return (x + 15) // 16 * 16
     S, hq, d, C, part = 256, 32, 128, 8192, 256
