@@ -11,8 +11,11 @@ chunks).  Inputs are resident in HBM before the timed region.
 Headline workload: 7B-shaped MHA decode (64 sequences, contexts U{128..2048},
 32 q = 32 KV heads, head_dim 128, fp16, block_size 16).  `value` is the
 step's algorithmic bytes (K/V read, q/out, tables, append) over the step time.
-A secondary measurement times chunked prefill on the mixed workload (8 chunks
-of 512 tokens on cached contexts U{0..4096}, 32/8 heads, bf16) in TFLOP/s.
+Secondary measurements: chunked prefill on the mixed workload (8 chunks of
+512 tokens on cached contexts U{0..4096}, 32/8 heads, bf16) in TFLOP/s, and
+plain vs prefix-grouped decode on the shared-prefix workload (256 sequences
+in groups of 8 forked from 512-token prompts, 32/8 heads, bf16), where the
+grouped path reads each shared block once.
 
 Prints one JSON line on stdout; progress goes to stderr.
 """
@@ -213,24 +216,103 @@ def cpu_baseline(wl, budget_s=15.0, min_s=10.0):
                       f"{t_used:.1f}s of oracle time), decode bytes of those sequences over that time"}
 
 
-def counter_traffic(kernel_source):
+DECODE_KERNEL_SOURCES = ("paged_kv_cache_403_amd/csrc/decode.hip", "paged_kv_cache_403_amd/csrc/decode_item.h",
+                         "paged_kv_cache_403_amd/csrc/common.h")
+
+
+def sources_sha256(paths):
+    """One SHA-256 over the files a kernel is compiled from, in order."""
+    import hashlib
+
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def counter_traffic(kernel_sources):
     """HBM bytes per launch of the dominant kernel from the committed
     rocprofv3 counter summary (FETCH_SIZE and WRITE_SIZE, each scaled by
     what the counter reads for a plain device copy of known size), or None
-    when the kernel source has changed since the counters were taken."""
-    import hashlib
-
+    when the kernel's sources have changed since the counters were taken."""
     path = os.path.join(ROOT, "profiles", "decode_kernel_mha_decode_7b_hbm_counters.json")
     try:
         with open(path) as f:
             rec = json.load(f)
-        with open(os.path.join(ROOT, kernel_source), "rb") as f:
-            sha = hashlib.sha256(f.read()).hexdigest()
+        sha = sources_sha256(kernel_sources)
     except OSError:
         return None
-    if rec.get("kernel_source_sha256") != sha:
+    if rec.get("kernel_sources_sha256") != sha:
         return None
     return int(rec["hbm_bytes_per_launch"])
+
+
+def decode_group_starts(wl, dec):
+    """Runs of consecutive decode sequences forked from one prompt (or a
+    prompt followed by its forks): the grouping hint of grouped decode."""
+    import numpy as np
+
+    batch = wl.batch
+    root = [batch[i].parent if batch[i].parent >= 0 else batch[i].seq_id for i in dec]
+    starts = [0] + [i for i in range(1, len(root)) if root[i] != root[i - 1]] + [len(root)]
+    return np.array(starts, dtype=np.int32)
+
+
+def measure_grouped(name, iters, warmup):
+    """Plain split decode against prefix-grouped decode on one workload's
+    decode batch: HIP-event times on the library's stream, and the K/V bytes
+    each must read (logical: every sequence's context; unique: each
+    physical block once)."""
+    import torch
+
+    import workloads
+
+    wl = workloads.make(name)
+    st = Step(wl, -1)
+    sp = wl.spec
+    P = st.P
+    st.copy_append()
+    hint = torch.from_numpy(decode_group_starts(wl, st.dec)).to("cuda")
+    n = len(st.dec)
+    part = 512
+    wsb = P.pa_decode_grouped_workspace_bytes(n, sp.num_q_heads, sp.head_dim, st.max_dec, part)
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(st.q_dec)
+
+    def grouped():
+        P.pa_decode_grouped(st.cache.desc, st.q_dec, out, st.tab_dec, st.len_dec, st.max_dec, sp.scale, hint, part,
+                            ws)
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(iters):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / iters * 1e3
+
+    plain_us = timed(st.decode)
+    grouped_us = timed(grouped)
+    torch.cuda.synchronize()
+    diff = float((out.float() - st.out_dec.float()).abs().max())
+    tabs, lens = st.plan.host_tables[st.dec], st.plan.host_lens[st.dec]
+    blocks = set()
+    for row, L in zip(tabs, lens):
+        blocks.update(int(b) for b in row[:(int(L) + sp.block_size - 1) // sp.block_size])
+    unique = len(blocks) * sp.num_kv_heads * sp.block_size * sp.head_dim * sp.elem_bytes * 2
+    log(f"{name}: plain decode {plain_us:.1f} us, grouped decode {grouped_us:.1f} us "
+        f"(unique K/V {unique / 1e6:.1f} MB of {st.dec_kv_bytes / 1e6:.1f} MB logical)")
+    return {"workload": name, "plain_decode_us": round(plain_us, 2), "plain_partition_tokens": st.part_used,
+            "grouped_decode_us": round(grouped_us, 2), "grouped_partition_tokens": part,
+            "speedup": round(plain_us / grouped_us, 3), "logical_kv_bytes": st.dec_kv_bytes,
+            "unique_kv_bytes": unique, "grouped_unique_gbs": round(unique / (grouped_us * 1e-6) / 1e9, 1),
+            "plain_logical_gbs": round(st.dec_kv_bytes / (plain_us * 1e-6) / 1e9, 1),
+            "max_abs_diff_vs_plain": diff}
 
 
 def main():
@@ -242,6 +324,7 @@ def main():
     ap.add_argument("--partition", type=int, default=-1, help="decode partition tokens (0 one pass, -1 auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true", help="skip the chunked-prefill measurement")
+    ap.add_argument("--no-grouped", action="store_true", help="skip the plain vs grouped decode measurement")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB a few times (the known-size reference for "
                          "the HBM byte counters) and exit")
@@ -301,7 +384,7 @@ def main():
         "roofline": {"bound": bound, "achieved": round(dom_bytes / (dom_ms * 1e-3) / 1e9, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(dom_bytes / (dom_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                     "traffic": counter_traffic("paged_kv_cache_403_amd/csrc/decode.hip"),
+                     "traffic": counter_traffic(DECODE_KERNEL_SOURCES),
                      "kernel": "decode_kernel", "bytes_per_launch": dom_bytes},
     }
     if not args.no_prefill:
@@ -318,6 +401,8 @@ def main():
             "tflops": round(tf, 2), "peak": MFMA_BF16_PEAK_TFLOPS, "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
             "decode_us": round(dc5 * 1e3, 2), "decode_gbs": round(dec_gbs, 1), "copy_append_us": round(ca5 * 1e3, 2),
         }
+    if not args.no_grouped:
+        result["shared_prefix"] = measure_grouped("gqa_shared_prefix", max(10, args.steps // 2), 3)
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a sample")
         result["cpu_baseline"] = cpu_baseline(wl)

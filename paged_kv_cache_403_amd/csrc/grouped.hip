@@ -397,21 +397,23 @@ __device__ __forceinline__ void prefix_item(PrefixLds<D>& sh, const GroupedParam
   // them): one tile per 32 keys, scored for all rows but kept only for the
   // member's own.  Tiles go round robin over the waves.
   if (part == (share_max + P.part_tokens - 1) / P.part_tokens - 1) {
+    // lane m holds member m's shared length and context length
+    const int tl0 = lane < members ? GP.seq_start[first + lane] : 0;
+    const int tlL = lane < members ? clamp_len(P.ctx_lens[first + lane], P.max_context) : 0;
     int g = 0;  // running tile index over the members
     for (int m = 0; m < members; ++m) {
-      const int sm = first + m;
-      const int t0 = __builtin_amdgcn_readfirstlane(GP.seq_start[sm]);
-      const int Lm = clamp_len(__builtin_amdgcn_readfirstlane(P.ctx_lens[sm]), P.max_context);
+      const int t0 = __builtin_amdgcn_readlane(tl0, m);
+      const int Lm = __builtin_amdgcn_readlane(tlL, m);
       const int tail = Lm - t0;
       if (tail <= 0 || tail > kFoldTail) continue;
-      const int32_t* mrow = P.tables + static_cast<int64_t>(sm) * P.max_blocks;
+      const int32_t* mrow = P.tables + static_cast<int64_t>(first + m) * P.max_blocks;
       for (int key0 = t0; key0 < Lm; key0 += kTile, ++g) {
         if (g % kWaves != wave) continue;
         // keys past the tail read the tail's last block again (masked)
         const int kb0 = mrow[min(key0 + kkey, Lm - 1) / BS];
         const int kb = (kb0 >= 0 && kb0 < P.num_blocks) ? kb0 : 0;
-        const elem* kp =
-            kc + static_cast<int64_t>(kb) * blk_stride + (static_cast<int64_t>(kvh) * BS + (key0 + kkey) % BS) * D + 8 * hf;
+        const elem* kp = kc + static_cast<int64_t>(kb) * blk_stride +
+                         (static_cast<int64_t>(kvh) * BS + (key0 + kkey) % BS) * D + 8 * hf;
 #pragma unroll
         for (int k = 0; k < KS; ++k) k0[k] = load16_nt(kp + 16 * k);
 #pragma unroll
@@ -419,7 +421,8 @@ __device__ __forceinline__ void prefix_item(PrefixLds<D>& sh, const GroupedParam
           const int key = key0 + 16 * k + 8 * hf;
           const int vb0 = mrow[min(key, Lm - 1) / BS];
           const int vb = (vb0 >= 0 && vb0 < P.num_blocks) ? vb0 : 0;
-          const elem* vp = vc + static_cast<int64_t>(vb) * blk_stride + (static_cast<int64_t>(kvh) * D + r) * BS + key % BS;
+          const elem* vp =
+              vc + static_cast<int64_t>(vb) * blk_stride + (static_cast<int64_t>(kvh) * D + r) * BS + key % BS;
 #pragma unroll
           for (int dt = 0; dt < DT; ++dt) v0[dt * 2 + k] = load16_nt(vp + dt * 32 * BS);
         }
