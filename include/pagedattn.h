@@ -33,7 +33,9 @@
  *  - Compiled instances: dtype {f32, f16, bf16} x head_dim {64, 128} x
  *    block_size {16, 32}; num_q_heads a multiple of num_kv_heads with group
  *    size num_q_heads/num_kv_heads in {1, 2, 4, 8}.  pa_prefill_chunk needs
- *    f16 or bf16 (its contractions run on the matrix cores).
+ *    f16 or bf16 (its contractions run on the matrix cores).  An FP8 pool
+ *    (see pa_cache) has head_dim 128 and f16 or bf16 activations, and is
+ *    supported by pa_kv_append, pa_copy_blocks and pa_decode.
  */
 #ifndef PAGEDATTN_H
 #define PAGEDATTN_H
@@ -45,7 +47,7 @@
 extern "C" {
 #endif
 
-typedef enum { PA_F32 = 0, PA_F16 = 1, PA_BF16 = 2 } pa_dtype;
+typedef enum { PA_F32 = 0, PA_F16 = 1, PA_BF16 = 2, PA_FP8_E4M3 = 3 } pa_dtype;
 
 typedef enum {
   PA_OK = 0,
@@ -61,7 +63,18 @@ typedef enum {
  *   k_cache  [num_blocks][num_kv_heads][block_size][head_dim]  (token rows)
  *   v_cache  [num_blocks][num_kv_heads][head_dim][block_size]  (V transposed
  *            inside the tile, so the PV contraction reads keys contiguously)
- * Token slot s lives in block s / block_size at position s % block_size. */
+ * Token slot s lives in block s / block_size at position s % block_size.
+ *
+ * FP8 pool (dtype PA_FP8_E4M3; lshu.cn/news/11644, "性能关键路径与瓶颈":
+ * quantising the KV cache halves what decode reads): elements are one-byte
+ * codes of the OCP E4M3 format without infinities (bias 7, 3 mantissa bits,
+ * largest finite 448, S.1111.111 = NaN).  q, out and the K/V rows given to
+ * pa_kv_append are in `act_dtype` (PA_F16 or PA_BF16); a stored code is the
+ * nearest E4M3 value to x * (1 / scale) -- the reciprocal and the product in
+ * fp32 -- ties to the even code, magnitudes past 448 saturating, and its
+ * value is code * scale, with `k_scale` for K and `v_scale` for V (positive
+ * and finite).  For the other dtypes act_dtype, k_scale and v_scale are
+ * ignored (a zero-initialised descriptor stays valid). */
 typedef struct {
   void* k_cache;
   void* v_cache;
@@ -69,13 +82,18 @@ typedef struct {
   int32_t num_kv_heads;
   int32_t block_size;
   int32_t head_dim;
-  int32_t dtype; /* pa_dtype */
+  int32_t dtype;     /* pa_dtype of the pool's elements */
+  int32_t act_dtype; /* FP8 pool: pa_dtype of q, out and appended rows */
+  float k_scale;     /* FP8 pool: value = code * scale */
+  float v_scale;
 } pa_cache;
 
 /* Write new tokens' K/V into their cache slots (decode appends the current
  * token before attending: zzmblog.top vLLM guide, "Transformer推理与KV缓存";
  * lshu.cn/news/11644, "方案：页式内存管理", the append rule).
- *   k_new, v_new  device [num_tokens][num_kv_heads][head_dim], cache dtype
+ *   k_new, v_new  device [num_tokens][num_kv_heads][head_dim] in the
+ *                 activation type (the pool's dtype; act_dtype for an FP8
+ *                 pool, whose rows are quantised as pa_cache describes)
  *   slot_mapping  device int64 [num_tokens]; slot < 0 skips the token
  * Slots of one call must be distinct. */
 int pa_kv_append(const pa_cache* cache, const void* k_new, const void* v_new,
@@ -99,7 +117,8 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t 
  * "方案：页式内存管理": the kernel reads the scattered blocks of a request
  * through its block table as one logical K/V sequence; "性能关键路径与瓶颈":
  * decode is bound by reading the KV cache).
- *   q, out          device [num_seqs][num_q_heads][head_dim], cache dtype;
+ *   q, out          device [num_seqs][num_q_heads][head_dim] in the
+ *                   activation type (act_dtype for an FP8 pool);
  *                   q head h reads KV head h / (num_q_heads / num_kv_heads)
  *   block_tables    device int32 [num_seqs][max_blocks_per_seq]
  *   context_lens    device int32 [num_seqs]; counts the token appended this
@@ -122,7 +141,9 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t 
  *                   covers every choice): partial states, the work list and
  *                   its length, all rewritten by each call, so calls that
  *                   share a workspace must be ordered on one stream
- * Output is rounded to the cache dtype (round to nearest even). */
+ * Output is rounded to the activation type (round to nearest even).  With
+ * an FP8 pool the codes are widened exactly and the scales applied in fp32
+ * (k_scale folded into the softmax scale, v_scale into the normalisation). */
 int pa_decode(const pa_cache* cache, const void* q, void* out, int32_t num_seqs, int32_t num_q_heads,
               const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
               int32_t max_context_len, float scale, int32_t partition_size, void* workspace,

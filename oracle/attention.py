@@ -16,10 +16,20 @@ Readings where the pages are silent:
   earlier part is already cached; lshu.cn/news/11644, "整体架构" scheduler
   loop; 5x10.cn/post/462, "分块预填充"); decode is n = 1;
 * a sequence with context length 0 yields zeros (no keys to attend).
+
+`kv` = (kv_dtype, k_scale, v_scale) describes an FP8 pool (the values are
+the codes times the scales, storage.kv_values); None: K/V share q's dtype.
 """
 import numpy as np
 
-from .storage import to_f64
+from .storage import kv_values, to_f64
+
+
+def kv_f64(k, v, dtype, kv=None):
+    """Stored K and V -> fp64 values."""
+    if kv is not None and kv[0] == "fp8":
+        return kv_values(k, kv[1]), kv_values(v, kv[2])
+    return to_f64(k, dtype), to_f64(v, dtype)
 
 
 def kv_head_of(h: int, num_q_heads: int, num_kv_heads: int) -> int:
@@ -36,7 +46,7 @@ def visible_keys(context_len: int, positions):
     return np.arange(context_len)[None, :] <= np.asarray(positions)[:, None]
 
 
-def gather(pool_k, pool_v, table, context_len, dtype):
+def gather(pool_k, pool_v, table, context_len, dtype, kv=None):
     """K/V of one sequence in logical order: [L][Hkv][D] each, fp64."""
     bs = pool_k.shape[2]
     nb = pool_k.shape[0]
@@ -44,7 +54,7 @@ def gather(pool_k, pool_v, table, context_len, dtype):
     blk = np.asarray(table)[j // bs]
     assert np.all((blk >= 0) & (blk < nb)), "block id out of range"
     off = j % bs
-    return to_f64(pool_k[blk, :, off, :], dtype), to_f64(pool_v[blk, :, off, :], dtype)
+    return kv_f64(pool_k[blk, :, off, :], pool_v[blk, :, off, :], dtype, kv)
 
 
 def attend(qv, K, V, scale):
@@ -59,21 +69,20 @@ def attend(qv, K, V, scale):
     return p @ V, m + np.log(l), p
 
 
-def attention_rows(q_rows, K, V, positions, scale, dtype):
+def attention_rows(q_rows, K, V, positions, scale, dtype, kv=None):
     """Rows of one (sequence, q head) against that head's K/V in logical
-    order (K, V [L][D] storage values): row i sees keys 0..positions[i].
+    order (K, V [L][D] as stored): row i sees keys 0..positions[i].
     The same definition as `paged_attention`, for a few sampled rows of a
     long sequence.  Returns out [n][D] fp64."""
     q = to_f64(np.asarray(q_rows), dtype)
-    Kf = to_f64(np.asarray(K), dtype)
-    Vf = to_f64(np.asarray(V), dtype)
+    Kf, Vf = kv_f64(np.asarray(K), np.asarray(V), dtype, kv)
     out = np.zeros((len(positions), Kf.shape[1]))
     for i, a in enumerate(positions):
         out[i], _, _ = attend(q[i], Kf[: int(a) + 1], Vf[: int(a) + 1], scale)
     return out
 
 
-def paged_attention(q, pool_k, pool_v, tables, context_lens, q_lens, scale, dtype):
+def paged_attention(q, pool_k, pool_v, tables, context_lens, q_lens, scale, dtype, kv=None):
     """q: [sum n][Hq][D] storage values, rows in sequence order.
 
     Returns out [sum n][Hq][D] and lse [sum n][Hq], both fp64.  For each
@@ -89,7 +98,7 @@ def paged_attention(q, pool_k, pool_v, tables, context_lens, q_lens, scale, dtyp
         L, n = int(context_lens[s]), int(q_lens[s])
         assert n <= L or L == 0
         if L > 0 and n > 0:
-            K, V = gather(pool_k, pool_v, tables[s], L, dtype)
+            K, V = gather(pool_k, pool_v, tables[s], L, dtype, kv)
             visible = visible_keys(L, query_positions(L, n))
             for h in range(Hq):
                 g = kv_head_of(h, Hq, Hkv)

@@ -18,14 +18,21 @@ from dataclasses import dataclass
 import numpy as np
 
 from .block_manager import BlockManager
-from .storage import host_dtype
+from .storage import host_dtype, kv_encode
 
 
 class Pool:
-    def __init__(self, num_blocks, num_kv_heads, block_size, head_dim, dtype, fill_bits=None):
+    """dtype: the pool's element type.  An "fp8" pool stores E4M3 codes of
+    the appended activation values (act_dtype) divided by k_scale / v_scale
+    (storage.kv_encode)."""
+
+    def __init__(self, num_blocks, num_kv_heads, block_size, head_dim, dtype, fill_bits=None, act_dtype=None,
+                 k_scale=1.0, v_scale=1.0):
         hd = host_dtype(dtype)
         shape = (num_blocks, num_kv_heads, block_size, head_dim)
         self.dtype = dtype
+        self.act_dtype = act_dtype or dtype
+        self.k_scale, self.v_scale = k_scale, v_scale
         self.block_size = block_size
         self.k = np.zeros(shape, dtype=hd)
         self.v = np.zeros(shape, dtype=hd)
@@ -37,9 +44,13 @@ class Pool:
         slots = np.asarray(slots, dtype=np.int64)
         keep = slots >= 0
         blk, off = np.divmod(slots[keep], self.block_size)
+        k_new, v_new = np.asarray(k_new)[keep], np.asarray(v_new)[keep]
+        if self.dtype == "fp8":
+            k_new = kv_encode(k_new, self.act_dtype, self.k_scale)
+            v_new = kv_encode(v_new, self.act_dtype, self.v_scale)
         # pool[blk, :, off, :] selects one [heads][head_dim] row per token
-        self.k[blk, :, off, :] = np.asarray(k_new)[keep]
-        self.v[blk, :, off, :] = np.asarray(v_new)[keep]
+        self.k[blk, :, off, :] = k_new
+        self.v[blk, :, off, :] = v_new
 
     def copy(self, pairs):
         for src, dst in pairs:
@@ -72,7 +83,8 @@ def run_workload(wl, fill_bits=None, with_pool=True) -> StepState:
     memory."""
     sp = wl.spec
     bm = BlockManager(sp.num_blocks, sp.block_size, wl.free_order)
-    pool = Pool(sp.num_blocks, sp.num_kv_heads, sp.block_size, sp.head_dim, sp.dtype, fill_bits) if with_pool else None
+    pool = (Pool(sp.num_blocks, sp.num_kv_heads, sp.block_size, sp.head_dim, sp.kv_dtype or sp.dtype, fill_bits,
+                 act_dtype=sp.dtype, k_scale=sp.k_scale, v_scale=sp.v_scale) if with_pool else None)
     setup_slots = []
     for op in wl.setup_ops():
         if op.kind == "add":

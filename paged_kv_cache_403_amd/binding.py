@@ -16,7 +16,7 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libpagedattn.so")
 
-PA_F32, PA_F16, PA_BF16 = 0, 1, 2
+PA_F32, PA_F16, PA_BF16, PA_FP8_E4M3 = 0, 1, 2, 3
 PA_OK, PA_EINVAL, PA_EUNSUPPORTED, PA_EWORKSPACE, PA_ENOMEM, PA_EHIP = range(6)
 
 
@@ -38,6 +38,9 @@ class pa_cache(ctypes.Structure):
         ("block_size", ctypes.c_int32),
         ("head_dim", ctypes.c_int32),
         ("dtype", ctypes.c_int32),
+        ("act_dtype", ctypes.c_int32),
+        ("k_scale", ctypes.c_float),
+        ("v_scale", ctypes.c_float),
     ]
 
 
@@ -146,13 +149,23 @@ def _stream(stream, like) -> int | None:
     return torch.cuda.current_stream(like.device).cuda_stream
 
 
-def make_cache(k_cache, v_cache) -> pa_cache:
-    """Descriptor of a pool: k_cache [NB][Hkv][BS][D], v_cache [NB][Hkv][D][BS]."""
+def make_cache(k_cache, v_cache, act_dtype=None, k_scale=1.0, v_scale=1.0) -> pa_cache:
+    """Descriptor of a pool: k_cache [NB][Hkv][BS][D], v_cache [NB][Hkv][D][BS].
+    uint8 tensors are an FP8 (E4M3) pool: act_dtype (torch.float16 /
+    torch.bfloat16) is then the type of q, out and appended rows, and
+    k_scale / v_scale its per-tensor scales."""
+    torch = _torch()
     nb, hkv, bs, d = k_cache.shape
     if tuple(v_cache.shape) != (nb, hkv, d, bs) or v_cache.dtype != k_cache.dtype:
         raise ValueError("v_cache must be [num_blocks][num_kv_heads][head_dim][block_size] of k_cache's dtype")
-    return pa_cache(_dev_ptr(k_cache, "k_cache"), _dev_ptr(v_cache, "v_cache"), nb, hkv, bs, d,
-                    _dtype_code(k_cache))
+    if k_cache.dtype == torch.uint8:
+        if act_dtype not in (torch.float16, torch.bfloat16):
+            raise ValueError("an FP8 pool needs act_dtype torch.float16 or torch.bfloat16")
+        act = {torch.float16: PA_F16, torch.bfloat16: PA_BF16}[act_dtype]
+        return pa_cache(_dev_ptr(k_cache, "k_cache"), _dev_ptr(v_cache, "v_cache"), nb, hkv, bs, d, PA_FP8_E4M3,
+                        act, float(k_scale), float(v_scale))
+    code = _dtype_code(k_cache)
+    return pa_cache(_dev_ptr(k_cache, "k_cache"), _dev_ptr(v_cache, "v_cache"), nb, hkv, bs, d, code, code, 1.0, 1.0)
 
 
 # ---- device entry points ------------------------------------------------------------

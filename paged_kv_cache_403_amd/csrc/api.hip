@@ -12,14 +12,25 @@ namespace {
 
 constexpr int32_t kMaxGridYZ = 65535;
 
-int elem_bytes(int32_t dtype) { return dtype == PA_F32 ? 4 : 2; }
+int elem_bytes(int32_t dtype) { return dtype == PA_F32 ? 4 : dtype == PA_FP8_E4M3 ? 1 : 2; }
+
+bool is_fp8(const pa_cache* c) { return c->dtype == PA_FP8_E4M3; }
+
+// Type of q / out / appended rows.
+int32_t act_dtype(const pa_cache* c) { return is_fp8(c) ? c->act_dtype : c->dtype; }
 
 // Validate the pool descriptor.
 int check_cache(const pa_cache* c) {
   if (!c || !c->k_cache || !c->v_cache) return PA_EINVAL;
   if (c->num_blocks <= 0 || c->num_kv_heads <= 0 || c->block_size <= 0 || c->head_dim <= 0) return PA_EINVAL;
-  if (c->dtype != PA_F32 && c->dtype != PA_F16 && c->dtype != PA_BF16) return PA_EINVAL;
+  if (c->dtype != PA_F32 && c->dtype != PA_F16 && c->dtype != PA_BF16 && c->dtype != PA_FP8_E4M3) return PA_EINVAL;
   if (c->head_dim != 64 && c->head_dim != 128) return PA_EUNSUPPORTED;
+  if (is_fp8(c)) {
+    if (c->act_dtype != PA_F16 && c->act_dtype != PA_BF16) return PA_EINVAL;
+    if (!(std::isfinite(c->k_scale) && c->k_scale > 0.f && std::isfinite(c->v_scale) && c->v_scale > 0.f))
+      return PA_EINVAL;
+    if (c->head_dim != 128) return PA_EUNSUPPORTED;
+  }
   if (c->block_size != 16 && c->block_size != 32) return PA_EUNSUPPORTED;
   if (c->num_kv_heads > kMaxGridYZ) return PA_EUNSUPPORTED;
   return PA_OK;
@@ -123,6 +134,11 @@ int pa_kv_append(const pa_cache* cache, const void* k_new, const void* v_new, co
   if (num_tokens < 0) return PA_EINVAL;
   if (num_tokens == 0) return PA_OK;
   if (!k_new || !v_new || !slot_mapping) return PA_EINVAL;
+  if (is_fp8(cache))
+    return hip_status(pa::launch_kv_append_fp8(k_new, v_new, slot_mapping, num_tokens, cache->k_cache, cache->v_cache,
+                                               cache->num_blocks, cache->num_kv_heads, cache->block_size,
+                                               cache->head_dim, cache->act_dtype, 1.0f / cache->k_scale,
+                                               1.0f / cache->v_scale, static_cast<hipStream_t>(stream)));
   return hip_status(pa::launch_kv_append(k_new, v_new, slot_mapping, num_tokens, cache->k_cache, cache->v_cache,
                                          cache->num_blocks, cache->num_kv_heads, cache->block_size, cache->head_dim,
                                          elem_bytes(cache->dtype), static_cast<hipStream_t>(stream)));
@@ -205,7 +221,12 @@ int pa_decode(const pa_cache* cache, const void* q, void* out, int32_t num_seqs,
                         : nullptr;
   a.ws_count = need > 0 ? a.ws_items + static_cast<int64_t>(num_seqs) * num_parts * 2 : nullptr;
   a.scale = scale;
+  if (is_fp8(cache)) {
+    a.k_scale = cache->k_scale;
+    a.v_scale = cache->v_scale;
+  }
   a.dtype = cache->dtype;
+  a.act_dtype = act_dtype(cache);
   a.head_dim = cache->head_dim;
   a.block_size = cache->block_size;
   a.group = group;
@@ -225,7 +246,7 @@ int pa_prefill_chunk(const pa_cache* cache, const void* q, void* out, const int3
                      int32_t max_context_len, float scale, void* stream) {
   int rc = check_cache(cache);
   if (rc != PA_OK) return rc;
-  if (cache->dtype == PA_F32) return PA_EUNSUPPORTED;
+  if (cache->dtype == PA_F32 || is_fp8(cache)) return PA_EUNSUPPORTED;
   int32_t group = 0;
   if ((rc = check_group(cache, num_q_heads, &group)) != PA_OK) return rc;
   if ((rc = check_scale(scale)) != PA_OK) return rc;
@@ -280,7 +301,7 @@ int pa_decode_grouped(const pa_cache* cache, const void* q, void* out, int32_t n
                       int32_t partition_size, void* workspace, size_t workspace_bytes, void* stream) {
   int rc = check_cache(cache);
   if (rc != PA_OK) return rc;
-  if (cache->dtype == PA_F32) return PA_EUNSUPPORTED;
+  if (cache->dtype == PA_F32 || is_fp8(cache)) return PA_EUNSUPPORTED;
   int32_t group = 0;
   if ((rc = check_group(cache, num_q_heads, &group)) != PA_OK) return rc;
   if ((rc = check_scale(scale)) != PA_OK) return rc;

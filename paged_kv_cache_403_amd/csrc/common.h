@@ -25,6 +25,12 @@ struct BF16 {
   using elem = __bf16;
   static constexpr int bytes = 2;
 };
+// One-byte OCP E4M3 codes (FP8 KV pools); widened exactly by the gfx950
+// conversion instructions.
+struct FP8 {
+  using elem = uint8_t;
+  static constexpr int bytes = 1;
+};
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
@@ -84,13 +90,76 @@ __device__ __forceinline__ float dot16<F32>(const u32x4& qv, const u32x4& kv, fl
 // Widen a 16-byte chunk to fp32 values (VEC = 16 / bytes of them).
 template <typename ST>
 __device__ __forceinline__ void widen16(const u32x4& v, float* out) {
-  if constexpr (ST::bytes == 4) {
+  if constexpr (ST::bytes == 1) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const uint32_t w = v[c];
+      const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(w, false);  // bytes 0, 1
+      const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(w, true);   // bytes 2, 3
+      out[4 * c] = lo[0];
+      out[4 * c + 1] = lo[1];
+      out[4 * c + 2] = hi[0];
+      out[4 * c + 3] = hi[1];
+    }
+  } else if constexpr (ST::bytes == 4) {
 #pragma unroll
     for (int c = 0; c < 4; ++c) out[c] = __uint_as_float(v[c]);
   } else {
 #pragma unroll
     for (int c = 0; c < 4; ++c) widen2<ST>(v[c], out[2 * c], out[2 * c + 1]);
   }
+}
+
+// fp32 dot product of 16 E4M3 codes (one 16-byte chunk of K) with the
+// matching 16 q values held as 8 packed 16-bit pairs (two 16-byte chunks):
+// each code pair is widened exactly to the q type, then v_dot2.
+template <typename AT>
+__device__ __forceinline__ float dot_fp8(const u32x4* qv, const u32x4& kv, float acc);
+template <>
+__device__ __forceinline__ float dot_fp8<F16>(const u32x4* qv, const u32x4& kv, float acc) {
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const uint32_t w = kv[c];
+    const uint32_t q0 = qv[c / 2][2 * (c % 2)], q1 = qv[c / 2][2 * (c % 2) + 1];
+    acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, q0), __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.f, false),
+                                 acc, false);
+    acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, q1), __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.f, true),
+                                 acc, false);
+  }
+  return acc;
+}
+template <>
+__device__ __forceinline__ float dot_fp8<BF16>(const u32x4* qv, const u32x4& kv, float acc) {
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const uint32_t w = kv[c];
+    const uint32_t q0 = qv[c / 2][2 * (c % 2)], q1 = qv[c / 2][2 * (c % 2) + 1];
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, q0),
+                                          __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.f, false), acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, q1),
+                                          __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.f, true), acc, false);
+  }
+  return acc;
+}
+
+// fp32 -> E4M3 code: nearest value, ties to the even code, magnitudes past
+// 448 saturate to +-448, NaN -> S.1111.111, the sign of zero kept.  Built
+// from the format's fields (RNE of the fp32 significand to 3 bits for
+// normals, of x * 2^9 to an integer below 2^-6).
+__device__ __forceinline__ uint32_t to_e4m3(float x) {
+  const uint32_t sign = (__float_as_uint(x) >> 24) & 0x80u;
+  if (x != x) return sign | 0x7Fu;
+  const float a = fminf(fabsf(x), 448.f);
+  uint32_t code;
+  if (a < 0.015625f) {  // below 2^-6: multiples of 2^-9
+    code = static_cast<uint32_t>(__builtin_rintf(a * 512.f));  // 8 is the smallest normal's code
+  } else {
+    uint32_t u = __float_as_uint(a);
+    u += 0x7FFFFu + ((u >> 20) & 1u);  // round the significand to 3 bits, ties to even
+    const uint32_t e = (u >> 23) - 127u + 7u;
+    code = (e << 3) | ((u >> 20) & 7u);
+  }
+  return sign | code;
 }
 
 __device__ __forceinline__ u32x4 load16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }

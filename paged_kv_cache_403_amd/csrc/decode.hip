@@ -42,11 +42,11 @@ namespace {
 
 // Grid (partition, KV head, sequence): used when every sequence has a single
 // partition, so no workgroup is launched without work.
-template <typename ST, int D, int BS, int G>
+template <typename ST, int D, int BS, int G, typename AT = ST>
 __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams P) {
   __shared__ DecodeLds<G, D, BS> sh;
   const int s = blockIdx.z;
-  decode_item<ST, D, BS, G>(sh, P, s, blockIdx.y, blockIdx.x, clamp_len(P.ctx_lens[s], P.max_context));
+  decode_item<ST, D, BS, G, AT>(sh, P, s, blockIdx.y, blockIdx.x, clamp_len(P.ctx_lens[s], P.max_context));
 }
 
 // Persistent variant for split contexts.  A grid the size of the chip walks
@@ -55,7 +55,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams P) {
 // one cost nothing for the partitions they do not have.  Consecutive items
 // are the KV heads of one (sequence, partition), which read neighbouring
 // tiles of the same blocks.
-template <typename ST, int D, int BS, int G>
+template <typename ST, int D, int BS, int G, typename AT = ST>
 __global__ __launch_bounds__(kThreads) void decode_persistent_kernel(DecodeParams P) {
   __shared__ DecodeLds<G, D, BS> sh;
   const int hk = P.num_kv_heads;
@@ -67,7 +67,7 @@ __global__ __launch_bounds__(kThreads) void decode_persistent_kernel(DecodeParam
     const int part = __builtin_amdgcn_readfirstlane(P.items[2 * item + 1]);
     const int L = clamp_len(P.ctx_lens[s], P.max_context);
     __syncthreads();  // the previous item's LDS merge is complete
-    decode_item<ST, D, BS, G>(sh, P, s, kvh, part, L);
+    decode_item<ST, D, BS, G, AT>(sh, P, s, kvh, part, L);
   }
 }
 
@@ -118,7 +118,8 @@ __global__ __launch_bounds__(kPlanThreads) void decode_plan_kernel(const int32_t
   if (tid == 0) *n_items = carry;
 }
 
-// Log-sum-exp merge of the partitions of one (sequence, q head).
+// Log-sum-exp merge of the partitions of one (sequence, q head); ST is the
+// output type.
 template <typename ST, int D>
 __global__ __launch_bounds__(D) void decode_reduce_kernel(const float* __restrict__ ws_ml,
                                                           const float* __restrict__ ws_o,
@@ -154,7 +155,7 @@ __global__ __launch_bounds__(D) void decode_reduce_kernel(const float* __restric
 
 // Workgroups of the persistent kernel: as many as fit on the device at once
 // (queried once per kernel instance and device).
-template <typename ST, int D, int BS, int G>
+template <typename ST, int D, int BS, int G, typename AT = ST>
 int persistent_grid() {
   constexpr int kMaxDev = 64;
   static std::atomic<int> cached[kMaxDev];  // 0 = not yet queried; racing writers store the same value
@@ -165,7 +166,7 @@ int persistent_grid() {
     int cus = 0, per_cu = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &per_cu, reinterpret_cast<const void*>(&decode_persistent_kernel<ST, D, BS, G>), kThreads, 0) !=
+            &per_cu, reinterpret_cast<const void*>(&decode_persistent_kernel<ST, D, BS, G, AT>), kThreads, 0) !=
             hipSuccess ||
         per_cu <= 0)
       per_cu = 2;
@@ -175,7 +176,7 @@ int persistent_grid() {
   return n;
 }
 
-template <typename ST, int D, int BS, int G>
+template <typename ST, int D, int BS, int G, typename AT = ST>
 hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t st) {
   DecodeParams P{};
   P.q = a.q;
@@ -188,7 +189,8 @@ hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t st) {
   P.out = a.out;
   P.ws_ml = a.ws_ml;
   P.ws_o = a.ws_o;
-  P.scale_log2 = a.scale * kLog2e;
+  P.scale_log2 = a.scale * kLog2e * a.k_scale;
+  P.v_scale = a.v_scale;
   P.max_blocks = a.max_blocks_per_seq;
   P.max_context = a.max_context_len;
   P.num_blocks = a.num_blocks;
@@ -196,7 +198,7 @@ hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t st) {
   P.part_tokens = a.part_tokens;
   P.max_parts = a.num_parts;
   if (a.num_parts <= 1) {
-    hipLaunchKernelGGL((decode_kernel<ST, D, BS, G>), dim3(1, a.num_kv_heads, a.num_seqs), dim3(kThreads), 0, st, P);
+    hipLaunchKernelGGL((decode_kernel<ST, D, BS, G, AT>), dim3(1, a.num_kv_heads, a.num_seqs), dim3(kThreads), 0, st, P);
     return hipGetLastError();
   }
   hipLaunchKernelGGL(decode_plan_kernel, dim3(1), dim3(kPlanThreads), 0, st, a.context_lens, a.num_seqs,
@@ -204,34 +206,34 @@ hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t st) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t upper = static_cast<int64_t>(a.num_seqs) * a.num_parts * a.num_kv_heads;
-  const int grid = static_cast<int>(std::min<int64_t>(upper, persistent_grid<ST, D, BS, G>()));
-  hipLaunchKernelGGL((decode_persistent_kernel<ST, D, BS, G>), dim3(grid), dim3(kThreads), 0, st, P);
+  const int grid = static_cast<int>(std::min<int64_t>(upper, persistent_grid<ST, D, BS, G, AT>()));
+  hipLaunchKernelGGL((decode_persistent_kernel<ST, D, BS, G, AT>), dim3(grid), dim3(kThreads), 0, st, P);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int num_q_heads = a.num_kv_heads * G;
-  hipLaunchKernelGGL((decode_reduce_kernel<ST, D>), dim3(num_q_heads, a.num_seqs), dim3(D),
+  hipLaunchKernelGGL((decode_reduce_kernel<AT, D>), dim3(num_q_heads, a.num_seqs), dim3(D),
                      a.num_parts * sizeof(float), st, a.ws_ml, a.ws_o, a.context_lens,
                      a.max_context_len, a.part_tokens, a.num_parts, num_q_heads,
-                     static_cast<typename ST::elem*>(a.out));
+                     static_cast<typename AT::elem*>(a.out));
   return hipGetLastError();
 }
 
-template <typename ST, int D, int BS>
+template <typename ST, int D, int BS, typename AT = ST>
 hipError_t by_group(const DecodeArgs& a, hipStream_t st) {
   switch (a.group) {
-    case 1: return launch_decode_t<ST, D, BS, 1>(a, st);
-    case 2: return launch_decode_t<ST, D, BS, 2>(a, st);
-    case 4: return launch_decode_t<ST, D, BS, 4>(a, st);
-    case 8: return launch_decode_t<ST, D, BS, 8>(a, st);
+    case 1: return launch_decode_t<ST, D, BS, 1, AT>(a, st);
+    case 2: return launch_decode_t<ST, D, BS, 2, AT>(a, st);
+    case 4: return launch_decode_t<ST, D, BS, 4, AT>(a, st);
+    case 8: return launch_decode_t<ST, D, BS, 8, AT>(a, st);
   }
   return hipErrorInvalidValue;
 }
 
-template <typename ST, int D>
+template <typename ST, int D, typename AT = ST>
 hipError_t by_block(const DecodeArgs& a, hipStream_t st) {
   switch (a.block_size) {
-    case 16: return by_group<ST, D, 16>(a, st);
-    case 32: return by_group<ST, D, 32>(a, st);
+    case 16: return by_group<ST, D, 16, AT>(a, st);
+    case 32: return by_group<ST, D, 32, AT>(a, st);
   }
   return hipErrorInvalidValue;
 }
@@ -245,6 +247,16 @@ hipError_t by_dim(const DecodeArgs& a, hipStream_t st) {
   return hipErrorInvalidValue;
 }
 
+// FP8 pool: head_dim 128, 16-bit activations.
+hipError_t by_act_fp8(const DecodeArgs& a, hipStream_t st) {
+  if (a.head_dim != 128) return hipErrorInvalidValue;
+  switch (a.act_dtype) {
+    case 1: return by_block<FP8, 128, F16>(a, st);
+    case 2: return by_block<FP8, 128, BF16>(a, st);
+  }
+  return hipErrorInvalidValue;
+}
+
 }  // namespace
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t st) {
@@ -252,6 +264,7 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t st) {
     case 0: return by_dim<F32>(a, st);
     case 1: return by_dim<F16>(a, st);
     case 2: return by_dim<BF16>(a, st);
+    case 3: return by_act_fp8(a, st);
   }
   return hipErrorInvalidValue;
 }

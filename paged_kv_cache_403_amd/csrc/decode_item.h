@@ -37,7 +37,7 @@ struct DecodeShape {
   static_assert(NI >= 1 && RPI * NI == BS, "tile rows");
   static_assert(NRED <= NI, "a lane's scores share one head");
   static_assert(HALV >= LOG_G, "head bits");
-  static_assert(CPD >= 2 && CPD <= 8, "token groups");
+  static_assert(CPD >= 1 && CPD <= 8, "token groups");
 };
 
 // ---- transposing butterfly over the lanes of one K row -----------------------
@@ -148,7 +148,8 @@ struct DecodeParams {
   void* out;
   float* ws_ml;
   float* ws_o;
-  float scale_log2;
+  float scale_log2;  // softmax scale * log2(e) (* k_scale for an FP8 pool)
+  float v_scale;     // FP8 pool: V value = code * v_scale
   int32_t max_blocks, max_context, num_blocks, num_kv_heads, part_tokens, max_parts;
 };
 
@@ -172,17 +173,22 @@ __device__ __forceinline__ int clamp_len(int L, int max_context) {
 // sequence's own part as `start` (the partitions then cover start..L-1) and
 // `partial` to leave partials, at slot slot0 + part, even for a single
 // partition.
-template <typename ST, int D, int BS, int G>
+// ST is the pool's element type, AT the type of q and out (the same except
+// for FP8 pools, whose codes meet 16-bit q values).
+template <typename ST, int D, int BS, int G, typename AT = ST>
 __device__ __forceinline__ void decode_item(DecodeLds<G, D, BS>& sh, const DecodeParams& P, int s, int kvh,
                                             int part, int L, int start = 0, int slot0 = 0, bool partial = false) {
   using S = DecodeShape<ST, D, BS, G>;
   constexpr int VEC = S::VEC, LPR = S::LPR, RPI = S::RPI, NI = S::NI, NV = S::NV, NRED = S::NRED,
                 CPD = S::CPD;
+  constexpr int QCH = VEC * AT::bytes / 16;  // 16-byte q chunks per K chunk
+  static_assert(ST::bytes == AT::bytes || (ST::bytes == 1 && AT::bytes == 2), "pool / activation types");
   using elem = typename ST::elem;
-  const elem* __restrict__ q = static_cast<const elem*>(P.q);
+  using aelem = typename AT::elem;
+  const aelem* __restrict__ q = static_cast<const aelem*>(P.q);
   const elem* __restrict__ kc = static_cast<const elem*>(P.kc);
   const elem* __restrict__ vc = static_cast<const elem*>(P.vc);
-  elem* __restrict__ out = static_cast<elem*>(P.out);
+  aelem* __restrict__ out = static_cast<aelem*>(P.out);
   const int num_kv_heads = P.num_kv_heads;
   const int num_q_heads = num_kv_heads * G;
   const int part_tokens = P.part_tokens;
@@ -199,7 +205,7 @@ __device__ __forceinline__ void decode_item(DecodeLds<G, D, BS>& sh, const Decod
   if (L == 0 && !partial) {
     if (part == 0) {
       for (int e = tid; e < G * D; e += kThreads)
-        out[(static_cast<int64_t>(s) * num_q_heads + kvh * G) * D + e] = narrow<ST>(0.f);
+        out[(static_cast<int64_t>(s) * num_q_heads + kvh * G) * D + e] = narrow<AT>(0.f);
     }
     return;
   }
@@ -220,10 +226,12 @@ __device__ __forceinline__ void decode_item(DecodeLds<G, D, BS>& sh, const Decod
 #pragma unroll
   for (int t = S::HALV; t < ilog2(LPR); ++t) owner = owner && !(seg & (LPR >> (t + 1)));
 
-  u32x4 qv[G];
-  const elem* qrow = q + (static_cast<int64_t>(s) * num_q_heads + kvh * G) * D + seg * VEC;
+  u32x4 qv[G][QCH];
+  const aelem* qrow = q + (static_cast<int64_t>(s) * num_q_heads + kvh * G) * D + seg * VEC;
 #pragma unroll
-  for (int h = 0; h < G; ++h) qv[h] = load16(qrow + h * D);
+  for (int h = 0; h < G; ++h)
+#pragma unroll
+    for (int c = 0; c < QCH; ++c) qv[h][c] = load16(qrow + h * D + c * (16 / AT::bytes));
 
   float m[G], acc[G][NI];
 #pragma unroll
@@ -263,7 +271,12 @@ __device__ __forceinline__ void decode_item(DecodeLds<G, D, BS>& sh, const Decod
 #pragma unroll
     for (int h = 0; h < G; ++h)
 #pragma unroll
-      for (int i = 0; i < NI; ++i) v[h * NI + i] = dot16<ST>(qv[h], kr[i], 0.f);
+      for (int i = 0; i < NI; ++i) {
+        if constexpr (ST::bytes == 1)
+          v[h * NI + i] = dot_fp8<AT>(qv[h], kr[i], 0.f);
+        else
+          v[h * NI + i] = dot16<ST>(qv[h][0], kr[i], 0.f);
+      }
     RowReduce<NV, LPR, 0>::run(v, seg);
     float bm = -INFINITY;
 #pragma unroll
@@ -410,11 +423,13 @@ __device__ __forceinline__ void decode_item(DecodeLds<G, D, BS>& sh, const Decod
       }
     }
     const int64_t qh = static_cast<int64_t>(s) * num_q_heads + kvh * G + h;
+    float o = num / den;
+    if constexpr (ST::bytes == 1) o *= P.v_scale;
     if (nparts == 1 && !partial) {
-      out[qh * D + d] = narrow<ST>(num / den);
+      out[qh * D + d] = narrow<AT>(o);
     } else {
       const int64_t pidx = qh * P.max_parts + slot0 + part;
-      P.ws_o[pidx * D + d] = num / den;
+      P.ws_o[pidx * D + d] = o;
       if (d == 0) {
         P.ws_ml[2 * pidx] = M;
         P.ws_ml[2 * pidx + 1] = den;

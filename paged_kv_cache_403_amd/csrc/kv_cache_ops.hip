@@ -1,5 +1,6 @@
-// Data movement into the paged pool: token append through a slot mapping,
-// and whole-block copies for copy-on-write.
+// Data movement into the paged pool: token append through a slot mapping
+// (quantising to E4M3 codes for an FP8 pool), and whole-block copies for
+// copy-on-write.
 //
 // Append (zzmblog.top vLLM guide, "Transformer推理与KV缓存"; lshu.cn/news/11644,
 // "方案：页式内存管理"): token t's K and V rows ([num_kv_heads][head_dim]) go
@@ -52,6 +53,46 @@ __global__ __launch_bounds__(256) void kv_append_kernel(const u32x4* __restrict_
   }
 }
 
+// Append into an FP8 pool: one thread per 16 elements of a (token, head)
+// row (two 16-byte chunks of 16-bit activations), each multiplied by the
+// fp32 reciprocal of its scale and rounded to an E4M3 code; the K codes are
+// stored as one 16-byte chunk, the V codes go to 16 rows of the transposed
+// tile.
+template <typename AT>
+__global__ __launch_bounds__(256) void kv_append_fp8_kernel(const u32x4* __restrict__ k_new,
+                                                            const u32x4* __restrict__ v_new,
+                                                            const int64_t* __restrict__ slots, int64_t total_groups,
+                                                            int groups_per_row, int num_kv_heads, int block_size,
+                                                            int64_t num_slots, float k_inv, float v_inv,
+                                                            u32x4* __restrict__ kc, uint8_t* __restrict__ vc) {
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < total_groups;
+       i += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+    const int c = static_cast<int>(i % groups_per_row);
+    const int64_t th = i / groups_per_row;  // token * heads + head
+    const int h = static_cast<int>(th % num_kv_heads);
+    const int64_t t = th / num_kv_heads;
+    const int64_t slot = slots[t];
+    if (slot < 0 || slot >= num_slots) continue;
+    const int64_t blk = slot / block_size;
+    const int64_t off = slot % block_size;
+    const int64_t tile = blk * num_kv_heads + h;
+    float x[16];
+    widen16<AT>(k_new[2 * i], x);
+    widen16<AT>(k_new[2 * i + 1], x + 8);
+    u32x4 kq;
+#pragma unroll
+    for (int w = 0; w < 4; ++w)
+      kq[w] = to_e4m3(x[4 * w] * k_inv) | (to_e4m3(x[4 * w + 1] * k_inv) << 8) |
+              (to_e4m3(x[4 * w + 2] * k_inv) << 16) | (to_e4m3(x[4 * w + 3] * k_inv) << 24);
+    kc[(tile * block_size + off) * groups_per_row + c] = kq;
+    widen16<AT>(v_new[2 * i], x);
+    widen16<AT>(v_new[2 * i + 1], x + 8);
+    uint8_t* vt = vc + (tile * (groups_per_row * 16) + c * 16) * block_size + off;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) vt[static_cast<int64_t>(k) * block_size] = static_cast<uint8_t>(to_e4m3(x[k] * v_inv));
+  }
+}
+
 // blockIdx.y = pair; the block's tiles are copied as 16-byte chunks.
 __global__ __launch_bounds__(256) void copy_blocks_kernel(const int32_t* __restrict__ pairs, int num_blocks,
                                                           int64_t chunks_per_block, u32x4* __restrict__ kc,
@@ -90,6 +131,23 @@ hipError_t launch_kv_append(const void* k_new, const void* v_new, const int64_t*
                        static_cast<const u32x4*>(v_new), slots, total, chunks_per_row, num_kv_heads, block_size,
                        num_slots, static_cast<u32x4*>(k_cache), static_cast<uint16_t*>(v_cache));
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_kv_append_fp8(const void* k_new, const void* v_new, const int64_t* slots, int32_t num_tokens,
+                                void* k_cache, void* v_cache, int32_t num_blocks, int32_t num_kv_heads,
+                                int32_t block_size, int32_t head_dim, int32_t act_dtype, float k_inv, float v_inv,
+                                hipStream_t st) {
+  const int groups_per_row = head_dim / 16;
+  const int64_t total = static_cast<int64_t>(num_tokens) * num_kv_heads * groups_per_row;
+  if (total == 0) return hipSuccess;
+  const int64_t want = (total + 255) / 256;
+  const int grid = static_cast<int>(want < 8192 ? want : 8192);
+  const int64_t num_slots = static_cast<int64_t>(num_blocks) * block_size;
+  auto kern = act_dtype == 1 ? kv_append_fp8_kernel<F16> : kv_append_fp8_kernel<BF16>;
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(256), 0, st, static_cast<const u32x4*>(k_new),
+                     static_cast<const u32x4*>(v_new), slots, total, groups_per_row, num_kv_heads, block_size, num_slots,
+                     k_inv, v_inv, static_cast<u32x4*>(k_cache), static_cast<uint8_t*>(v_cache));
   return hipGetLastError();
 }
 

@@ -19,7 +19,9 @@ struct DecodeArgs {
   int32_t* ws_items;  // [S * num_parts][2]  (sequence, partition) work list
   int32_t* ws_count;  // [1]  entries in ws_items
   float scale;
+  float k_scale = 1.f, v_scale = 1.f;  // FP8 pool scales (1 otherwise)
   int32_t dtype, head_dim, block_size, group;
+  int32_t act_dtype;  // q / out type: dtype, or F16 / BF16 for an FP8 pool
   int32_t num_seqs, num_kv_heads, num_blocks, max_blocks_per_seq;
   int32_t max_context_len;  // host bound; device lengths are clamped to it
   int32_t part_tokens;  // tokens per partition (multiple of block_size)
@@ -61,6 +63,13 @@ struct PrefillArgs {
 hipError_t launch_kv_append(const void* k_new, const void* v_new, const int64_t* slots, int32_t num_tokens,
                             void* k_cache, void* v_cache, int32_t num_blocks, int32_t num_kv_heads,
                             int32_t block_size, int32_t head_dim, int32_t elem_bytes, hipStream_t st);
+
+// Append into an FP8 pool: rows of act_dtype (F16 / BF16) quantised with the
+// fp32 reciprocals of the scales.
+hipError_t launch_kv_append_fp8(const void* k_new, const void* v_new, const int64_t* slots, int32_t num_tokens,
+                                void* k_cache, void* v_cache, int32_t num_blocks, int32_t num_kv_heads,
+                                int32_t block_size, int32_t head_dim, int32_t act_dtype, float k_inv, float v_inv,
+                                hipStream_t st);
 
 hipError_t launch_copy_blocks(const int32_t* pairs, int32_t num_pairs, void* k_cache, void* v_cache,
                               int32_t num_blocks, int64_t block_bytes, hipStream_t st);

@@ -52,17 +52,27 @@ class StepPlan:
 
 
 class PagedKVCache:
+    """dtype: the activation type (q, out, appended rows).  kv_dtype "fp8"
+    makes the pool E4M3 codes (uint8) with scales k_scale / v_scale; a
+    fill_value then fills unused slots with the NaN code if it is NaN, else
+    with the largest finite code."""
+
     def __init__(self, num_blocks, num_kv_heads, block_size, head_dim, dtype: str, device="cuda",
-                 free_order=None, fill_value=None):
+                 free_order=None, fill_value=None, kv_dtype=None, k_scale=1.0, v_scale=1.0):
         self.dtype = dtype
+        self.kv_dtype = kv_dtype or dtype
         self.device = torch.device(device)
-        td = TORCH_DTYPE[dtype]
+        td = torch.uint8 if self.kv_dtype == "fp8" else TORCH_DTYPE[dtype]
         self.k = torch.empty((num_blocks, num_kv_heads, block_size, head_dim), dtype=td, device=self.device)
         self.v = torch.empty((num_blocks, num_kv_heads, head_dim, block_size), dtype=td, device=self.device)
         if fill_value is not None:
-            self.k.fill_(fill_value)
-            self.v.fill_(fill_value)
-        self.desc = B.make_cache(self.k, self.v)
+            fill = (0x7F if np.isnan(fill_value) else 0x7E) if self.kv_dtype == "fp8" else fill_value
+            self.k.fill_(fill)
+            self.v.fill_(fill)
+        if self.kv_dtype == "fp8":
+            self.desc = B.make_cache(self.k, self.v, TORCH_DTYPE[dtype], k_scale, v_scale)
+        else:
+            self.desc = B.make_cache(self.k, self.v)
         self.bm = B.BlockManager(num_blocks, block_size, free_order)
         self.block_size = block_size
         self.num_blocks = num_blocks

@@ -37,7 +37,7 @@ def run_step(wl, fill=SENTINEL, free_order=None, partition_size=0, device="cuda"
     sp = wl.spec
     order = wl.free_order if free_order is None else free_order
     cache = PagedKVCache(sp.num_blocks, sp.num_kv_heads, sp.block_size, sp.head_dim, sp.dtype, device, order,
-                         fill_value=fill)
+                         fill_value=fill, kv_dtype=sp.kv_dtype or None, k_scale=sp.k_scale, v_scale=sp.v_scale)
     setup_slots = cache.apply_ops(wl.setup_ops())
     batch = wl.batch
     plan = cache.prepare_step([p.seq_id for p in batch], [p.n_new for p in batch], sp.poison_block)

@@ -122,3 +122,35 @@ def test_repeatable():
     a = run_step(wl, keep_pool=False, grouped=True, group_start=hint)
     b = run_step(wl, keep_pool=False, grouped=True, group_start=hint)
     assert np.array_equal(a.out, b.out)
+
+
+def test_shared_prefix_fullsize_sampled():
+    """Full-size shared-prefix workload through grouped decode in the launch
+    configuration bench.py times (natural hints, 512-token partitions):
+    sampled rows -- every group's longest sequence and one more member of
+    each group, a random q head each -- against attention of the row over
+    its sequence's logical K/V (fp64)."""
+    wl = workloads.make("gqa_shared_prefix")
+    sp = wl.spec
+    print("[gpu] grouped full size gqa_shared_prefix", flush=True)
+    res = run_step(wl, partition_size=512, keep_pool=False, grouped=True, group_start=workloads.group_starts(wl))
+    batch = wl.batch
+    lens = np.array([p.context_len for p in batch])
+    starts = workloads.group_starts(wl)
+    rng = np.random.default_rng(403)
+    G = sp.num_q_heads // sp.num_kv_heads
+    picks = []
+    for a, b in zip(starts[:-1], starts[1:]):
+        picks.append(a + int(np.argmax(lens[a:b])))
+        picks.append(int(rng.integers(a, b)))
+    worst = 0.0
+    for r in sorted(set(picks)):
+        p = batch[r]
+        h = int(rng.integers(sp.num_q_heads))
+        K, V = wl.logical_kv(p.seq_id)
+        ref = A.attention_rows(wl.q[p.seq_id][0:1, h], K[:, h // G], V[:, h // G], [p.context_len - 1], sp.scale,
+                               sp.dtype)[0]
+        err = float(np.abs(to_f64(res.out[r, h], sp.dtype) - ref).max())
+        worst = max(worst, err)
+        assert err <= TOL[sp.dtype], (r, h, err)
+    print(f"[gpu]   sampled max|err| = {worst:.3e} over {len(set(picks))} rows", flush=True)

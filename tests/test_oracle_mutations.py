@@ -67,7 +67,7 @@ class _LifoBM(BMmod.BlockManager):
         return b
 
 
-def _gather_next_slot(pk, pv, table, L, dtype):
+def _gather_next_slot(pk, pv, table, L, dtype, kv=None):
     """Slip: reads the slot after the right one inside each block."""
     bs = pk.shape[2]
     j = np.arange(L)
