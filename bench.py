@@ -12,10 +12,11 @@ Headline workload: 7B-shaped MHA decode (64 sequences, contexts U{128..2048},
 32 q = 32 KV heads, head_dim 128, fp16, block_size 16).  `value` is the
 step's algorithmic bytes (K/V read, q/out, tables, append) over the step time.
 Secondary measurements: chunked prefill on the mixed workload (8 chunks of
-512 tokens on cached contexts U{0..4096}, 32/8 heads, bf16) in TFLOP/s, and
+512 tokens on cached contexts U{0..4096}, 32/8 heads, bf16) in TFLOP/s;
 plain vs prefix-grouped decode on the shared-prefix workload (256 sequences
 in groups of 8 forked from 512-token prompts, 32/8 heads, bf16), where the
-grouped path reads each shared block once.
+grouped path reads each shared block once; and the headline decode batch
+again with an FP8 (E4M3) pool, whose K/V bytes are half.
 
 Prints one JSON line on stdout; progress goes to stderr.
 """
@@ -37,11 +38,13 @@ def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
 
-def decode_bytes(lens, num_q_heads, num_kv_heads, head_dim, block_size, eb):
+def decode_bytes(lens, num_q_heads, num_kv_heads, head_dim, block_size, eb, kv_eb=None):
+    """Algorithmic bytes of decode: K/V read (kv_eb bytes per element, eb if
+    None), q read and out written (eb), table entries and lengths."""
     import numpy as np
 
     lens = np.asarray(lens, dtype=np.int64)
-    kv = int(lens.sum()) * num_kv_heads * head_dim * eb * 2
+    kv = int(lens.sum()) * num_kv_heads * head_dim * (kv_eb or eb) * 2
     qo = len(lens) * num_q_heads * head_dim * eb * 2
     meta = int(((lens + block_size - 1) // block_size).sum()) * 4 + len(lens) * 4
     return int(kv + qo + meta), int(kv)
@@ -72,7 +75,8 @@ class Step:
         self.wl = wl
         t0 = time.time()
         self.cache = PagedKVCache(sp.num_blocks, sp.num_kv_heads, sp.block_size, sp.head_dim, sp.dtype, device,
-                                  wl.free_order, fill_value=1.0e4)
+                                  wl.free_order, fill_value=1.0e4, kv_dtype=sp.kv_dtype or None, k_scale=sp.k_scale,
+                                  v_scale=sp.v_scale)
         self.cache.apply_ops(wl.setup_ops())
         batch = wl.batch
         self.plan = self.cache.prepare_step([p.seq_id for p in batch], [p.n_new for p in batch], sp.poison_block)
@@ -99,7 +103,7 @@ class Step:
                               if partition_size == -1 else partition_size)
             self.dec_bytes, self.dec_kv_bytes = decode_bytes(self.plan.host_lens[dec], sp.num_q_heads,
                                                              sp.num_kv_heads, sp.head_dim, sp.block_size,
-                                                             sp.elem_bytes)
+                                                             sp.elem_bytes, sp.kv_elem_bytes)
         else:
             self.dec_bytes = self.dec_kv_bytes = 0
         if len(pre):
@@ -118,10 +122,10 @@ class Step:
         else:
             self.pre_flops = 0
         T = int(n_new.sum())
-        eb = sp.elem_bytes
-        self.append_bytes = T * sp.num_kv_heads * sp.head_dim * eb * 4 + T * 8
+        eb, kb = sp.elem_bytes, sp.kv_elem_bytes
+        self.append_bytes = T * sp.num_kv_heads * sp.head_dim * (eb + kb) * 2 + T * 8
         npairs = len(self.plan.host_pairs)
-        self.copy_bytes = npairs * sp.num_kv_heads * sp.block_size * sp.head_dim * eb * 4 + npairs * 8
+        self.copy_bytes = npairs * sp.num_kv_heads * sp.block_size * sp.head_dim * kb * 4 + npairs * 8
         torch.cuda.synchronize()
         log(f"{sp.name}: setup {time.time() - t0:.1f}s, {len(dec)} decode seqs, {len(pre)} chunks, "
             f"{npairs} copy pairs")
@@ -259,6 +263,40 @@ def decode_group_starts(wl, dec):
     return np.array(starts, dtype=np.int32)
 
 
+def time_decode(st, iters, warmup):
+    """Average decode launch time (HIP events on the library's stream), us."""
+    import torch
+
+    for _ in range(warmup):
+        st.decode()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(iters):
+        st.decode()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / iters * 1e3
+
+
+def measure_fp8(name, ref_us, iters, warmup):
+    """Decode of the same batch with an FP8 (E4M3) pool and 16-bit
+    activations: time, algorithmic bytes (1-byte K/V), rate, and the speedup
+    over the 16-bit pool's decode time ref_us."""
+    import workloads
+
+    wl = workloads.with_fp8_kv(workloads.make(name))
+    st = Step(wl, -1)
+    st.copy_append()
+    us = time_decode(st, iters, warmup)
+    gbs = st.dec_bytes / (us * 1e-6) / 1e9
+    log(f"{wl.spec.name}: decode {us:.1f} us, {gbs:.0f} GB/s, x{ref_us / us:.2f} over the 16-bit pool")
+    return {"workload": wl.spec.name, "kv_dtype": "fp8 e4m3", "act_dtype": wl.spec.dtype,
+            "k_scale": wl.spec.k_scale, "v_scale": wl.spec.v_scale, "decode_us": round(us, 2),
+            "bytes_per_launch": st.dec_bytes, "achieved_gbs": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4),
+            "speedup_vs_16bit_pool": round(ref_us / us, 3), "decode_partition_tokens": st.part_used}
+
+
 def measure_grouped(name, iters, warmup):
     """Plain split decode against prefix-grouped decode on one workload's
     decode batch: HIP-event times on the library's stream, and the K/V bytes
@@ -325,6 +363,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true", help="skip the chunked-prefill measurement")
     ap.add_argument("--no-grouped", action="store_true", help="skip the plain vs grouped decode measurement")
+    ap.add_argument("--no-fp8", action="store_true", help="skip the FP8 KV-pool decode measurement")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB a few times (the known-size reference for "
                          "the HBM byte counters) and exit")
@@ -403,6 +442,8 @@ def main():
         }
     if not args.no_grouped:
         result["shared_prefix"] = measure_grouped("gqa_shared_prefix", max(10, args.steps // 2), 3)
+    if not args.no_fp8 and sp.dtype in ("f16", "bf16"):
+        result["fp8_kv"] = measure_fp8(args.workload, dc_ms * 1e3, max(10, args.steps // 2), 3)
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a sample")
         result["cpu_baseline"] = cpu_baseline(wl)
