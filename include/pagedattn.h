@@ -31,10 +31,13 @@
  *    0 and lengths clamped to the host bounds; the result for that
  *    token/sequence is then undefined, and nothing faults.
  *  - Compiled instances: dtype {f32, f16, bf16} x head_dim {64, 128} x
- *    block_size {16, 32}; num_q_heads a multiple of num_kv_heads with group
- *    size num_q_heads/num_kv_heads in {1, 2, 4, 8}.  pa_prefill_chunk needs
- *    f16 or bf16 (its contractions run on the matrix cores).  An FP8 pool
- *    (see pa_cache) has head_dim 128 and f16 or bf16 activations, and is
+ *    block_size {8, 16, 32, 64} (zzmblog.top vLLM guide, "核心参数调优":
+ *    larger blocks for long contexts, 8 for many short sequences);
+ *    num_q_heads a multiple of num_kv_heads with group size
+ *    num_q_heads/num_kv_heads in {1, 2, 4, 8}.  pa_prefill_chunk needs f16
+ *    or bf16 (its contractions run on the matrix cores); pa_decode_grouped
+ *    needs f16 or bf16 and block_size 16 or 32.  An FP8 pool (see pa_cache)
+ *    has head_dim 128, block_size 16..64 and f16 or bf16 activations, and is
  *    supported by pa_kv_append, pa_copy_blocks and pa_decode.
  */
 #ifndef PAGEDATTN_H
@@ -261,6 +264,16 @@ int32_t pa_bm_num_free(const pa_bm* bm);
 int32_t pa_bm_free_list(const pa_bm* bm, int32_t* out, int32_t cap);
 /* Reference count of a block (0 when free or never handed out). */
 int32_t pa_bm_refcount(const pa_bm* bm, int32_t block);
+
+/* Pool occupancy, for the memory-waste figure the pages compare against
+ * static reservation (lshu.cn/news/11644, "问题：KV Cache 的内存困境" and
+ * "收益分析"; m.ypxx.net, "2.1 PagedAttention分页注意力核心机制": paged
+ * blocks leave at most a partly filled last block per sequence).
+ * blocks_in_use: blocks with a nonzero reference count; slots_filled: over
+ * those blocks, the slots holding tokens (a block shared by several
+ * sequences counts the most any of them has written into it).  Internal
+ * waste = 1 - slots_filled / (blocks_in_use * block_size). */
+int pa_bm_usage(const pa_bm* bm, int64_t* blocks_in_use, int64_t* slots_filled);
 
 #ifdef __cplusplus
 }

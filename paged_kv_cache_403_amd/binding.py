@@ -77,6 +77,7 @@ _SIGNATURES = {
     "pa_bm_num_free": (_i32, [_vp]),
     "pa_bm_free_list": (_i32, [_vp, _vp, _i32]),
     "pa_bm_refcount": (_i32, [_vp, _i32]),
+    "pa_bm_usage": (ctypes.c_int, [_vp, _vp, _vp]),
 }
 
 
@@ -320,3 +321,9 @@ class BlockManager:
 
     def refcount(self, block: int) -> int:
         return int(lib().pa_bm_refcount(self._h, block))
+
+    def usage(self):
+        """(blocks in use, filled slots of those blocks)."""
+        held, used = ctypes.c_int64(0), ctypes.c_int64(0)
+        _check(lib().pa_bm_usage(self._h, ctypes.byref(held), ctypes.byref(used)), "pa_bm_usage")
+        return int(held.value), int(used.value)

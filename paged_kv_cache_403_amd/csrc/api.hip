@@ -29,9 +29,9 @@ int check_cache(const pa_cache* c) {
     if (c->act_dtype != PA_F16 && c->act_dtype != PA_BF16) return PA_EINVAL;
     if (!(std::isfinite(c->k_scale) && c->k_scale > 0.f && std::isfinite(c->v_scale) && c->v_scale > 0.f))
       return PA_EINVAL;
-    if (c->head_dim != 128) return PA_EUNSUPPORTED;
+    if (c->head_dim != 128 || c->block_size < 16) return PA_EUNSUPPORTED;
   }
-  if (c->block_size != 16 && c->block_size != 32) return PA_EUNSUPPORTED;
+  if (c->block_size != 8 && c->block_size != 16 && c->block_size != 32 && c->block_size != 64) return PA_EUNSUPPORTED;
   if (c->num_kv_heads > kMaxGridYZ) return PA_EUNSUPPORTED;
   return PA_OK;
 }
@@ -257,7 +257,7 @@ int pa_prefill_chunk(const pa_cache* cache, const void* q, void* out, const int3
     return PA_EINVAL;
   if (num_seqs > kMaxGridYZ) return PA_EUNSUPPORTED;
   // the block-table entries of the longest context are staged in LDS
-  if (pa::prefill_lds_bytes(cache->dtype, cache->head_dim, max_context_len) > pa::kPrefillMaxLds)
+  if (pa::prefill_lds_bytes(cache->dtype, cache->head_dim, cache->block_size, max_context_len) > pa::kPrefillMaxLds)
     return PA_EUNSUPPORTED;
   if (num_seqs == 0 || total_q == 0 || max_q_len == 0) return PA_OK;
   if (!q || !out || !cu_q_lens || !context_lens || !block_tables) return PA_EINVAL;
@@ -302,6 +302,7 @@ int pa_decode_grouped(const pa_cache* cache, const void* q, void* out, int32_t n
   int rc = check_cache(cache);
   if (rc != PA_OK) return rc;
   if (cache->dtype == PA_F32 || is_fp8(cache)) return PA_EUNSUPPORTED;
+  if (cache->block_size != 16 && cache->block_size != 32) return PA_EUNSUPPORTED;
   int32_t group = 0;
   if ((rc = check_group(cache, num_q_heads, &group)) != PA_OK) return rc;
   if ((rc = check_scale(scale)) != PA_OK) return rc;

@@ -18,6 +18,8 @@
 #include <unordered_map>
 #include <vector>
 
+#include <algorithm>
+
 #include "pagedattn.h"
 
 namespace {
@@ -219,6 +221,30 @@ int32_t pa_bm_free_list(const pa_bm* bm, int32_t* out, int32_t cap) {
     out[n++] = b;
   }
   return n;
+}
+
+int pa_bm_usage(const pa_bm* bm, int64_t* blocks_in_use, int64_t* slots_filled) {
+  if (!bm || !blocks_in_use || !slots_filled) return PA_EINVAL;
+  // filled slots of each held block: the most any holder has written into it
+  std::vector<int32_t> filled(bm->num_blocks, 0);
+  for (const auto& kv : bm->seqs) {
+    const Seq& q = kv.second;
+    for (size_t j = 0; j < q.table.size(); ++j) {
+      const int64_t f = std::min<int64_t>(bm->block_size, q.len - static_cast<int64_t>(j) * bm->block_size);
+      int32_t& slot = filled[q.table[j]];
+      slot = std::max<int32_t>(slot, static_cast<int32_t>(std::max<int64_t>(f, 0)));
+    }
+  }
+  int64_t held = 0, used = 0;
+  for (int32_t b = 0; b < bm->num_blocks; ++b) {
+    if (bm->ref[b] > 0) {
+      ++held;
+      used += filled[b];
+    }
+  }
+  *blocks_in_use = held;
+  *slots_filled = used;
+  return PA_OK;
 }
 
 int32_t pa_bm_refcount(const pa_bm* bm, int32_t block) {

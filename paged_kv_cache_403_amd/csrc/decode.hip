@@ -232,8 +232,12 @@ hipError_t by_group(const DecodeArgs& a, hipStream_t st) {
 template <typename ST, int D, typename AT = ST>
 hipError_t by_block(const DecodeArgs& a, hipStream_t st) {
   switch (a.block_size) {
+    case 8:
+      if constexpr (ST::bytes == 1) return hipErrorInvalidValue;  // a 16-byte chunk of codes spans 16 keys
+      else return by_group<ST, D, 8, AT>(a, st);
     case 16: return by_group<ST, D, 16, AT>(a, st);
     case 32: return by_group<ST, D, 32, AT>(a, st);
+    case 64: return by_group<ST, D, 64, AT>(a, st);
   }
   return hipErrorInvalidValue;
 }

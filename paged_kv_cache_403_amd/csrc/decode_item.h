@@ -153,12 +153,16 @@ struct DecodeParams {
   int32_t max_blocks, max_context, num_blocks, num_kv_heads, part_tokens, max_parts;
 };
 
+// Key tile of the decode loop: a whole block up to 32 tokens, else 32-token
+// parts of a block.
+constexpr int decode_tile(int BS) { return BS > 32 ? 32 : BS; }
+
 template <int G, int D, int BS>
 struct DecodeLds {
   float red_acc[kWaves][G][D];
   float red_m[kWaves][G];
   float red_l[kWaves][G];
-  __attribute__((aligned(16))) float p_lds[kWaves][G][BS];
+  __attribute__((aligned(16))) float p_lds[kWaves][G][decode_tile(BS)];
 };
 
 __device__ __forceinline__ int clamp_len(int L, int max_context) {
@@ -178,7 +182,9 @@ __device__ __forceinline__ int clamp_len(int L, int max_context) {
 template <typename ST, int D, int BS, int G, typename AT = ST>
 __device__ __forceinline__ void decode_item(DecodeLds<G, D, BS>& sh, const DecodeParams& P, int s, int kvh,
                                             int part, int L, int start = 0, int slot0 = 0, bool partial = false) {
-  using S = DecodeShape<ST, D, BS, G>;
+  constexpr int TS = decode_tile(BS);  // tokens per key tile
+  constexpr int SUB = BS / TS;         // tiles per block
+  using S = DecodeShape<ST, D, TS, G>;
   constexpr int VEC = S::VEC, LPR = S::LPR, RPI = S::RPI, NI = S::NI, NV = S::NV, NRED = S::NRED,
                 CPD = S::CPD;
   constexpr int QCH = VEC * AT::bytes / 16;  // 16-byte q chunks per K chunk
@@ -214,7 +220,8 @@ __device__ __forceinline__ void decode_item(DecodeLds<G, D, BS>& sh, const Decod
   const int tok_begin = start + part * part_tokens;  // a multiple of BS
   const int tok_end = min(L, tok_begin + part_tokens);
   const int blk_begin = tok_begin / BS;
-  const int nb = (tok_end + BS - 1) / BS - blk_begin;  // blocks in this partition
+  const int tile_begin = tok_begin / TS;                 // a multiple of SUB
+  const int nb = (tok_end + TS - 1) / TS - tile_begin;  // key tiles in this partition
 
   // where this lane's reduced scores sit: head h_own, tokens i*RPI + row
   int off = 0;
@@ -246,26 +253,30 @@ __device__ __forceinline__ void decode_item(DecodeLds<G, D, BS>& sh, const Decod
   const int64_t head_off = static_cast<int64_t>(kvh) * BS * D;
   const int64_t blk_stride = static_cast<int64_t>(num_kv_heads) * BS * D;
   const int lane_off = lane * VEC;
+  // a V^T tile part is TS keys of each of D rows (rows BS apart)
+  const int v_lane_off = SUB == 1 ? lane_off : (lane / CPD) * BS + (lane % CPD) * VEC;
   const int num_blocks = P.num_blocks;
 
   const int my_blocks = nb > wave ? (nb - wave + kWaves - 1) / kWaves : 0;
 
   // address of a tile from its physical block id (never dereferenced out of range)
-  auto load_tile = [&](int b, u32x4* kr, u32x4* vr) {
+  auto load_tile = [&](int b, int sub, u32x4* kr, u32x4* vr) {
     b = (b >= 0 && b < num_blocks) ? b : 0;
-    const int64_t base = static_cast<int64_t>(b) * blk_stride + head_off + lane_off;
+    const int64_t base = static_cast<int64_t>(b) * blk_stride + head_off;
+    const int64_t kbase = base + sub * TS * D + lane_off;
+    const int64_t vbase = base + sub * TS + v_lane_off;
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
-      kr[i] = load16_nt(kc + base + i * 64 * VEC);
-      vr[i] = load16_nt(vc + base + i * 64 * VEC);
+      kr[i] = load16_nt(kc + kbase + i * 64 * VEC);
+      vr[i] = load16_nt(vc + vbase + i * (64 / CPD) * BS);
     }
   };
 
   float* pw = &sh.p_lds[wave][0][0];
 
   auto process = [&](int j, const u32x4* kr, const u32x4* vr) {
-    const int blk = blk_begin + wave + j * kWaves;
-    const bool partial = blk * BS + BS > tok_end;
+    const int t0 = (tile_begin + wave + j * kWaves) * TS;  // first token of the tile
+    const bool partial = t0 + TS > tok_end;
     // QK partial dot products, index h*NI + i
     float v[NV];
 #pragma unroll
@@ -282,7 +293,7 @@ __device__ __forceinline__ void decode_item(DecodeLds<G, D, BS>& sh, const Decod
 #pragma unroll
     for (int j2 = 0; j2 < NRED; ++j2) {
       float x = v[j2] * scale_log2;
-      if (partial) x = (blk * BS + (i_own + j2) * RPI + row < tok_end) ? x : -INFINITY;
+      if (partial) x = (t0 + (i_own + j2) * RPI + row < tok_end) ? x : -INFINITY;
       v[j2] = x;
       bm = fmaxf(bm, x);
     }
@@ -305,7 +316,7 @@ __device__ __forceinline__ void decode_item(DecodeLds<G, D, BS>& sh, const Decod
     for (int j2 = 0; j2 < NRED; ++j2) {
       const float p = __builtin_amdgcn_exp2f(v[j2] - m[h_own]);
       ps += p;
-      pw[h_own * BS + (i_own + j2) * RPI + row] = p;
+      pw[h_own * TS + (i_own + j2) * RPI + row] = p;
     }
     l_own = l_own * alpha[h_own] + (owner ? ps : 0.f);
     wave_lds_sync();
@@ -316,7 +327,7 @@ __device__ __forceinline__ void decode_item(DecodeLds<G, D, BS>& sh, const Decod
     if (partial) {
 #pragma unroll
       for (int c = 0; c < VEC; ++c) {
-        const bool ok = blk * BS + tg * VEC + c < tok_end;
+        const bool ok = t0 + tg * VEC + c < tok_end;
 #pragma unroll
         for (int i = 0; i < NI; ++i) vt[i][c] = ok ? vt[i][c] : 0.f;
       }
@@ -326,7 +337,7 @@ __device__ __forceinline__ void decode_item(DecodeLds<G, D, BS>& sh, const Decod
       float p[VEC];
 #pragma unroll
       for (int c = 0; c < VEC; c += 4) {
-        const float4 x = *reinterpret_cast<const float4*>(pw + h * BS + tg * VEC + c);
+        const float4 x = *reinterpret_cast<const float4*>(pw + h * TS + tg * VEC + c);
         p[c] = x.x;
         p[c + 1] = x.y;
         p[c + 2] = x.z;
@@ -352,18 +363,19 @@ __device__ __forceinline__ void decode_item(DecodeLds<G, D, BS>& sh, const Decod
   // an unrolled tail.
   for (int c0 = 0; c0 < my_blocks; c0 += 64) {
     const int cn = min(64, my_blocks - c0);
-    const int tv = lane < cn ? trow[wave + (c0 + lane) * kWaves] : 0;
+    const int tv = lane < cn ? trow[(wave + (c0 + lane) * kWaves) / SUB] : 0;
     auto block_id = [&](int j) -> int { return __builtin_amdgcn_readlane(tv, j); };
+    auto sub_of = [&](int j) -> int { return SUB == 1 ? 0 : (wave + (c0 + j) * kWaves) % SUB; };
     constexpr int NB = S::NBUF;
     u32x4 kb[NB][NI], vb[NB][NI];
 #pragma unroll
     for (int b = 0; b < NB - 1; ++b)
-      if (b < cn) load_tile(block_id(b), kb[b], vb[b]);
+      if (b < cn) load_tile(block_id(b), sub_of(b), kb[b], vb[b]);
     int j0 = 0;
     for (; j0 + 2 * NB - 2 < cn; j0 += NB) {
 #pragma unroll
       for (int b = 0; b < NB; ++b) {
-        load_tile(block_id(j0 + b + NB - 1), kb[(b + NB - 1) % NB], vb[(b + NB - 1) % NB]);
+        load_tile(block_id(j0 + b + NB - 1), sub_of(j0 + b + NB - 1), kb[(b + NB - 1) % NB], vb[(b + NB - 1) % NB]);
         process(c0 + j0 + b, kb[b], vb[b]);
       }
     }
@@ -371,7 +383,8 @@ __device__ __forceinline__ void decode_item(DecodeLds<G, D, BS>& sh, const Decod
     for (int b = 0; b < 2 * NB - 1; ++b) {
       const int j = j0 + b;
       if (j < cn) {
-        if (j + NB - 1 < cn) load_tile(block_id(j + NB - 1), kb[(b + NB - 1) % NB], vb[(b + NB - 1) % NB]);
+        if (j + NB - 1 < cn)
+          load_tile(block_id(j + NB - 1), sub_of(j + NB - 1), kb[(b + NB - 1) % NB], vb[(b + NB - 1) % NB]);
         process(c0 + j, kb[b % NB], vb[b % NB]);
       }
     }

@@ -82,6 +82,6 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st);
 // the block-table entries of every key tile (bound by max_context_len).  The
 // bound leaves 1 KiB of the 160 KiB for the kernel's static LDS.
 constexpr size_t kPrefillMaxLds = 159 * 1024;
-size_t prefill_lds_bytes(int32_t dtype, int32_t head_dim, int32_t max_context_len);
+size_t prefill_lds_bytes(int32_t dtype, int32_t head_dim, int32_t block_size, int32_t max_context_len);
 
 }  // namespace pa

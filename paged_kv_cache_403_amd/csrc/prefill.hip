@@ -383,8 +383,10 @@ hipError_t by_group(const PrefillArgs& a, hipStream_t st) {
 template <typename ST, int D>
 hipError_t by_block(const PrefillArgs& a, hipStream_t st) {
   switch (a.block_size) {
+    case 8: return by_group<ST, D, 8>(a, st);
     case 16: return by_group<ST, D, 16>(a, st);
     case 32: return by_group<ST, D, 32>(a, st);
+    case 64: return by_group<ST, D, 64>(a, st);
   }
   return hipErrorInvalidValue;
 }
@@ -400,13 +402,14 @@ hipError_t by_dim(const PrefillArgs& a, hipStream_t st) {
 
 }  // namespace
 
-size_t prefill_lds_bytes(int32_t dtype, int32_t head_dim, int32_t max_context_len) {
+size_t prefill_lds_bytes(int32_t dtype, int32_t head_dim, int32_t block_size, int32_t max_context_len) {
   (void)dtype;  // both matrix-core types are 16-bit
   const size_t stage = static_cast<size_t>(kKeys) * (head_dim + 8) + static_cast<size_t>(head_dim) * (kKeys + 8);
   const size_t max_tiles = (static_cast<size_t>(max_context_len) + kKeys - 1) / kKeys;
-  // table entries (64 keys per tile over blocks of at least 16 tokens), or
-  // the item costs of the longest-first ordering if more
-  return 2 * stage * 2 + std::max<size_t>(max_tiles * (kKeys / 16), kSortMax) * sizeof(int32_t);
+  const size_t blocks_per_tile = block_size >= kKeys ? 1 : kKeys / block_size;
+  // table entries of every tile, or the item costs of the longest-first
+  // ordering if more
+  return 2 * stage * 2 + std::max<size_t>(max_tiles * blocks_per_tile, kSortMax) * sizeof(int32_t);
 }
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st) {

@@ -438,3 +438,13 @@ def with_fp8_kv(wl: Workload, k_scale: float = FP8_K_SCALE, v_scale: float = FP8
         raise ValueError("FP8 pools take 16-bit activations")
     spec = replace(wl.spec, name=wl.spec.name + "_fp8", kv_dtype="fp8", k_scale=k_scale, v_scale=v_scale)
     return replace(wl, spec=spec)
+
+
+def with_block_size(wl: Workload, block_size: int) -> Workload:
+    """The same sequences and values on a pool of another block size: the
+    pool is re-sized for it and its free order drawn again (from a stream of
+    its own), everything else is kept."""
+    spec = replace(wl.spec, name=f"{wl.spec.name}_bs{block_size}", block_size=block_size,
+                   num_blocks=sized_pool(wl.seqs, block_size))
+    g = np.random.default_rng(np.random.SeedSequence(list(_stream(wl.seed, 1, block_size))))
+    return replace(wl, spec=spec, free_order=g.permutation(spec.num_blocks - 1).astype(np.int32))
