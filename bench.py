@@ -15,8 +15,9 @@ Secondary measurements: chunked prefill on the mixed workload (8 chunks of
 512 tokens on cached contexts U{0..4096}, 32/8 heads, bf16) in TFLOP/s;
 plain vs prefix-grouped decode on the shared-prefix workload (256 sequences
 in groups of 8 forked from 512-token prompts, 32/8 heads, bf16), where the
-grouped path reads each shared block once; and the headline decode batch
-again with an FP8 (E4M3) pool, whose K/V bytes are half.
+grouped path reads each shared block once; the headline decode batch again
+with an FP8 (E4M3) pool, whose K/V bytes are half; and that batch on pools
+of block size 8, 16, 32 and 64 with each pool's unused share.
 
 Prints one JSON line on stdout; progress goes to stderr.
 """
@@ -279,6 +280,34 @@ def time_decode(st, iters, warmup):
     return a.elapsed_time(b) / iters * 1e3
 
 
+def measure_block_sizes(name, iters, warmup, sizes=(8, 16, 32, 64)):
+    """The same decode batch on pools of several block sizes: decode time
+    and rate, and the pool's unused share from the library's block manager
+    (1 - filled slots / slots of the blocks held) next to what reserving the
+    batch's longest context for every sequence would leave unused."""
+    import numpy as np
+
+    import workloads
+
+    base = workloads.make(name)
+    rows = []
+    for bs in sizes:
+        wl = base if bs == base.spec.block_size else workloads.with_block_size(base, bs)
+        st = Step(wl, -1)
+        st.copy_append()
+        us = time_decode(st, iters, warmup)
+        held, used = st.cache.bm.usage()
+        rows.append({"block_size": bs, "decode_us": round(us, 2),
+                     "achieved_gbs": round(st.dec_bytes / (us * 1e-6) / 1e9, 1),
+                     "decode_partition_tokens": st.part_used, "blocks_in_use": held,
+                     "paged_waste": round(1.0 - used / (held * bs), 5)})
+        log(f"{name} block_size {bs}: decode {us:.1f} us, unused share {rows[-1]['paged_waste']:.4f}")
+    lens = np.array([p.context_len for p in base.batch], dtype=np.int64)
+    static = 1.0 - float(lens.sum()) / float(len(lens) * lens.max())
+    return {"workload": name, "sizes": rows, "static_reservation_waste": round(static, 4),
+            "static_reservation_tokens": int(lens.max())}
+
+
 def measure_fp8(name, ref_us, iters, warmup):
     """Decode of the same batch with an FP8 (E4M3) pool and 16-bit
     activations: time, algorithmic bytes (1-byte K/V), rate, and the speedup
@@ -364,6 +393,7 @@ def main():
     ap.add_argument("--no-prefill", action="store_true", help="skip the chunked-prefill measurement")
     ap.add_argument("--no-grouped", action="store_true", help="skip the plain vs grouped decode measurement")
     ap.add_argument("--no-fp8", action="store_true", help="skip the FP8 KV-pool decode measurement")
+    ap.add_argument("--no-block-sizes", action="store_true", help="skip the block-size sweep")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB a few times (the known-size reference for "
                          "the HBM byte counters) and exit")
@@ -444,6 +474,8 @@ def main():
         result["shared_prefix"] = measure_grouped("gqa_shared_prefix", max(10, args.steps // 2), 3)
     if not args.no_fp8 and sp.dtype in ("f16", "bf16"):
         result["fp8_kv"] = measure_fp8(args.workload, dc_ms * 1e3, max(10, args.steps // 2), 3)
+    if not args.no_block_sizes:
+        result["block_sizes"] = measure_block_sizes(args.workload, max(10, args.steps // 2), 3)
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a sample")
         result["cpu_baseline"] = cpu_baseline(wl)

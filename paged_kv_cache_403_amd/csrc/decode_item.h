@@ -153,16 +153,23 @@ struct DecodeParams {
   int32_t max_blocks, max_context, num_blocks, num_kv_heads, part_tokens, max_parts;
 };
 
-// Key tile of the decode loop: a whole block up to 32 tokens, else 32-token
-// parts of a block.
-constexpr int decode_tile(int BS) { return BS > 32 ? 32 : BS; }
+// Key tile of the decode loop: a whole block, except that 64-token blocks
+// are walked in 32-token parts where a whole block's registers (K and V
+// chunks, G heads of accumulators) would leave one wavefront per SIMD or
+// spill: fp32 pools, and 16-bit pools of head_dim 128 with more than 2 q
+// heads per KV head (more than 4 at head_dim 64 or with 1-byte codes).
+template <typename ST, int D, int G>
+constexpr int decode_tile(int BS) {
+  return BS <= 32 ? BS
+                  : ((ST::bytes == 1 && G <= 4) || (ST::bytes == 2 && (G <= 2 || (D == 64 && G <= 4))) ? 64 : 32);
+}
 
 template <int G, int D, int BS>
 struct DecodeLds {
   float red_acc[kWaves][G][D];
   float red_m[kWaves][G];
   float red_l[kWaves][G];
-  __attribute__((aligned(16))) float p_lds[kWaves][G][decode_tile(BS)];
+  __attribute__((aligned(16))) float p_lds[kWaves][G][BS];
 };
 
 __device__ __forceinline__ int clamp_len(int L, int max_context) {
@@ -182,7 +189,7 @@ __device__ __forceinline__ int clamp_len(int L, int max_context) {
 template <typename ST, int D, int BS, int G, typename AT = ST>
 __device__ __forceinline__ void decode_item(DecodeLds<G, D, BS>& sh, const DecodeParams& P, int s, int kvh,
                                             int part, int L, int start = 0, int slot0 = 0, bool partial = false) {
-  constexpr int TS = decode_tile(BS);  // tokens per key tile
+  constexpr int TS = decode_tile<ST, D, G>(BS);  // tokens per key tile
   constexpr int SUB = BS / TS;         // tiles per block
   using S = DecodeShape<ST, D, TS, G>;
   constexpr int VEC = S::VEC, LPR = S::LPR, RPI = S::RPI, NI = S::NI, NV = S::NV, NRED = S::NRED,
