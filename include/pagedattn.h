@@ -275,6 +275,50 @@ int32_t pa_bm_refcount(const pa_bm* bm, int32_t block);
  * waste = 1 - slots_filled / (blocks_in_use * block_size). */
 int pa_bm_usage(const pa_bm* bm, int64_t* blocks_in_use, int64_t* slots_filled);
 
+/* ---- host scheduler loop (CPU only, no HIP calls) --------------------------
+ * One call of pa_sched_step is one iteration of the centralized scheduler
+ * (lshu.cn/news/11644, "整体架构": check the free pool, pull waiting requests,
+ * allocate blocks, prefill long prompts in chunks over several iterations,
+ * batch every running request's current token, and free a finished
+ * request's blocks at once), over a block manager the caller owns.  Request
+ * ids are sequence ids of that manager (>= 0, unused there).  Conventions:
+ * a token budget per iteration; decode tokens first (oldest admission
+ * first), then the next chunk of prompts being prefilled, then new requests
+ * in arrival order; a chunk is bounded by the prompt's remainder, the budget
+ * left and the pool's room; a decode token that finds the pool empty
+ * preempts the newest running request not yet scheduled in the iteration
+ * (freed, put back at the front of the queue, prefilled again from its
+ * first token); the iteration that caches a prompt's last token yields the
+ * first new token, each decode one more; a request that has produced
+ * max_new_tokens finishes and its blocks are freed by the next call.  The
+ * caller runs each batch's kernels (append, then prefill / decode) before
+ * the next call, on one stream. */
+typedef struct pa_sched pa_sched;
+
+typedef struct {
+  int32_t num_decode;    /* reqs[0 .. num_decode-1]: one token each */
+  int32_t num_prefill;   /* reqs[num_decode ..]: prompt chunks of n_new tokens */
+  int64_t num_slots;     /* slots[]: the batch's tokens in batch order */
+  int32_t num_pairs;     /* copy pairs (none without forks) */
+  int32_t num_finished;  /* requests whose last token this batch yields */
+  int32_t num_preempted; /* requests sent back to the queue */
+} pa_sched_batch;
+
+/* NULL on bad arguments.  `bm` must outlive the scheduler. */
+pa_sched* pa_sched_create(pa_bm* bm, int32_t max_batched_tokens, int32_t max_running);
+void pa_sched_destroy(pa_sched* s);
+/* Queue a request (arrival order = call order). */
+int pa_sched_add(pa_sched* s, int32_t req, int32_t prompt_len, int32_t max_new_tokens);
+/* Requests not yet finished (queued or running). */
+int32_t pa_sched_unfinished(const pa_sched* s);
+/* One iteration.  Host outputs: reqs / n_new [cap >= min(requests,
+ * max_running)], slots [slot_cap >= max_batched_tokens], pairs [pair_cap]
+ * (may be NULL with pair_cap 0), finished / preempted [list_cap >= requests
+ * added].  PA_EINVAL (too small) before any state changes. */
+int pa_sched_step(pa_sched* s, int32_t* reqs, int32_t* n_new, int32_t cap, int64_t* slots, int64_t slot_cap,
+                  int32_t* pairs, int32_t pair_cap, int32_t* finished, int32_t* preempted, int32_t list_cap,
+                  pa_sched_batch* out);
+
 #ifdef __cplusplus
 }
 #endif

@@ -78,7 +78,23 @@ _SIGNATURES = {
     "pa_bm_free_list": (_i32, [_vp, _vp, _i32]),
     "pa_bm_refcount": (_i32, [_vp, _i32]),
     "pa_bm_usage": (ctypes.c_int, [_vp, _vp, _vp]),
+    "pa_sched_create": (_vp, [_vp, _i32, _i32]),
+    "pa_sched_destroy": (None, [_vp]),
+    "pa_sched_add": (ctypes.c_int, [_vp, _i32, _i32, _i32]),
+    "pa_sched_unfinished": (_i32, [_vp]),
+    "pa_sched_step": (ctypes.c_int, [_vp, _vp, _vp, _i32, _vp, ctypes.c_int64, _vp, _i32, _vp, _vp, _i32, _vp]),
 }
+
+
+class pa_sched_batch(ctypes.Structure):
+    _fields_ = [
+        ("num_decode", ctypes.c_int32),
+        ("num_prefill", ctypes.c_int32),
+        ("num_slots", ctypes.c_int64),
+        ("num_pairs", ctypes.c_int32),
+        ("num_finished", ctypes.c_int32),
+        ("num_preempted", ctypes.c_int32),
+    ]
 
 
 def lib():
@@ -327,3 +343,48 @@ class BlockManager:
         held, used = ctypes.c_int64(0), ctypes.c_int64(0)
         _check(lib().pa_bm_usage(self._h, ctypes.byref(held), ctypes.byref(used)), "pa_bm_usage")
         return int(held.value), int(used.value)
+
+
+class Scheduler:
+    """The library's scheduler loop over a `BlockManager` (which must outlive
+    it).  step() returns (decode ids, [(prefill id, tokens)], slots int64,
+    copy pairs int32 [n][2], finished ids, preempted ids)."""
+
+    def __init__(self, bm: "BlockManager", max_batched_tokens: int, max_running: int):
+        self._bm = bm
+        self._h = lib().pa_sched_create(bm._h, int(max_batched_tokens), int(max_running))
+        if not self._h:
+            raise ValueError("pa_sched_create: bad arguments")
+        self.budget, self.max_running, self._n = int(max_batched_tokens), int(max_running), 0
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h and _lib is not None:
+            _lib.pa_sched_destroy(h)
+            self._h = None
+
+    def add(self, req: int, prompt_len: int, max_new_tokens: int):
+        _check(lib().pa_sched_add(self._h, int(req), int(prompt_len), int(max_new_tokens)), "pa_sched_add")
+        self._n += 1
+
+    def unfinished(self) -> int:
+        return int(lib().pa_sched_unfinished(self._h))
+
+    def step(self):
+        cap = max(min(self._n, self.max_running), 1)
+        reqs = np.zeros(cap, np.int32)
+        n_new = np.zeros(cap, np.int32)
+        slots = np.zeros(self.budget, np.int64)
+        pairs = np.zeros((max(self.budget, 1), 2), np.int32)
+        lst = max(self._n, 1)
+        fin = np.zeros(lst, np.int32)
+        pre = np.zeros(lst, np.int32)
+        out = pa_sched_batch()
+        _check(lib().pa_sched_step(self._h, _np_ptr(reqs), _np_ptr(n_new), cap, _np_ptr(slots), self.budget,
+                                   _np_ptr(pairs), pairs.shape[0], _np_ptr(fin), _np_ptr(pre), lst,
+                                   ctypes.byref(out)), "pa_sched_step")
+        nd, npf = out.num_decode, out.num_prefill
+        decodes = reqs[:nd].tolist()
+        prefills = list(zip(reqs[nd:nd + npf].tolist(), n_new[nd:nd + npf].tolist()))
+        return (decodes, prefills, slots[:out.num_slots].copy(), pairs[:out.num_pairs].copy(),
+                fin[:out.num_finished].tolist(), pre[:out.num_preempted].tolist())

@@ -64,7 +64,8 @@ def _prefill(cache, num_seqs=2, total_q=10, num_q_heads=32, max_blocks=8, max_q=
     (dict(num_blocks=0), P.PA_EINVAL),
     (dict(dtype=7), P.PA_EINVAL),
     (dict(head_dim=96), P.PA_EUNSUPPORTED),
-    (dict(block_size=8), P.PA_EUNSUPPORTED),
+    (dict(block_size=12), P.PA_EUNSUPPORTED),
+    (dict(block_size=128), P.PA_EUNSUPPORTED),
 ])
 def test_cache_descriptor_validation(kw, code):
     assert _decode(_cache(**kw)) == code
@@ -91,6 +92,23 @@ def test_cache_descriptor_validation(kw, code):
 ])
 def test_decode_validation(kw, code):
     assert _decode(_cache(), **kw) == code
+
+
+def test_fp8_descriptor_validation():
+    def fp8(**kw):
+        c = _cache(dtype=P.PA_FP8_E4M3, **{k: v for k, v in kw.items() if k not in ("act", "ks", "vs")})
+        c.act_dtype, c.k_scale, c.v_scale = kw.get("act", P.PA_BF16), kw.get("ks", 0.5), kw.get("vs", 0.5)
+        return c
+    assert _decode(fp8(act=P.PA_F32)) == P.PA_EINVAL
+    assert _decode(fp8(ks=0.0)) == P.PA_EINVAL
+    assert _decode(fp8(vs=float("inf"))) == P.PA_EINVAL
+    assert _decode(fp8(head_dim=64)) == P.PA_EUNSUPPORTED
+    assert _decode(fp8(block_size=8)) == P.PA_EUNSUPPORTED
+    assert _prefill(fp8()) == P.PA_EUNSUPPORTED
+    assert _grouped(fp8()) == P.PA_EUNSUPPORTED
+    # block sizes 8 and 64 pass the descriptor checks (then fail on max_ctx here)
+    assert _decode(_cache(block_size=8), max_ctx=100) == P.PA_EINVAL
+    assert _decode(_cache(block_size=64), num_seqs=0) == P.PA_OK
 
 
 def test_decode_null_cache_and_empty_batch():

@@ -448,3 +448,17 @@ def with_block_size(wl: Workload, block_size: int) -> Workload:
                    num_blocks=sized_pool(wl.seqs, block_size))
     g = np.random.default_rng(np.random.SeedSequence(list(_stream(wl.seed, 1, block_size))))
     return replace(wl, spec=spec, free_order=g.permutation(spec.num_blocks - 1).astype(np.int32))
+
+
+def arrival_trace(n_requests: int, seed: int = 0, median_prompt: int = 160, max_prompt: int = 1500,
+                  max_new: int = 48, mean_gap: float = 0.7):
+    """Synthetic request arrivals for the scheduler loop: (arrival
+    iteration, request id, prompt tokens, new tokens to produce), in
+    arrival order.  Prompts lognormal (sigma 1) around median_prompt,
+    capped; new tokens uniform in 1..max_new; gaps between arrivals
+    exponential with mean mean_gap iterations (several may share one)."""
+    g = np.random.default_rng(np.random.SeedSequence([SEED_ROOT, 77, seed]))
+    prompts = np.clip(np.rint(np.exp(g.normal(math.log(median_prompt), 1.0, size=n_requests))), 1, max_prompt)
+    news = g.integers(1, max_new, size=n_requests, endpoint=True)
+    t = np.floor(np.cumsum(g.exponential(mean_gap, size=n_requests))).astype(np.int64)
+    return [(int(t[i]), i, int(prompts[i]), int(news[i])) for i in range(n_requests)]
