@@ -41,11 +41,35 @@ namespace pa {
 namespace {
 
 // Grid (partition, KV head, sequence): used when every sequence has a single
-// partition, so no workgroup is launched without work.
+// partition, so no workgroup is launched without work.  Workgroups are
+// dispatched in blockIdx order, so with up to kRankMax sequences the one at
+// grid position z takes the z-th longest sequence (ties by index): the
+// longest contexts start first and the short ones fill the tail, instead of
+// a long one starting last and running alone (greedy longest-first list
+// scheduling).  Each workgroup ranks the lengths itself from LDS.
+constexpr int kRankMax = 256;
 template <typename ST, int D, int BS, int G, typename AT = ST>
 __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams P) {
   __shared__ DecodeLds<G, D, BS> sh;
-  const int s = blockIdx.z;
+  __shared__ int lens_sh[kRankMax];
+  __shared__ int pick;
+  const int S = gridDim.z;
+  int s = blockIdx.z;
+  if (S <= kRankMax) {
+    for (int t = threadIdx.x; t < S; t += kThreads) lens_sh[t] = clamp_len(P.ctx_lens[t], P.max_context);
+    __syncthreads();
+    for (int t = threadIdx.x; t < S; t += kThreads) {
+      const int Lt = lens_sh[t];
+      int r = 0;
+      for (int j = 0; j < S; ++j) {
+        const int Lj = lens_sh[j];
+        r += (Lj > Lt) || (Lj == Lt && j < t);
+      }
+      if (r == static_cast<int>(blockIdx.z)) pick = t;
+    }
+    __syncthreads();
+    s = __builtin_amdgcn_readfirstlane(pick);
+  }
   decode_item<ST, D, BS, G, AT>(sh, P, s, blockIdx.y, blockIdx.x, clamp_len(P.ctx_lens[s], P.max_context));
 }
 
@@ -72,50 +96,58 @@ __global__ __launch_bounds__(kThreads) void decode_persistent_kernel(DecodeParam
 }
 
 // Work list of the persistent kernel: every (sequence, partition) pair with
-// tokens in it, in sequence order (a sequence of length 0 gets one pair, whose
-// item writes its zero output).  One workgroup scans the lengths 1024 at a
-// time.
+// tokens in it (a sequence of length 0 gets one pair, whose item writes its
+// zero output), largest first.  The persistent grid deals the list out round
+// robin, so putting the full partitions first and the short last ones after
+// them in falling size leaves short items for the end -- the same
+// longest-first rule as the one-pass grid.  A counting sort over kPlanBuckets
+// size classes of part_tokens / kPlanBuckets tokens (order inside a class is
+// whatever the atomics give; each pair is computed the same way wherever it
+// lands).
 constexpr int kPlanThreads = 1024;
+constexpr int kPlanBuckets = 32;
 
 __global__ __launch_bounds__(kPlanThreads) void decode_plan_kernel(const int32_t* __restrict__ ctx_lens, int num_seqs,
                                                                    int max_context, int part_tokens,
                                                                    int32_t* __restrict__ items,
                                                                    int32_t* __restrict__ n_items) {
-  __shared__ int wave_tot[kPlanThreads / 64];
-  const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
-  int carry = 0;
-  for (int base = 0; base < num_seqs; base += kPlanThreads) {
-    const int s = base + tid;
-    int np = 0;
-    if (s < num_seqs) {
-      const int L = clamp_len(ctx_lens[s], max_context);
-      np = L == 0 ? 1 : (L + part_tokens - 1) / part_tokens;
-    }
-    // inclusive scan over the wavefront, then over the wavefront totals
-    int x = np;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int y = __shfl_up(x, o, 64);
-      if (lane >= o) x += y;
-    }
-    if (lane == 63) wave_tot[wave] = x;
-    __syncthreads();
-    int before = carry, total = 0;
-#pragma unroll
-    for (int w = 0; w < kPlanThreads / 64; ++w) {
-      const int t = wave_tot[w];
-      before += w < wave ? t : 0;
-      total += t;
-    }
-    const int first = before + x - np;
-    for (int p = 0; p < np; ++p) {
-      items[2 * (first + p)] = s;
-      items[2 * (first + p) + 1] = p;
-    }
-    carry += total;
-    __syncthreads();  // wave_tot is rewritten by the next round
+  __shared__ int count[kPlanBuckets];
+  __shared__ int start[kPlanBuckets];
+  const int tid = threadIdx.x;
+  // size class of a partition of t tokens (t = 0 only for an empty sequence)
+  auto bucket = [&](int t) { return t <= 0 ? 0 : static_cast<int>((static_cast<int64_t>(t - 1) * kPlanBuckets) / part_tokens); };
+  if (tid < kPlanBuckets) count[tid] = 0;
+  __syncthreads();
+  for (int s = tid; s < num_seqs; s += kPlanThreads) {
+    const int L = clamp_len(ctx_lens[s], max_context);
+    const int np = L == 0 ? 1 : (L + part_tokens - 1) / part_tokens;
+    if (np > 1) atomicAdd(&count[kPlanBuckets - 1], np - 1);
+    atomicAdd(&count[bucket(L - (np - 1) * part_tokens)], 1);
   }
-  if (tid == 0) *n_items = carry;
+  __syncthreads();
+  if (tid == 0) {
+    int acc = 0;
+    for (int k = kPlanBuckets - 1; k >= 0; --k) {
+      start[k] = acc;
+      acc += count[k];
+    }
+    *n_items = acc;
+  }
+  __syncthreads();
+  for (int s = tid; s < num_seqs; s += kPlanThreads) {
+    const int L = clamp_len(ctx_lens[s], max_context);
+    const int np = L == 0 ? 1 : (L + part_tokens - 1) / part_tokens;
+    if (np > 1) {
+      const int first = atomicAdd(&start[kPlanBuckets - 1], np - 1);
+      for (int p = 0; p < np - 1; ++p) {
+        items[2 * (first + p)] = s;
+        items[2 * (first + p) + 1] = p;
+      }
+    }
+    const int at = atomicAdd(&start[bucket(L - (np - 1) * part_tokens)], 1);
+    items[2 * at] = s;
+    items[2 * at + 1] = np - 1;
+  }
 }
 
 // Log-sum-exp merge of the partitions of one (sequence, q head); ST is the
