@@ -342,7 +342,7 @@ def measure_grouped(name, iters, warmup):
     st.copy_append()
     hint = torch.from_numpy(decode_group_starts(wl, st.dec)).to("cuda")
     n = len(st.dec)
-    part = 512
+    part = 1024
     wsb = P.pa_decode_grouped_workspace_bytes(n, sp.num_q_heads, sp.head_dim, st.max_dec, part)
     ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
     out = torch.empty_like(st.q_dec)

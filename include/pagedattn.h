@@ -176,7 +176,7 @@ size_t pa_decode_grouped_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, 
  *                   tables how many leading full blocks each sequence has in
  *                   common with its chunk's longest sequence; any grouping
  *                   (NULL with num_groups 0 included) gives the same result
- *   partition_size  0 = 256; else a multiple of 32 and of block_size, at
+ *   partition_size  0 = 1024; else a multiple of 32 and of block_size, at
  *                   most 64 blocks: tokens per partition of both the shared
  *                   prefix and each sequence's own suffix
  *   workspace       device scratch of at least
@@ -184,8 +184,8 @@ size_t pa_decode_grouped_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, 
  *                   call, so calls sharing it must be ordered on one stream
  * PA_EUNSUPPORTED above 4096 sequences, or when (num_q_heads /
  * num_kv_heads) * 2 * ceil(max_context_len / partition) exceeds 16384 (the
- * merge's per-head slot weights live in 64 KiB of LDS; with 256-token
- * partitions that is 262144 tokens of context at 8 q heads per KV head).  Runs four kernels
+ * merge's per-head slot weights live in 64 KiB of LDS; with 1024-token
+ * partitions that is 1048576 tokens of context at 8 q heads per KV head).  Runs four kernels
  * on `stream`: a one-workgroup planner, the shared-prefix kernel (matrix
  * cores, one chunk's rows per workgroup), the suffix partitions of the split
  * decode kernel, and the log-sum-exp merge. */

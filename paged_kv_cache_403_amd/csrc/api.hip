@@ -74,7 +74,7 @@ size_t workspace_for(int64_t num_seqs, int64_t num_q_heads, int64_t head_dim, in
 
 // Prefix-grouped decode: partitions of `part` tokens, 2 * ceil(C / part)
 // slots per row (prefix slots of the chunk, then the sequence's own).
-constexpr int32_t kGroupedDefaultPartition = 256;
+constexpr int32_t kGroupedDefaultPartition = 1024;
 constexpr int64_t kGroupedMergeLds = 64 * 1024;
 
 struct GroupedLayout {
@@ -161,13 +161,14 @@ int32_t pa_decode_choose_partition(const pa_cache* cache, int32_t num_seqs, int3
   (void)num_q_heads;
   if (!cache || cache->num_kv_heads <= 0 || cache->block_size <= 0) return 0;
   const int64_t units = static_cast<int64_t>(num_seqs) * cache->num_kv_heads;
-  // One pass when the batch alone fills the chip and contexts are short.
-  // Otherwise split: with many sequences (lengths likely uneven) into
-  // 512-token partitions, which balance the load; with few, into the
-  // longest partitions (up to 2048 tokens) that still give about a thousand
-  // work items, since every partition has a fixed start-up cost.
-  if (max_context_len <= 512 || (units >= 1024 && max_context_len <= 2048)) return 0;
-  if (units >= 256) return 512;
+  // One pass when the batch gives the chip about two workgroups per compute
+  // unit or more and no context is long: the one-pass grid starts the
+  // longest sequences first, so uneven lengths balance out.  Otherwise split
+  // into the longest partitions (up to 2048 tokens) that still give about a
+  // thousand work items, since every partition has a fixed start-up cost;
+  // long contexts beside short ones are then cut into pieces the short ones
+  // can fill in around.
+  if (max_context_len <= 512 || (units >= 512 && max_context_len <= 4096)) return 0;
   int32_t p = 2048;
   while (p > 512 && units * ((max_context_len + p - 1) / p) < 1024) p /= 2;
   return p < cache->block_size ? cache->block_size : p;

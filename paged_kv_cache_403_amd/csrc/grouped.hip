@@ -53,6 +53,7 @@ namespace {
 constexpr int kPlanThreads = 1024;
 constexpr int kPlanWaves = kPlanThreads / 64;
 constexpr int kTile = 32;  // keys per matrix tile
+constexpr int kSufBuckets = 32;  // size classes of the suffix work list
 constexpr int kFoldTail = 64;  // private tails up to this many keys ride along with the shared prefix
 
 // Inclusive scan of x over the workgroup (kPlanThreads threads) under the
@@ -98,7 +99,7 @@ __global__ __launch_bounds__(kPlanThreads) void grouped_plan_kernel(PlanParams P
   __shared__ int share[kGroupedMaxSeqs];   // shared tokens (block multiple); a reference holds its chunk's max
   __shared__ int len[kGroupedMaxSeqs];     // clamped context lengths
   __shared__ int wtot_i[kPlanWaves];
-  __shared__ long long wtot_l[kPlanWaves];
+  __shared__ int bucket_count[kSufBuckets];
   const int S = P.num_seqs, tid = threadIdx.x, BS = P.block_size;
 
   // 1. run starts: sequence 0 and every in-range group start
@@ -180,10 +181,14 @@ __global__ __launch_bounds__(kPlanThreads) void grouped_plan_kernel(PlanParams P
   // 5. work lists.  Prefix items (first member, members, partition,
   //    reference) for each chunk with a shared prefix, emitted by the
   //    chunk's first sequence; suffix items (sequence, partition) over each
-  //    sequence's own tokens.  Both counts are scanned at once as the two
-  //    halves of a 64-bit value.
-  long long carry2 = 0;
+  //    sequence's own tokens are counted per size class here and placed in
+  //    step 6.
+  int carry2 = 0;
   const int PT = P.part_tokens;
+  // size class of a suffix item of t tokens
+  auto suf_bucket = [&](int t) { return static_cast<int>((static_cast<int64_t>(t - 1) * kSufBuckets) / PT); };
+  for (int k = tid; k < kSufBuckets; k += kPlanThreads) bucket_count[k] = 0;
+  __syncthreads();
   for (int base = 0; base < S; base += kPlanThreads) {
     const int s = base + tid;
     int own_pre = 0, np = 0, sh = 0, sb = 0, ref = 0;
@@ -195,12 +200,8 @@ __global__ __launch_bounds__(kPlanThreads) void grouped_plan_kernel(PlanParams P
       const int tail = len[s] - sh;
       np = tail <= 0 || (sb > 0 && tail <= kFoldTail) ? 0 : (tail + PT - 1) / PT;
     }
-    const long long packed = static_cast<long long>(own_pre) | (static_cast<long long>(np) << 32);
-    long long total = 0;
-    const long long incl = block_scan(packed, 0LL, [](long long a, long long b) { return a + b; }, wtot_l, total);
-    const long long excl = carry2 + incl - packed;
-    const int pfirst = static_cast<int>(excl & 0xffffffffLL);
-    const int sfirst = static_cast<int>(excl >> 32);
+    int total = 0;
+    const int pfirst = carry2 + block_scan(own_pre, 0, [](int a, int b) { return a + b; }, wtot_i, total) - own_pre;
     if (s < S) {
       P.seq_start[s] = sh;
       P.slot_base[s] = sb;
@@ -216,16 +217,44 @@ __global__ __launch_bounds__(kPlanThreads) void grouped_plan_kernel(PlanParams P
           it[3] = ref;
         }
       }
-      for (int p = 0; p < np; ++p) {
-        P.suf_items[2 * (sfirst + p)] = s;
-        P.suf_items[2 * (sfirst + p) + 1] = p;
-      }
+      if (np > 1) atomicAdd(&bucket_count[kSufBuckets - 1], np - 1);
+      if (np > 0) atomicAdd(&bucket_count[suf_bucket(len[s] - sh - (np - 1) * PT)], 1);
     }
     carry2 += total;
   }
+  __syncthreads();
+
+  // 6. suffix items in falling size (a counting sort over size classes):
+  //    the persistent kernel deals positions out round robin, so the short
+  //    items come last and fill in behind the long ones
   if (tid == 0) {
-    *P.pre_count = static_cast<int>(carry2 & 0xffffffffLL);
-    *P.suf_count = static_cast<int>(carry2 >> 32);
+    int acc = 0;
+    for (int k = kSufBuckets - 1; k >= 0; --k) {
+      const int c = bucket_count[k];
+      bucket_count[k] = acc;
+      acc += c;
+    }
+    *P.pre_count = carry2;
+    *P.suf_count = acc;
+  }
+  __syncthreads();
+  for (int s = tid; s < S; s += kPlanThreads) {
+    const int sh = share[s];
+    const int sb = (share[ref_of[s]] + PT - 1) / PT;
+    const int tail = len[s] - sh;
+    const int np = tail <= 0 || (sb > 0 && tail <= kFoldTail) ? 0 : (tail + PT - 1) / PT;
+    if (np > 1) {
+      const int first = atomicAdd(&bucket_count[kSufBuckets - 1], np - 1);
+      for (int p = 0; p < np - 1; ++p) {
+        P.suf_items[2 * (first + p)] = s;
+        P.suf_items[2 * (first + p) + 1] = p;
+      }
+    }
+    if (np > 0) {
+      const int at = atomicAdd(&bucket_count[suf_bucket(tail - (np - 1) * PT)], 1);
+      P.suf_items[2 * at] = s;
+      P.suf_items[2 * at + 1] = np - 1;
+    }
   }
 }
 

@@ -169,7 +169,7 @@ def _grouped(cache, num_seqs=4, num_q_heads=32, max_blocks=8, max_ctx=100, scale
     (dict(q=0), P.PA_EINVAL),
     (dict(ws=0), P.PA_EWORKSPACE),
     (dict(ws_bytes=64), P.PA_EWORKSPACE),
-    (dict(num_q_heads=64, max_blocks=20000, max_ctx=300000), P.PA_EUNSUPPORTED),  # merge weights over 64 KiB
+    (dict(num_q_heads=64, max_blocks=80000, max_ctx=1200000), P.PA_EUNSUPPORTED),  # merge weights over 64 KiB
 ])
 def test_grouped_decode_validation(kw, code):
     assert _grouped(_cache(), **kw) == code
@@ -186,12 +186,12 @@ def test_grouped_workspace_size_formula():
     # three per-sequence arrays and two list lengths, each 16-byte aligned
     def a16(x):
         return (x + 15) // 16 * 16
-    S, hq, d, C, part = 256, 32, 128, 8192, 256
+    S, hq, d, C, part = 256, 32, 128, 8192, 1024
     parts = C // part
     want = (a16(S * hq * 2 * parts * 2 * 4) + a16(S * hq * 2 * parts * d * 4) + a16(S * parts * 2 * 4)
             + a16(S * parts * 4 * 4) + 3 * a16(S * 4) + a16(8))
     assert P.pa_decode_grouped_workspace_bytes(S, hq, d, C, part) == want
-    assert P.pa_decode_grouped_workspace_bytes(S, hq, d, C, 0) == want  # 0 = 256 tokens
+    assert P.pa_decode_grouped_workspace_bytes(S, hq, d, C, 0) == want  # 0 = 1024 tokens
     assert P.pa_decode_grouped_workspace_bytes(0, hq, d, C, 0) == 0
 
 
