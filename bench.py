@@ -146,11 +146,35 @@ class Step:
                                 self.maxq_pre, self.maxc_pre, sp.scale)
 
 
-def time_steps(st, steps, warmup):
-    """Time `steps` whole steps, plus each kernel group with events on the
-    stream the library launches on (torch's current stream)."""
+SETTLE_S = 0.1  # untimed repetitions before any warm-up and timing
+
+
+def settle(fn, seconds=SETTLE_S):
+    """Repeat fn for `seconds` of wall time: the clocks take tens of ms of
+    sustained matrix work to reach their steady state."""
     import torch
 
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(8):
+            fn()
+        torch.cuda.synchronize()
+
+
+def time_steps(st, steps, warmup):
+    """Time `steps` whole steps, plus each kernel group with events on the
+    stream the library launches on (torch's current stream), after
+    SETTLE_S seconds of the same step and `warmup` more steps."""
+    import torch
+
+    def one():
+        st.copy_append()
+        if len(st.pre):
+            st.prefill()
+        if len(st.dec):
+            st.decode()
+
+    settle(one)
     for _ in range(warmup):
         st.copy_append()
         if len(st.pre):
@@ -268,6 +292,7 @@ def time_decode(st, iters, warmup):
     """Average decode launch time (HIP events on the library's stream), us."""
     import torch
 
+    settle(st.decode)
     for _ in range(warmup):
         st.decode()
     torch.cuda.synchronize()
@@ -306,6 +331,33 @@ def measure_block_sizes(name, iters, warmup, sizes=(8, 16, 32, 64)):
     static = 1.0 - float(lens.sum()) / float(len(lens) * lens.max())
     return {"workload": name, "sizes": rows, "static_reservation_waste": round(static, 4),
             "static_reservation_tokens": int(lens.max())}
+
+
+def measure_long(name, iters, warmup):
+    """Split-K decode of a few very long sequences: the library's partition
+    choice and 512-token partitions, HIP-event launch times (planner, walk
+    and merge together) and the rate of the decode's algorithmic bytes."""
+    import torch
+
+    import workloads
+
+    wl = workloads.make(name)
+    st = Step(wl, -1)
+    st.copy_append()
+    rows = []
+    for part in (-1, 512):
+        st.partition_size = part
+        if part != -1:
+            st.part_used = part
+        wsb = st.P.pa_decode_workspace_bytes(len(st.dec), wl.spec.num_q_heads, wl.spec.head_dim, st.max_dec,
+                                             part)
+        st.ws = torch.empty(max(wsb, 4), dtype=torch.uint8, device="cuda") if wsb else None
+        us = time_decode(st, iters, warmup)
+        rows.append({"partition_tokens": st.part_used, "decode_us": round(us, 2),
+                     "achieved_gbs": round(st.dec_bytes / (us * 1e-6) / 1e9, 1),
+                     "frac": round(st.dec_bytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)})
+        log(f"{name}: {st.part_used}-token partitions, decode {us:.1f} us = {rows[-1]['achieved_gbs']:.0f} GB/s")
+    return {"workload": name, "bytes_per_launch": st.dec_bytes, "runs": rows}
 
 
 def measure_fp8(name, ref_us, iters, warmup):
@@ -352,6 +404,7 @@ def measure_grouped(name, iters, warmup):
                             ws)
 
     def timed(fn):
+        settle(fn)
         for _ in range(warmup):
             fn()
         torch.cuda.synchronize()
@@ -394,6 +447,7 @@ def main():
     ap.add_argument("--no-grouped", action="store_true", help="skip the plain vs grouped decode measurement")
     ap.add_argument("--no-fp8", action="store_true", help="skip the FP8 KV-pool decode measurement")
     ap.add_argument("--no-block-sizes", action="store_true", help="skip the block-size sweep")
+    ap.add_argument("--no-long", action="store_true", help="skip the long-context split-K measurement")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB a few times (the known-size reference for "
                          "the HBM byte counters) and exit")
@@ -435,6 +489,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle_s": SETTLE_S,
         "ms_per_step": round(ms, 5),
         "higher_is_better": True,
         "scaling": "weak",
@@ -476,6 +531,8 @@ def main():
         result["fp8_kv"] = measure_fp8(args.workload, dc_ms * 1e3, max(10, args.steps // 2), 3)
     if not args.no_block_sizes:
         result["block_sizes"] = measure_block_sizes(args.workload, max(10, args.steps // 2), 3)
+    if not args.no_long:
+        result["long_split"] = measure_long("long_splitk_decode", max(10, args.steps // 2), 3)
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a sample")
         result["cpu_baseline"] = cpu_baseline(wl)
