@@ -360,7 +360,24 @@ def measure_long(name, iters, warmup):
     return {"workload": name, "bytes_per_launch": st.dec_bytes, "runs": rows}
 
 
-def measure_fp8(name, ref_us, iters, warmup):
+def time_prefill(st, iters, warmup):
+    """Average prefill launch time (HIP events on the library's stream), us."""
+    import torch
+
+    settle(st.prefill)
+    for _ in range(warmup):
+        st.prefill()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(iters):
+        st.prefill()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / iters * 1e3
+
+
+def measure_fp8(name, ref_us, iters, warmup, prefill_name=None):
     """Decode of the same batch with an FP8 (E4M3) pool and 16-bit
     activations: time, algorithmic bytes (1-byte K/V), rate, and the speedup
     over the 16-bit pool's decode time ref_us."""
@@ -372,10 +389,21 @@ def measure_fp8(name, ref_us, iters, warmup):
     us = time_decode(st, iters, warmup)
     gbs = st.dec_bytes / (us * 1e-6) / 1e9
     log(f"{wl.spec.name}: decode {us:.1f} us, {gbs:.0f} GB/s, x{ref_us / us:.2f} over the 16-bit pool")
-    return {"workload": wl.spec.name, "kv_dtype": "fp8 e4m3", "act_dtype": wl.spec.dtype,
-            "k_scale": wl.spec.k_scale, "v_scale": wl.spec.v_scale, "decode_us": round(us, 2),
-            "bytes_per_launch": st.dec_bytes, "achieved_gbs": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4),
-            "speedup_vs_16bit_pool": round(ref_us / us, 3), "decode_partition_tokens": st.part_used}
+    res = {"workload": wl.spec.name, "kv_dtype": "fp8 e4m3", "act_dtype": wl.spec.dtype,
+           "k_scale": wl.spec.k_scale, "v_scale": wl.spec.v_scale, "decode_us": round(us, 2),
+           "bytes_per_launch": st.dec_bytes, "achieved_gbs": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4),
+           "speedup_vs_16bit_pool": round(ref_us / us, 3), "decode_partition_tokens": st.part_used}
+    if prefill_name:
+        # chunked prefill over an FP8 pool (the codes widened while staging)
+        wlp = workloads.with_fp8_kv(workloads.make(prefill_name))
+        stp = Step(wlp, -1)
+        stp.copy_append()
+        pus = time_prefill(stp, max(5, iters // 2), warmup)
+        tf = stp.pre_flops / (pus * 1e-6) / 1e12
+        log(f"{wlp.spec.name}: prefill {pus:.1f} us = {tf:.1f} TFLOP/s")
+        res["prefill"] = {"workload": wlp.spec.name, "prefill_us": round(pus, 2), "tflops": round(tf, 2),
+                          "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4)}
+    return res
 
 
 def measure_grouped(name, iters, warmup):
@@ -528,7 +556,8 @@ def main():
     if not args.no_grouped:
         result["shared_prefix"] = measure_grouped("gqa_shared_prefix", max(10, args.steps // 2), 3)
     if not args.no_fp8 and sp.dtype in ("f16", "bf16"):
-        result["fp8_kv"] = measure_fp8(args.workload, dc_ms * 1e3, max(10, args.steps // 2), 3)
+        result["fp8_kv"] = measure_fp8(args.workload, dc_ms * 1e3, max(10, args.steps // 2), 3,
+                                       None if args.no_prefill else "mixed_chunked_prefill")
     if not args.no_block_sizes:
         result["block_sizes"] = measure_block_sizes(args.workload, max(10, args.steps // 2), 3)
     if not args.no_long:

@@ -38,7 +38,8 @@
  *    or bf16 (its contractions run on the matrix cores); pa_decode_grouped
  *    needs f16 or bf16 and block_size 16 or 32.  An FP8 pool (see pa_cache)
  *    has head_dim 128, block_size 16..64 and f16 or bf16 activations, and is
- *    supported by pa_kv_append, pa_copy_blocks and pa_decode.
+ *    supported by pa_kv_append, pa_copy_blocks, pa_decode and
+ *    pa_prefill_chunk.
  */
 #ifndef PAGEDATTN_H
 #define PAGEDATTN_H
@@ -207,7 +208,10 @@ int pa_decode_grouped(const pa_cache* cache, const void* q, void* out, int32_t n
  *   max_q_len, max_context_len  host bounds of n_s and context_lens
  * A workgroup stages its sequence's block-table entries in LDS, so contexts
  * whose table does not fit (about 360k tokens at block_size 16, head_dim
- * 128) return PA_EUNSUPPORTED. */
+ * 128) return PA_EUNSUPPORTED.  With an FP8 pool the codes are widened
+ * exactly to the activation type as the K/V tiles are staged, and the
+ * scales enter in fp32 (k_scale folded into the softmax scale, v_scale into
+ * the normalisation); the output is rounded to the activation type. */
 int pa_prefill_chunk(const pa_cache* cache, const void* q, void* out, const int32_t* cu_q_lens,
                      const int32_t* context_lens, int32_t num_seqs, int32_t total_q, int32_t num_q_heads,
                      const int32_t* block_tables, int32_t max_blocks_per_seq, int32_t max_q_len,

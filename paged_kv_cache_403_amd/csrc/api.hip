@@ -247,7 +247,7 @@ int pa_prefill_chunk(const pa_cache* cache, const void* q, void* out, const int3
                      int32_t max_context_len, float scale, void* stream) {
   int rc = check_cache(cache);
   if (rc != PA_OK) return rc;
-  if (cache->dtype == PA_F32 || is_fp8(cache)) return PA_EUNSUPPORTED;
+  if (cache->dtype == PA_F32) return PA_EUNSUPPORTED;
   int32_t group = 0;
   if ((rc = check_group(cache, num_q_heads, &group)) != PA_OK) return rc;
   if ((rc = check_scale(scale)) != PA_OK) return rc;
@@ -271,7 +271,12 @@ int pa_prefill_chunk(const pa_cache* cache, const void* q, void* out, const int3
   a.context_lens = context_lens;
   a.cu_q_lens = cu_q_lens;
   a.scale = scale;
-  a.dtype = cache->dtype;
+  a.dtype = act_dtype(cache);  // the matrix type; FP8 codes are widened to it exactly
+  if (is_fp8(cache)) {
+    a.kv_fp8 = 1;
+    a.k_scale = cache->k_scale;
+    a.v_scale = cache->v_scale;
+  }
   a.head_dim = cache->head_dim;
   a.block_size = cache->block_size;
   a.group = group;

@@ -142,6 +142,27 @@ __device__ __forceinline__ float dot_fp8<BF16>(const u32x4* qv, const u32x4& kv,
   return acc;
 }
 
+// Two E4M3 codes of a dword (bytes 0-1, or 2-3 when HI) widened exactly to
+// a packed pair of the 16-bit type.
+template <typename ST, bool HI>
+__device__ __forceinline__ uint32_t widen_fp8_pair(uint32_t w);
+template <>
+__device__ __forceinline__ uint32_t widen_fp8_pair<F16, false>(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.f, false));
+}
+template <>
+__device__ __forceinline__ uint32_t widen_fp8_pair<F16, true>(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.f, true));
+}
+template <>
+__device__ __forceinline__ uint32_t widen_fp8_pair<BF16, false>(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.f, false));
+}
+template <>
+__device__ __forceinline__ uint32_t widen_fp8_pair<BF16, true>(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.f, true));
+}
+
 // fp32 -> E4M3 code: nearest value, ties to the even code, magnitudes past
 // 448 saturate to +-448, NaN -> S.1111.111, the sign of zero kept.  Built
 // from the format's fields (RNE of the fp32 significand to 3 bits for

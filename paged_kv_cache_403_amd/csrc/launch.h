@@ -58,6 +58,10 @@ struct PrefillArgs {
   int32_t dtype, head_dim, block_size, group;
   int32_t num_seqs, total_q, num_kv_heads, num_blocks, max_blocks_per_seq;
   int32_t max_q_len, max_context_len;
+  // FP8 pool: dtype above is the activation type; the pool holds E4M3 codes
+  // that mean code * k_scale (K) and code * v_scale (V)
+  int32_t kv_fp8 = 0;
+  float k_scale = 1.f, v_scale = 1.f;
 };
 
 hipError_t launch_kv_append(const void* k_new, const void* v_new, const int64_t* slots, int32_t num_tokens,

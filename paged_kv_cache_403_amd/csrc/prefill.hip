@@ -50,31 +50,36 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLazy = 8.f;  // log2 units the running max may lag the true max
 constexpr int kSortMax = 4096;  // items per XCD ordered longest first (more keep index order)
 
-template <typename ST, int D, int BS, int G>
+// ST: the matrix (activation) type; PT: the pool's element type (ST, or FP8
+// codes widened to ST while staging)
+template <typename ST, typename PT, int D, int BS, int G>
 struct PrefillShape {
   static constexpr int KPAD = D + 8;       // K tile row stride (elements)
   static constexpr int VPAD = kKeys + 8;   // V^T tile row stride (elements)
   static constexpr int K_ELEMS = kKeys * KPAD;
   static constexpr int V_ELEMS = D * VPAD;
   static constexpr int STAGE = K_ELEMS + V_ELEMS;
-  static constexpr int CHUNKS = kKeys * D / 8;       // 16-byte chunks per K (and per V) tile
+  static constexpr int CPE = 16 / PT::bytes;          // pool elements per 16-byte chunk
+  static constexpr int CHUNKS = kKeys * D / CPE;     // 16-byte pool chunks per K (and per V) tile
   static constexpr int PER_THREAD = CHUNKS / kThreads;
   static constexpr int BLOCKS = kKeys / BS;          // cache blocks per tile
-  static constexpr int CPB = BS * D / 8;             // chunks per block tile
+  static constexpr int CPB = BS * D / CPE;           // chunks per block tile
   static constexpr int TOK = kRows / G;              // tokens per workgroup tile
   static constexpr int KSTEPS = D / 16;
   static constexpr int DSUB = D / 32;
   static_assert(PER_THREAD >= 1 && PER_THREAD * kThreads == CHUNKS, "tile chunks");
   static_assert(BLOCKS * BS == kKeys, "blocks per tile");
+  static_assert(BS % CPE == 0 || CPE == 8, "a V chunk stays inside one block's dim row");
 };
 
-template <typename ST, int D, int BS, int G>
+template <typename ST, typename PT, int D, int BS, int G>
 __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(
-    const typename ST::elem* __restrict__ q, const typename ST::elem* __restrict__ kc,
-    const typename ST::elem* __restrict__ vc, const int32_t* __restrict__ tables, int max_blocks,
+    const typename ST::elem* __restrict__ q, const typename PT::elem* __restrict__ kc,
+    const typename PT::elem* __restrict__ vc, const int32_t* __restrict__ tables, int max_blocks,
     const int32_t* __restrict__ ctx_lens, const int32_t* __restrict__ cu_q, int num_blocks, int num_kv_heads,
-    int num_units, int row_tiles, int max_context, float scale_log2, typename ST::elem* __restrict__ out) {
-  using S = PrefillShape<ST, D, BS, G>;
+    int num_units, int row_tiles, int max_context, float scale_log2, float v_scale,
+    typename ST::elem* __restrict__ out) {
+  using S = PrefillShape<ST, PT, D, BS, G>;
   using elem = typename ST::elem;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
   elem* smem = reinterpret_cast<elem*>(smem_raw);
@@ -183,7 +188,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(
       const int b = c / S::CPB;  // block within the tile
       const int cc = c % S::CPB;
       const int blk = tbl[t * S::BLOCKS + b];
-      const int64_t base = static_cast<int64_t>(blk) * blk_stride + head_k + static_cast<int64_t>(cc) * 8;
+      const int64_t base = static_cast<int64_t>(blk) * blk_stride + head_k + static_cast<int64_t>(cc) * S::CPE;
       kst[i] = load16(kc + base);
       vst[i] = load16(vc + base);
     }
@@ -198,27 +203,49 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(
       const int c = tid + i * kThreads;
       const int b = c / S::CPB;
       const int cc = c % S::CPB;
-      // K chunk: key row within block, 8 dims
-      const int krow = cc / (D / 8);
-      const int kdc = cc % (D / 8);
-      u32x4 kv = kst[i];
-      // V^T chunk: one dim, 8 consecutive keys of the block
-      const int vdim = cc / (BS / 8);
-      const int vkc = cc % (BS / 8);
-      u32x4 vv = vst[i];
+      // K chunk: key row within block, CPE dims; V^T chunk: one dim, CPE
+      // consecutive keys of the block
+      const int krow = cc / (D / S::CPE);
+      const int kdc = cc % (D / S::CPE);
+      const int vdim = cc / (BS / S::CPE);
+      const int vkc = cc % (BS / S::CPE);
+      constexpr int W = S::CPE / 8;  // 16-byte LDS rows per chunk once widened
+      u32x4 kv[W], vv[W];
+      if constexpr (W == 1) {
+        kv[0] = kst[i];
+        vv[0] = vst[i];
+      } else {
+        // sixteen E4M3 codes -> sixteen 16-bit values, exactly
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            kv[h][2 * e] = widen_fp8_pair<ST, false>(kst[i][2 * h + e]);
+            kv[h][2 * e + 1] = widen_fp8_pair<ST, true>(kst[i][2 * h + e]);
+            vv[h][2 * e] = widen_fp8_pair<ST, false>(vst[i][2 * h + e]);
+            vv[h][2 * e + 1] = widen_fp8_pair<ST, true>(vst[i][2 * h + e]);
+          }
+      }
       if (tail) {
         const int key_k = t * kKeys + b * BS + krow;
-        if (key_k >= L) kv = u32x4{0, 0, 0, 0};
-        const int key_v = t * kKeys + b * BS + vkc * 8;
+        const int key_v = t * kKeys + b * BS + vkc * S::CPE;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const uint32_t lo = key_v + 2 * e < L ? 0x0000ffffu : 0u;
-          const uint32_t hi = key_v + 2 * e + 1 < L ? 0xffff0000u : 0u;
-          vv[e] &= (lo | hi);
+        for (int w = 0; w < W; ++w) {
+          if (key_k >= L) kv[w] = u32x4{0, 0, 0, 0};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int key = key_v + 8 * w + 2 * e;
+            const uint32_t lo = key < L ? 0x0000ffffu : 0u;
+            const uint32_t hi = key + 1 < L ? 0xffff0000u : 0u;
+            vv[w][e] &= (lo | hi);
+          }
         }
       }
-      store16(kl + (b * BS + krow) * S::KPAD + kdc * 8, kv);
-      store16(vl + vdim * S::VPAD + b * BS + vkc * 8, vv);
+#pragma unroll
+      for (int w = 0; w < W; ++w) {
+        store16(kl + (b * BS + krow) * S::KPAD + kdc * S::CPE + 8 * w, kv[w]);
+        store16(vl + vdim * S::VPAD + b * BS + vkc * S::CPE + 8 * w, vv[w]);
+      }
     }
   };
 
@@ -324,7 +351,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(
 
   const float l_tot = halves_sum(l_run);  // both halves of the row
   if (!row_ok) return;
-  const float inv = 1.f / l_tot;
+  const float inv = v_scale / l_tot;
   elem* op = out + (static_cast<int64_t>(q0 + tok) * num_q_heads + hq) * D;
   // lane value j of dim-subtile ds is dim 32 ds + 8 (j/4) + 4 half + j%4
 #pragma unroll
@@ -339,9 +366,9 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(
     }
 }
 
-template <typename ST, int D, int BS, int G>
+template <typename ST, typename PT, int D, int BS, int G>
 hipError_t launch_t(const PrefillArgs& a, hipStream_t st) {
-  using S = PrefillShape<ST, D, BS, G>;
+  using S = PrefillShape<ST, PT, D, BS, G>;
   using elem = typename ST::elem;
   const int row_tiles = (a.max_q_len + S::TOK - 1) / S::TOK;
   if (row_tiles == 0 || a.num_seqs == 0) return hipSuccess;
@@ -356,26 +383,27 @@ hipError_t launch_t(const PrefillArgs& a, hipStream_t st) {
   if (lds > kPrefillMaxLds) return hipErrorInvalidValue;
   static bool lds_attr_set = false;  // above 64 KiB of dynamic LDS must be allowed explicitly
   if (!lds_attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_kernel<ST, D, BS, G>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_kernel<ST, PT, D, BS, G>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(kPrefillMaxLds));
     if (e != hipSuccess) return e;
     lds_attr_set = true;
   }
-  hipLaunchKernelGGL((prefill_kernel<ST, D, BS, G>), dim3(static_cast<unsigned>(grid)), dim3(kThreads), lds, st,
-                     static_cast<const elem*>(a.q), static_cast<const elem*>(a.k_cache),
-                     static_cast<const elem*>(a.v_cache), a.block_tables, a.max_blocks_per_seq, a.context_lens,
+  using pelem = typename PT::elem;
+  hipLaunchKernelGGL((prefill_kernel<ST, PT, D, BS, G>), dim3(static_cast<unsigned>(grid)), dim3(kThreads), lds, st,
+                     static_cast<const elem*>(a.q), static_cast<const pelem*>(a.k_cache),
+                     static_cast<const pelem*>(a.v_cache), a.block_tables, a.max_blocks_per_seq, a.context_lens,
                      a.cu_q_lens, a.num_blocks, a.num_kv_heads, units, row_tiles, a.max_context_len,
-                     a.scale * kLog2e, static_cast<elem*>(a.out));
+                     a.scale * kLog2e * a.k_scale, a.v_scale, static_cast<elem*>(a.out));
   return hipGetLastError();
 }
 
-template <typename ST, int D, int BS>
+template <typename ST, typename PT, int D, int BS>
 hipError_t by_group(const PrefillArgs& a, hipStream_t st) {
   switch (a.group) {
-    case 1: return launch_t<ST, D, BS, 1>(a, st);
-    case 2: return launch_t<ST, D, BS, 2>(a, st);
-    case 4: return launch_t<ST, D, BS, 4>(a, st);
-    case 8: return launch_t<ST, D, BS, 8>(a, st);
+    case 1: return launch_t<ST, PT, D, BS, 1>(a, st);
+    case 2: return launch_t<ST, PT, D, BS, 2>(a, st);
+    case 4: return launch_t<ST, PT, D, BS, 4>(a, st);
+    case 8: return launch_t<ST, PT, D, BS, 8>(a, st);
   }
   return hipErrorInvalidValue;
 }
@@ -383,16 +411,29 @@ hipError_t by_group(const PrefillArgs& a, hipStream_t st) {
 template <typename ST, int D>
 hipError_t by_block(const PrefillArgs& a, hipStream_t st) {
   switch (a.block_size) {
-    case 8: return by_group<ST, D, 8>(a, st);
-    case 16: return by_group<ST, D, 16>(a, st);
-    case 32: return by_group<ST, D, 32>(a, st);
-    case 64: return by_group<ST, D, 64>(a, st);
+    case 8: return by_group<ST, ST, D, 8>(a, st);
+    case 16: return by_group<ST, ST, D, 16>(a, st);
+    case 32: return by_group<ST, ST, D, 32>(a, st);
+    case 64: return by_group<ST, ST, D, 64>(a, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+// FP8 pools: head_dim 128, blocks of 16 tokens or more
+template <typename ST>
+hipError_t by_block_fp8(const PrefillArgs& a, hipStream_t st) {
+  if (a.head_dim != 128) return hipErrorInvalidValue;
+  switch (a.block_size) {
+    case 16: return by_group<ST, FP8, 128, 16>(a, st);
+    case 32: return by_group<ST, FP8, 128, 32>(a, st);
+    case 64: return by_group<ST, FP8, 128, 64>(a, st);
   }
   return hipErrorInvalidValue;
 }
 
 template <typename ST>
 hipError_t by_dim(const PrefillArgs& a, hipStream_t st) {
+  if (a.kv_fp8) return by_block_fp8<ST>(a, st);
   switch (a.head_dim) {
     case 64: return by_block<ST, 64>(a, st);
     case 128: return by_block<ST, 128>(a, st);

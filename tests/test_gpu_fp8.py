@@ -95,3 +95,78 @@ def test_fp8_fullsize_sampled():
         worst = max(worst, err)
         assert err <= TOL[sp.dtype], (r, h, err)
     print(f"[gpu]   sampled max|err| = {worst:.3e}", flush=True)
+
+
+def test_fp8_mixed_prefill_reduced_parity():
+    """Chunked prefill (and the decode side) of the mixed step over an FP8
+    pool: every output row against the oracle's attention over the codes
+    times the scales."""
+    wl = workloads.with_fp8_kv(workloads.make("mixed_chunked_prefill", reduced=True))
+    print("[gpu] fp8 mixed_chunked_prefill reduced", flush=True)
+    st, ref = _oracle(wl)
+    res = run_step(wl, partition_size=-1)
+    _check_pool(res, st)
+    err = _err(res, ref, wl.spec.dtype)
+    print(f"[gpu]   max|err| = {err:.3e}", flush=True)
+    assert err <= TOL[wl.spec.dtype]
+
+
+FP8_PREFILL_SHAPES = [  # (Hq, Hkv, BS, activation dtype): q heads per KV head 1, 2, 4, 8; every block size
+    (8, 8, 16, "f16"), (16, 8, 32, "bf16"), (16, 4, 64, "bf16"), (16, 2, 16, "f16"), (32, 8, 64, "f16"),
+]
+
+
+@pytest.mark.parametrize("shape", FP8_PREFILL_SHAPES)
+def test_fp8_prefill_shapes_and_ragged_chunks(shape):
+    """Chunks of ragged lengths (one row, a partial tile, several 64-key
+    tiles with a tail) on cached contexts that start mid-block."""
+    hq, hkv, bs, dt = shape
+    lens = [1, 70, 200, 331]
+    n_new = [1, 37, 130, 64]
+    wl = workloads.with_fp8_kv(workloads.custom(hq, hkv, 128, bs, dt, lens, n_new=n_new, seed=hq * 7 + bs))
+    print(f"[gpu] fp8 prefill shape {shape}", flush=True)
+    st, ref = _oracle(wl)
+    res = run_step(wl, prefill_all=True)
+    _check_pool(res, st)
+    err = _err(res, ref, dt)
+    print(f"[gpu]   max|err| = {err:.3e}", flush=True)
+    assert err <= TOL[dt], shape
+
+
+def test_fp8_prefill_nan_codes_in_unused_slots_do_not_leak():
+    wl = workloads.with_fp8_kv(workloads.make("mixed_chunked_prefill", reduced=True))
+    a = run_step(wl, fill=float("nan"), keep_pool=False)
+    b = run_step(wl, keep_pool=False)
+    assert np.isfinite(to_f64(a.out, wl.spec.dtype)).all()
+    assert np.array_equal(a.out, b.out)
+
+
+def test_fp8_mixed_fullsize_sampled():
+    """The mixed chunked-prefill step at full size on an FP8 pool, in the
+    launch configuration bench.py times: the first and last row of every
+    chunk and sampled decode rows against attention over the quantised
+    logical K/V (fp64)."""
+    wl = workloads.with_fp8_kv(workloads.make("mixed_chunked_prefill"))
+    sp = wl.spec
+    print("[gpu] fp8 full size mixed_chunked_prefill", flush=True)
+    res = run_step(wl, partition_size=-1, keep_pool=False)
+    rng = np.random.default_rng(9)
+    starts = np.concatenate([[0], np.cumsum([p.n_new for p in wl.batch])])
+    picks = []
+    for r, p in enumerate(wl.batch):
+        if p.n_new > 1:
+            picks += [(r, 0), (r, p.n_new - 1)]
+    picks += [(int(r), 0) for r in rng.integers(8, len(wl.batch), size=6)]
+    worst = 0.0
+    for r, i in sorted(set(picks)):
+        p = wl.batch[r]
+        h = int(rng.integers(sp.num_q_heads))
+        g = h // (sp.num_q_heads // sp.num_kv_heads)
+        K, V = wl.logical_kv(p.seq_id)
+        kq, vq = kv_encode(K[:, g], sp.dtype, sp.k_scale), kv_encode(V[:, g], sp.dtype, sp.v_scale)
+        a = p.context_len - p.n_new + i
+        ref = A.attention_rows(wl.q[p.seq_id][i:i + 1, h], kq, vq, [a], sp.scale, sp.dtype, sp.kv)[0]
+        err = float(np.abs(to_f64(res.out[starts[r] + i, h], sp.dtype) - ref).max())
+        worst = max(worst, err)
+        assert err <= TOL[sp.dtype], (r, i, h, err)
+    print(f"[gpu]   sampled max|err| = {worst:.3e}", flush=True)
