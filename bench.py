@@ -406,7 +406,7 @@ def measure_fp8(name, ref_us, iters, warmup, prefill_name=None):
     return res
 
 
-def measure_grouped(name, iters, warmup):
+def measure_grouped(name, iters, warmup, fp8=False):
     """Plain split decode against prefix-grouped decode on one workload's
     decode batch: HIP-event times on the library's stream, and the K/V bytes
     each must read (logical: every sequence's context; unique: each
@@ -416,6 +416,8 @@ def measure_grouped(name, iters, warmup):
     import workloads
 
     wl = workloads.make(name)
+    if fp8:
+        wl = workloads.with_fp8_kv(wl)
     st = Step(wl, -1)
     sp = wl.spec
     P = st.P
@@ -452,10 +454,10 @@ def measure_grouped(name, iters, warmup):
     blocks = set()
     for row, L in zip(tabs, lens):
         blocks.update(int(b) for b in row[:(int(L) + sp.block_size - 1) // sp.block_size])
-    unique = len(blocks) * sp.num_kv_heads * sp.block_size * sp.head_dim * sp.elem_bytes * 2
-    log(f"{name}: plain decode {plain_us:.1f} us, grouped decode {grouped_us:.1f} us "
+    unique = len(blocks) * sp.num_kv_heads * sp.block_size * sp.head_dim * sp.kv_elem_bytes * 2
+    log(f"{sp.name}: plain decode {plain_us:.1f} us, grouped decode {grouped_us:.1f} us "
         f"(unique K/V {unique / 1e6:.1f} MB of {st.dec_kv_bytes / 1e6:.1f} MB logical)")
-    return {"workload": name, "plain_decode_us": round(plain_us, 2), "plain_partition_tokens": st.part_used,
+    return {"workload": sp.name, "plain_decode_us": round(plain_us, 2), "plain_partition_tokens": st.part_used,
             "grouped_decode_us": round(grouped_us, 2), "grouped_partition_tokens": part,
             "speedup": round(plain_us / grouped_us, 3), "logical_kv_bytes": st.dec_kv_bytes,
             "unique_kv_bytes": unique, "grouped_unique_gbs": round(unique / (grouped_us * 1e-6) / 1e9, 1),
@@ -555,6 +557,9 @@ def main():
         }
     if not args.no_grouped:
         result["shared_prefix"] = measure_grouped("gqa_shared_prefix", max(10, args.steps // 2), 3)
+        if not args.no_fp8:
+            result["shared_prefix"]["fp8_kv"] = measure_grouped("gqa_shared_prefix", max(10, args.steps // 2), 3,
+                                                                fp8=True)
     if not args.no_fp8 and sp.dtype in ("f16", "bf16"):
         result["fp8_kv"] = measure_fp8(args.workload, dc_ms * 1e3, max(10, args.steps // 2), 3,
                                        None if args.no_prefill else "mixed_chunked_prefill")

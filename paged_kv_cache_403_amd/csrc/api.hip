@@ -55,13 +55,13 @@ int hip_status(hipError_t e) {
   return PA_EHIP;
 }
 
-int32_t round_up(int32_t x, int32_t m) { return (x + m - 1) / m * m; }
-
-// Tokens per partition actually used for a requested partition_size.
+// Tokens per partition actually used for a requested partition_size (one
+// pass: the context rounded up to whole blocks, capped at INT32_MAX).
 int32_t effective_partition(int32_t requested, int32_t block_size, int32_t max_context_len, int32_t chosen) {
   const int32_t p = requested == -1 ? chosen : requested;
-  if (p == 0) return round_up(max_context_len > 0 ? max_context_len : 1, block_size);
-  return p;
+  if (p != 0) return p;
+  const int64_t c = max_context_len > 0 ? max_context_len : 1;
+  return static_cast<int32_t>(std::min<int64_t>((c + block_size - 1) / block_size * block_size, INT32_MAX));
 }
 
 // Split-K workspace: partial softmax states [S][Hq][P][2] and outputs
@@ -204,7 +204,9 @@ int pa_decode(const pa_cache* cache, const void* q, void* out, int32_t num_seqs,
   if (!q || !out || !block_tables || !context_lens) return PA_EINVAL;
   const int32_t chosen = pa_decode_choose_partition(cache, num_seqs, num_q_heads, max_context_len);
   const int32_t part_tokens = effective_partition(partition_size, cache->block_size, max_context_len, chosen);
-  const int32_t num_parts = max_context_len > 0 ? (max_context_len + part_tokens - 1) / part_tokens : 1;
+  const int32_t num_parts =
+      max_context_len > 0 ? static_cast<int32_t>((static_cast<int64_t>(max_context_len) + part_tokens - 1) / part_tokens)
+                          : 1;
   const size_t need = workspace_for(num_seqs, num_q_heads, cache->head_dim, num_parts);
   if (need > 0 && (!workspace || workspace_bytes < need)) return PA_EWORKSPACE;
 
@@ -307,7 +309,7 @@ int pa_decode_grouped(const pa_cache* cache, const void* q, void* out, int32_t n
                       int32_t partition_size, void* workspace, size_t workspace_bytes, void* stream) {
   int rc = check_cache(cache);
   if (rc != PA_OK) return rc;
-  if (cache->dtype == PA_F32 || is_fp8(cache)) return PA_EUNSUPPORTED;
+  if (cache->dtype == PA_F32) return PA_EUNSUPPORTED;
   if (cache->block_size != 16 && cache->block_size != 32) return PA_EUNSUPPORTED;
   int32_t group = 0;
   if ((rc = check_group(cache, num_q_heads, &group)) != PA_OK) return rc;
@@ -339,7 +341,12 @@ int pa_decode_grouped(const pa_cache* cache, const void* q, void* out, int32_t n
   a.ws_items = reinterpret_cast<int32_t*>(ws + L.suf_items);
   a.ws_count = reinterpret_cast<int32_t*>(ws + L.counts);
   a.scale = scale;
+  if (is_fp8(cache)) {
+    a.k_scale = cache->k_scale;
+    a.v_scale = cache->v_scale;
+  }
   a.dtype = cache->dtype;
+  a.act_dtype = act_dtype(cache);
   a.head_dim = cache->head_dim;
   a.block_size = cache->block_size;
   a.group = group;

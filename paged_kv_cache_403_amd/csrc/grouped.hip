@@ -282,10 +282,26 @@ union GroupedLds {
   PrefixLds<D> pre;
 };
 
+// Eight pool elements from p as one MFMA operand of the 16-bit type AT:
+// one 16-byte load, or 8 E4M3 codes widened exactly.
+template <typename ST, typename AT>
+__device__ __forceinline__ u32x4 load8_operand(const typename ST::elem* p) {
+  if constexpr (ST::bytes == 1) {
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+    const u32x2 w = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+    const uint32_t w0 = w[0], w1 = w[1];
+    return u32x4{widen_fp8_pair<AT, false>(w0), widen_fp8_pair<AT, true>(w0), widen_fp8_pair<AT, false>(w1),
+                 widen_fp8_pair<AT, true>(w1)};
+  } else {
+    return load16_nt(p);
+  }
+}
+
 // A shared-prefix item: the rows r = member * G + h of one chunk over one
 // partition of the shared prefix, keys read through the reference's table;
 // wave w takes key tiles w, w + 4, ...  Writes slot `part` of every member.
-template <typename ST, int D, int BS, int G>
+// ST: the pool's element type; AT: the activation (matrix) type.
+template <typename ST, int D, int BS, int G, typename AT>
 __device__ __forceinline__ void prefix_item(PrefixLds<D>& sh, const GroupedParams& GP, int item, int kvh, int& first,
                                             int& members) {
   static_assert(D % 32 == 0 && D >= 64, "head_dim");
@@ -294,8 +310,9 @@ __device__ __forceinline__ void prefix_item(PrefixLds<D>& sh, const GroupedParam
   constexpr int DT = D / 32;      // 32-wide column tiles of O^T
   constexpr int TB = kTile / BS;  // blocks per key tile
   using elem = typename ST::elem;
+  using qelem = typename AT::elem;
   const DecodeParams& P = GP.dec;
-  const elem* __restrict__ q = static_cast<const elem*>(P.q);
+  const qelem* __restrict__ q = static_cast<const qelem*>(P.q);
   const elem* __restrict__ kc = static_cast<const elem*>(P.kc);
   const elem* __restrict__ vc = static_cast<const elem*>(P.vc);
   const int hk = P.num_kv_heads, hq = hk * G;
@@ -319,7 +336,7 @@ __device__ __forceinline__ void prefix_item(PrefixLds<D>& sh, const GroupedParam
 
   // Q^T as the B operand: row r, dims 8 * (2k + hf) ..
   u32x4 qb[KS];
-  const elem* qrow = q + (static_cast<int64_t>(first + (row_ok ? mem : 0)) * hq + kvh * G + hh) * D + 8 * hf;
+  const qelem* qrow = q + (static_cast<int64_t>(first + (row_ok ? mem : 0)) * hq + kvh * G + hh) * D + 8 * hf;
 #pragma unroll
   for (int k = 0; k < KS; ++k) qb[k] = row_ok ? load16(qrow + 16 * k) : u32x4{0, 0, 0, 0};
 
@@ -334,21 +351,28 @@ __device__ __forceinline__ void prefix_item(PrefixLds<D>& sh, const GroupedParam
   for (int t = 0; t < DT; ++t) o[t] = f32x16{};
   float m_run = -INFINITY, l_run = 0.f;
 
-  // K rows in A-operand order (key_perm) and V^T rows for the PV steps
+  // K rows in A-operand order (key_perm) and V^T rows for the PV steps.
+  // Keys at or past tok1 (the last tile's end when the shared length is not
+  // a multiple of 32) are masked out of the scores, but their V rows still
+  // meet a zero probability in the PV products, and 0 * NaN is NaN: unused
+  // slots may hold NaN, so such 8-key groups (tok1 is a block multiple, so
+  // a group is wholly in or out) read the partition's first keys instead.
   const int kkey = key_perm(r);
   auto load_tile = [&](int t, u32x4* kr, u32x4* vr) __attribute__((always_inline)) {
     const int kb = __shfl(bid, t * TB + kkey / BS, 64);
     const elem* kp =
         kc + static_cast<int64_t>(kb) * blk_stride + (static_cast<int64_t>(kvh) * BS + kkey % BS) * D + 8 * hf;
 #pragma unroll
-    for (int k = 0; k < KS; ++k) kr[k] = load16_nt(kp + 16 * k);
+    for (int k = 0; k < KS; ++k) kr[k] = load8_operand<ST, AT>(kp + 16 * k);
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
-      const int key = 16 * k + 8 * hf;  // first of this lane's 8 keys in the step
-      const int vb = __shfl(bid, t * TB + key / BS, 64);
+      const int key0 = 16 * k + 8 * hf;  // first of this lane's 8 keys in the step
+      const bool in = tok0 + t * kTile + key0 < tok1;
+      const int key = in ? key0 : 0;
+      const int vb = __shfl(bid, in ? t * TB + key / BS : 0, 64);
       const elem* vp = vc + static_cast<int64_t>(vb) * blk_stride + (static_cast<int64_t>(kvh) * D + r) * BS + key % BS;
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) vr[dt * 2 + k] = load16_nt(vp + dt * 32 * BS);
+      for (int dt = 0; dt < DT; ++dt) vr[dt * 2 + k] = load8_operand<ST, AT>(vp + dt * 32 * BS);
     }
   };
 
@@ -359,7 +383,7 @@ __device__ __forceinline__ void prefix_item(PrefixLds<D>& sh, const GroupedParam
   auto compute = [&](int key0, int lim, const u32x4* kr, const u32x4* vr) __attribute__((always_inline)) {
     f32x16 s = f32x16{};
 #pragma unroll
-    for (int k = 0; k < KS; ++k) s = mfma32<ST>(kr[k], qb[k], s);
+    for (int k = 0; k < KS; ++k) s = mfma32<AT>(kr[k], qb[k], s);
 
     float x[16];
     float tmax = -INFINITY;
@@ -387,19 +411,19 @@ __device__ __forceinline__ void prefix_item(PrefixLds<D>& sh, const GroupedParam
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         const float a0 = x[8 * k + 2 * c], a1 = x[8 * k + 2 * c + 1];
-        const uint32_t h = pack2<ST>(a0, a1);
+        const uint32_t h = pack2<AT>(a0, a1);
         float h0, h1;
-        widen2<ST>(h, h0, h1);
+        widen2<AT>(h, h0, h1);
         hi[k][c] = h;
-        lo[k][c] = pack2<ST>(a0 - h0, a1 - h1);
+        lo[k][c] = pack2<AT>(a0 - h0, a1 - h1);
       }
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
       o[dt] *= alpha;
 #pragma unroll
       for (int k = 0; k < 2; ++k) {
-        o[dt] = mfma32<ST>(vr[dt * 2 + k], hi[k], o[dt]);
-        o[dt] = mfma32<ST>(vr[dt * 2 + k], lo[k], o[dt]);
+        o[dt] = mfma32<AT>(vr[dt * 2 + k], hi[k], o[dt]);
+        o[dt] = mfma32<AT>(vr[dt * 2 + k], lo[k], o[dt]);
       }
     }
   };
@@ -444,7 +468,7 @@ __device__ __forceinline__ void prefix_item(PrefixLds<D>& sh, const GroupedParam
         const elem* kp = kc + static_cast<int64_t>(kb) * blk_stride +
                          (static_cast<int64_t>(kvh) * BS + (key0 + kkey) % BS) * D + 8 * hf;
 #pragma unroll
-        for (int k = 0; k < KS; ++k) k0[k] = load16_nt(kp + 16 * k);
+        for (int k = 0; k < KS; ++k) k0[k] = load8_operand<ST, AT>(kp + 16 * k);
 #pragma unroll
         for (int k = 0; k < 2; ++k) {
           const int key = key0 + 16 * k + 8 * hf;
@@ -453,7 +477,20 @@ __device__ __forceinline__ void prefix_item(PrefixLds<D>& sh, const GroupedParam
           const elem* vp =
               vc + static_cast<int64_t>(vb) * blk_stride + (static_cast<int64_t>(kvh) * D + r) * BS + key % BS;
 #pragma unroll
-          for (int dt = 0; dt < DT; ++dt) v0[dt * 2 + k] = load16_nt(vp + dt * 32 * BS);
+          for (int dt = 0; dt < DT; ++dt) v0[dt * 2 + k] = load8_operand<ST, AT>(vp + dt * 32 * BS);
+        }
+        // keys at or past Lm: unused slots that may hold NaN, zeroed (their
+        // zero probabilities would not cancel a NaN)
+        if (key0 + kTile > Lm) {
+#pragma unroll
+          for (int k = 0; k < 2; ++k)
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+              const int key = key0 + 16 * k + 8 * hf + 2 * c;
+              const uint32_t keep = (key < Lm ? 0x0000ffffu : 0u) | (key + 1 < Lm ? 0xffff0000u : 0u);
+#pragma unroll
+              for (int dt = 0; dt < DT; ++dt) v0[dt * 2 + k][c] &= keep;
+            }
         }
         compute(key0, mem == m ? Lm : 0, k0, v0);
       }
@@ -487,7 +524,8 @@ __device__ __forceinline__ void prefix_item(PrefixLds<D>& sh, const GroupedParam
       sh.c[w][tid] = c;
       L += c * sh.l[w][tid];
     }
-    sh.inv[tid] = L > 0.f ? 1.f / L : 0.f;
+    // (an FP8 pool's V scale enters here, as in the decode items)
+    sh.inv[tid] = L > 0.f ? (ST::bytes == 1 ? P.v_scale : 1.f) / L : 0.f;
     const int mm = tid / G;
     if (mm < members) {
       const int64_t pidx = (static_cast<int64_t>(first + mm) * hq + kvh * G + tid % G) * P.max_parts + part;
@@ -511,7 +549,7 @@ __device__ __forceinline__ void prefix_item(PrefixLds<D>& sh, const GroupedParam
 // The persistent kernel: prefix items, then suffix items, each times the KV
 // heads.  A suffix item that is its sequence's only slot writes the output
 // directly; every other item leaves partials for the merge kernel.
-template <typename ST, int D, int BS, int G>
+template <typename ST, int D, int BS, int G, typename AT>
 __global__ __launch_bounds__(kThreads, 2) void grouped_decode_kernel(GroupedParams GP) {
   __shared__ GroupedLds<G, D, BS> sh;
   const DecodeParams& P = GP.dec;
@@ -523,7 +561,7 @@ __global__ __launch_bounds__(kThreads, 2) void grouped_decode_kernel(GroupedPara
     if (it < n_pre) {
       const int item = it / hk;
       int first, members;
-      prefix_item<ST, D, BS, G>(sh.pre, GP, item, it - item * hk, first, members);
+      prefix_item<ST, D, BS, G, AT>(sh.pre, GP, item, it - item * hk, first, members);
     } else {
       const int j = it - n_pre, item = j / hk;
       const int s = __builtin_amdgcn_readfirstlane(P.items[2 * item]);
@@ -531,7 +569,8 @@ __global__ __launch_bounds__(kThreads, 2) void grouped_decode_kernel(GroupedPara
       const int L = clamp_len(P.ctx_lens[s], P.max_context);
       const bool only = __builtin_amdgcn_readfirstlane(GP.nslots[s]) == 1 &&
                         __builtin_amdgcn_readfirstlane(GP.slot_base[s]) == 0;
-      decode_item<ST, D, BS, G>(sh.dec, P, s, j - item * hk, part, L, __builtin_amdgcn_readfirstlane(GP.seq_start[s]),
+      decode_item<ST, D, BS, G, AT>(sh.dec, P, s, j - item * hk, part, L,
+                                    __builtin_amdgcn_readfirstlane(GP.seq_start[s]),
                                 __builtin_amdgcn_readfirstlane(GP.slot_base[s]), !only);
     }
   }
@@ -543,7 +582,7 @@ __global__ __launch_bounds__(kThreads, 2) void grouped_decode_kernel(GroupedPara
 // independent.  Slots without keys (sum 0) carry no weight; a row with none
 // (context 0) is written as zeros.  Rows written directly by the decode
 // kernel are skipped.
-template <typename ST, int D, int G>
+template <typename AT, int D, int G>
 __global__ __launch_bounds__(kThreads) void grouped_merge_kernel(DecodeParams P, const int32_t* __restrict__ nslots,
                                                                 const int32_t* __restrict__ slot_base) {
   extern __shared__ float w_sh[];  // [G][max_parts]
@@ -572,7 +611,7 @@ __global__ __launch_bounds__(kThreads) void grouped_merge_kernel(DecodeParams P,
     w_sh[h * mp + p] = m == -INFINITY ? 0.f : ml[2 * (h * mp + p) + 1] * __builtin_amdgcn_exp2f(m - M_sh[h]);
   }
   __syncthreads();
-  typename ST::elem* out = static_cast<typename ST::elem*>(P.out);
+  typename AT::elem* out = static_cast<typename AT::elem*>(P.out);
   for (int e = tid; e < G * D; e += kThreads) {
     const int h = e / D, d = e - h * D;
     const float* o = P.ws_o + (qh0 + h) * mp * D + d;
@@ -582,12 +621,12 @@ __global__ __launch_bounds__(kThreads) void grouped_merge_kernel(DecodeParams P,
       num = __builtin_fmaf(w[p], o[static_cast<int64_t>(p) * D], num);
       den += w[p];
     }
-    out[(qh0 + h) * D + d] = narrow<ST>(den > 0.f ? num / den : 0.f);
+    out[(qh0 + h) * D + d] = narrow<AT>(den > 0.f ? num / den : 0.f);
   }
 }
 
 // Workgroups of the persistent kernel that fit on the device at once.
-template <typename ST, int D, int BS, int G>
+template <typename ST, int D, int BS, int G, typename AT>
 int grouped_grid() {
   constexpr int kMaxDev = 64;
   static std::atomic<int> cached[kMaxDev];  // 0 = not yet queried; racing writers store the same value
@@ -598,7 +637,7 @@ int grouped_grid() {
     int cus = 0, per_cu = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &per_cu, reinterpret_cast<const void*>(&grouped_decode_kernel<ST, D, BS, G>), kThreads, 0) !=
+            &per_cu, reinterpret_cast<const void*>(&grouped_decode_kernel<ST, D, BS, G, AT>), kThreads, 0) !=
             hipSuccess ||
         per_cu <= 0)
       per_cu = 1;
@@ -608,7 +647,7 @@ int grouped_grid() {
   return n;
 }
 
-template <typename ST, int D, int BS, int G>
+template <typename ST, int D, int BS, int G, typename AT>
 hipError_t launch_t(const GroupedArgs& g, hipStream_t st) {
   const DecodeArgs& a = g.d;
   PlanParams pp{};
@@ -644,7 +683,8 @@ hipError_t launch_t(const GroupedArgs& g, hipStream_t st) {
   P.dec.out = a.out;
   P.dec.ws_ml = a.ws_ml;
   P.dec.ws_o = a.ws_o;
-  P.dec.scale_log2 = a.scale * kLog2e;
+  P.dec.scale_log2 = a.scale * kLog2e * a.k_scale;
+  P.dec.v_scale = a.v_scale;
   P.dec.max_blocks = a.max_blocks_per_seq;
   P.dec.max_context = a.max_context_len;
   P.dec.num_blocks = a.num_blocks;
@@ -660,31 +700,32 @@ hipError_t launch_t(const GroupedArgs& g, hipStream_t st) {
   const int64_t parts =
       std::max<int64_t>(1, (static_cast<int64_t>(a.max_context_len) + a.part_tokens - 1) / a.part_tokens);
   const int64_t upper = (a.num_seqs / 2 + a.num_seqs) * parts * a.num_kv_heads;
-  const int grid = static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(upper, grouped_grid<ST, D, BS, G>())));
-  hipLaunchKernelGGL((grouped_decode_kernel<ST, D, BS, G>), dim3(grid), dim3(kThreads), 0, st, P);
+  const int grid =
+      static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(upper, grouped_grid<ST, D, BS, G, AT>())));
+  hipLaunchKernelGGL((grouped_decode_kernel<ST, D, BS, G, AT>), dim3(grid), dim3(kThreads), 0, st, P);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((grouped_merge_kernel<ST, D, G>), dim3(a.num_kv_heads, a.num_seqs), dim3(kThreads),
+  hipLaunchKernelGGL((grouped_merge_kernel<AT, D, G>), dim3(a.num_kv_heads, a.num_seqs), dim3(kThreads),
                      static_cast<size_t>(G) * a.num_parts * sizeof(float), st, P.dec, g.nslots, g.slot_base);
   return hipGetLastError();
 }
 
-template <typename ST, int D, int BS>
+template <typename ST, int D, int BS, typename AT>
 hipError_t by_group(const GroupedArgs& a, hipStream_t st) {
   switch (a.d.group) {
-    case 1: return launch_t<ST, D, BS, 1>(a, st);
-    case 2: return launch_t<ST, D, BS, 2>(a, st);
-    case 4: return launch_t<ST, D, BS, 4>(a, st);
-    case 8: return launch_t<ST, D, BS, 8>(a, st);
+    case 1: return launch_t<ST, D, BS, 1, AT>(a, st);
+    case 2: return launch_t<ST, D, BS, 2, AT>(a, st);
+    case 4: return launch_t<ST, D, BS, 4, AT>(a, st);
+    case 8: return launch_t<ST, D, BS, 8, AT>(a, st);
   }
   return hipErrorInvalidValue;
 }
 
-template <typename ST, int D>
+template <typename ST, int D, typename AT>
 hipError_t by_block(const GroupedArgs& a, hipStream_t st) {
   switch (a.d.block_size) {
-    case 16: return by_group<ST, D, 16>(a, st);
-    case 32: return by_group<ST, D, 32>(a, st);
+    case 16: return by_group<ST, D, 16, AT>(a, st);
+    case 32: return by_group<ST, D, 32, AT>(a, st);
   }
   return hipErrorInvalidValue;
 }
@@ -692,15 +733,29 @@ hipError_t by_block(const GroupedArgs& a, hipStream_t st) {
 template <typename ST>
 hipError_t by_dim(const GroupedArgs& a, hipStream_t st) {
   switch (a.d.head_dim) {
-    case 64: return by_block<ST, 64>(a, st);
-    case 128: return by_block<ST, 128>(a, st);
+    case 64: return by_block<ST, 64, ST>(a, st);
+    case 128: return by_block<ST, 128, ST>(a, st);
   }
   return hipErrorInvalidValue;
+}
+
+// FP8 pools (head_dim 128) with 16-bit activations
+template <typename AT>
+hipError_t by_act_fp8(const GroupedArgs& a, hipStream_t st) {
+  if (a.d.head_dim != 128) return hipErrorInvalidValue;
+  return by_block<FP8, 128, AT>(a, st);
 }
 
 }  // namespace
 
 hipError_t launch_decode_grouped(const GroupedArgs& a, hipStream_t st) {
+  if (a.d.dtype == 3) {
+    switch (a.d.act_dtype) {
+      case 1: return by_act_fp8<F16>(a, st);
+      case 2: return by_act_fp8<BF16>(a, st);
+    }
+    return hipErrorInvalidValue;
+  }
   switch (a.d.dtype) {
     case 1: return by_dim<F16>(a, st);
     case 2: return by_dim<BF16>(a, st);

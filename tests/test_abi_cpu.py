@@ -106,7 +106,7 @@ def test_fp8_descriptor_validation():
     assert _decode(fp8(block_size=8)) == P.PA_EUNSUPPORTED
     assert _prefill(fp8(), num_seqs=0) == P.PA_OK  # FP8 pools are accepted (no rows: nothing to launch)
     assert _prefill(fp8(head_dim=64)) == P.PA_EUNSUPPORTED
-    assert _grouped(fp8()) == P.PA_EUNSUPPORTED
+    assert _grouped(fp8(), num_seqs=0) == P.PA_OK  # FP8 pools are accepted (block_size 16 or 32)
     # block sizes 8 and 64 pass the descriptor checks (then fail on max_ctx here)
     assert _decode(_cache(block_size=8), max_ctx=100) == P.PA_EINVAL
     assert _decode(_cache(block_size=64), num_seqs=0) == P.PA_OK

@@ -22,7 +22,7 @@ pytestmark = pytest.mark.gpu
 def _oracle(wl):
     st = run_workload(wl, fill_bits=None)
     out, _ = A.paged_attention(wl.step_q(), st.pool.k, st.pool.v, st.tables, st.context_lens, st.q_lens,
-                               wl.spec.scale, wl.spec.dtype)
+                               wl.spec.scale, wl.spec.dtype, kv=wl.spec.kv)
     return st, out
 
 
@@ -116,6 +116,18 @@ def test_zero_lengths_and_hint_out_of_range():
     assert np.abs(a - b).max() <= 2 * TOL["bf16"]
 
 
+def test_nan_in_unused_slots_does_not_leak():
+    """Unused pool slots filled with NaN: the shared-prefix tiles past the
+    shared length and the folded private tails past the context must not
+    let them into the output (16-bit pool)."""
+    wl = workloads.make("gqa_shared_prefix", reduced=True)
+    hint = workloads.group_starts(wl)
+    a = run_step(wl, fill=float("nan"), keep_pool=False, grouped=True, group_start=hint)
+    b = run_step(wl, keep_pool=False, grouped=True, group_start=hint)
+    assert np.isfinite(to_f64(a.out, wl.spec.dtype)).all()
+    assert np.array_equal(a.out, b.out)
+
+
 def test_repeatable():
     wl = workloads.make("gqa_shared_prefix", reduced=True)
     hint = workloads.group_starts(wl)
@@ -126,14 +138,14 @@ def test_repeatable():
 
 def test_shared_prefix_fullsize_sampled():
     """Full-size shared-prefix workload through grouped decode in the launch
-    configuration bench.py times (natural hints, 512-token partitions):
+    configuration bench.py times (natural hints, 1024-token partitions):
     sampled rows -- every group's longest sequence and one more member of
     each group, a random q head each -- against attention of the row over
     its sequence's logical K/V (fp64)."""
     wl = workloads.make("gqa_shared_prefix")
     sp = wl.spec
     print("[gpu] grouped full size gqa_shared_prefix", flush=True)
-    res = run_step(wl, partition_size=512, keep_pool=False, grouped=True, group_start=workloads.group_starts(wl))
+    res = run_step(wl, partition_size=1024, keep_pool=False, grouped=True, group_start=workloads.group_starts(wl))
     batch = wl.batch
     lens = np.array([p.context_len for p in batch])
     starts = workloads.group_starts(wl)
@@ -154,3 +166,53 @@ def test_shared_prefix_fullsize_sampled():
         worst = max(worst, err)
         assert err <= TOL[sp.dtype], (r, h, err)
     print(f"[gpu]   sampled max|err| = {worst:.3e} over {len(set(picks))} rows", flush=True)
+
+
+# FP8 pools: grouped decode against the oracle's attention over the codes
+# times the scales (the prefix items widen the codes to the MFMA operands,
+# the suffix items are the FP8 decode items).
+@pytest.mark.parametrize("part", [0, 64])
+def test_fp8_shared_prefix_reduced(part):
+    wl = workloads.with_fp8_kv(workloads.make("gqa_shared_prefix", reduced=True))
+    print(f"[gpu] grouped fp8 shared-prefix reduced part={part}", flush=True)
+    st, ref = _oracle(wl)
+    for name in ("natural", "none", "random"):
+        hint = _hints(wl)[name]
+        res = run_step(wl, partition_size=part, keep_pool=False, grouped=True, group_start=hint)
+        err = _err(res, ref, wl.spec.dtype)
+        print(f"[gpu]   hint {name}: max|err| = {err:.3e}", flush=True)
+        assert err <= TOL[wl.spec.dtype], name
+
+
+FP8_GROUP_SHAPES = [  # (Hq, Hkv, BS, activation dtype): q heads per KV head 1, 2, 4, 8
+    (8, 8, 16, "f16"), (16, 8, 32, "bf16"), (32, 8, 16, "bf16"), (16, 2, 32, "f16"),
+]
+
+
+@pytest.mark.parametrize("shape", FP8_GROUP_SHAPES)
+def test_fp8_group_shapes_and_edges(shape):
+    hq, hkv, bs, dt = shape
+    g = hq // hkv
+    groups = [
+        (3 * bs + 5, [1, bs, 3 * bs + 5, 3 * bs + 6, 200]),
+        (4 * bs, [4 * bs, 4 * bs + 1, 9 * bs]),
+        (0, [7, 40]),
+        (300, [int(x) for x in np.linspace(280, 420, 32 // g + 3)]),
+    ]
+    wl = workloads.with_fp8_kv(workloads.custom_shared(hq, hkv, 128, bs, dt, groups, seed=hq + bs))
+    print(f"[gpu] grouped fp8 shape {shape}", flush=True)
+    st, ref = _oracle(wl)
+    for part in (0, max(32, bs)):
+        res = run_step(wl, partition_size=part, keep_pool=False, grouped=True,
+                       group_start=workloads.group_starts(wl))
+        err = _err(res, ref, dt)
+        assert err <= TOL[dt], (part, err)
+
+
+def test_fp8_grouped_nan_codes_in_unused_slots_do_not_leak():
+    wl = workloads.with_fp8_kv(workloads.make("gqa_shared_prefix", reduced=True))
+    hint = workloads.group_starts(wl)
+    a = run_step(wl, fill=float("nan"), keep_pool=False, grouped=True, group_start=hint)
+    b = run_step(wl, keep_pool=False, grouped=True, group_start=hint)
+    assert np.isfinite(to_f64(a.out, wl.spec.dtype)).all()
+    assert np.array_equal(a.out, b.out)
