@@ -36,10 +36,10 @@
  *    num_q_heads a multiple of num_kv_heads with group size
  *    num_q_heads/num_kv_heads in {1, 2, 4, 8}.  pa_prefill_chunk needs f16
  *    or bf16 (its contractions run on the matrix cores); pa_decode_grouped
- *    needs f16 or bf16 and block_size 16 or 32.  An FP8 pool (see pa_cache)
+ *    needs f16 or bf16 and block_size 16, 32 or 64.  An FP8 pool (see pa_cache)
  *    has head_dim 128, block_size 16..64 and f16 or bf16 activations, and is
  *    supported by pa_kv_append, pa_copy_blocks, pa_decode,
- *    pa_prefill_chunk and (block_size 16 or 32) pa_decode_grouped.
+ *    pa_prefill_chunk and pa_decode_grouped.
  */
 #ifndef PAGEDATTN_H
 #define PAGEDATTN_H

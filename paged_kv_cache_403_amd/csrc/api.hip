@@ -310,7 +310,7 @@ int pa_decode_grouped(const pa_cache* cache, const void* q, void* out, int32_t n
   int rc = check_cache(cache);
   if (rc != PA_OK) return rc;
   if (cache->dtype == PA_F32) return PA_EUNSUPPORTED;
-  if (cache->block_size != 16 && cache->block_size != 32) return PA_EUNSUPPORTED;
+  if (cache->block_size == 8) return PA_EUNSUPPORTED;
   int32_t group = 0;
   if ((rc = check_group(cache, num_q_heads, &group)) != PA_OK) return rc;
   if ((rc = check_scale(scale)) != PA_OK) return rc;

@@ -305,10 +305,9 @@ template <typename ST, int D, int BS, int G, typename AT>
 __device__ __forceinline__ void prefix_item(PrefixLds<D>& sh, const GroupedParams& GP, int item, int kvh, int& first,
                                             int& members) {
   static_assert(D % 32 == 0 && D >= 64, "head_dim");
-  static_assert(BS == 16 || BS == 32, "block size");
+  static_assert(BS == 16 || BS == 32 || BS == 64, "block size");
   constexpr int KS = D / 16;      // contraction steps of S^T = K Q^T
   constexpr int DT = D / 32;      // 32-wide column tiles of O^T
-  constexpr int TB = kTile / BS;  // blocks per key tile
   using elem = typename ST::elem;
   using qelem = typename AT::elem;
   const DecodeParams& P = GP.dec;
@@ -359,17 +358,19 @@ __device__ __forceinline__ void prefix_item(PrefixLds<D>& sh, const GroupedParam
   // a group is wholly in or out) read the partition's first keys instead.
   const int kkey = key_perm(r);
   auto load_tile = [&](int t, u32x4* kr, u32x4* vr) __attribute__((always_inline)) {
-    const int kb = __shfl(bid, t * TB + kkey / BS, 64);
+    // keys are counted from the partition's start (a block boundary)
+    const int kabs = t * kTile + kkey;
+    const int kb = __shfl(bid, kabs / BS, 64);
     const elem* kp =
-        kc + static_cast<int64_t>(kb) * blk_stride + (static_cast<int64_t>(kvh) * BS + kkey % BS) * D + 8 * hf;
+        kc + static_cast<int64_t>(kb) * blk_stride + (static_cast<int64_t>(kvh) * BS + kabs % BS) * D + 8 * hf;
 #pragma unroll
     for (int k = 0; k < KS; ++k) kr[k] = load8_operand<ST, AT>(kp + 16 * k);
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
       const int key0 = 16 * k + 8 * hf;  // first of this lane's 8 keys in the step
       const bool in = tok0 + t * kTile + key0 < tok1;
-      const int key = in ? key0 : 0;
-      const int vb = __shfl(bid, in ? t * TB + key / BS : 0, 64);
+      const int key = in ? t * kTile + key0 : 0;
+      const int vb = __shfl(bid, key / BS, 64);
       const elem* vp = vc + static_cast<int64_t>(vb) * blk_stride + (static_cast<int64_t>(kvh) * D + r) * BS + key % BS;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) vr[dt * 2 + k] = load8_operand<ST, AT>(vp + dt * 32 * BS);
@@ -726,6 +727,7 @@ hipError_t by_block(const GroupedArgs& a, hipStream_t st) {
   switch (a.d.block_size) {
     case 16: return by_group<ST, D, 16, AT>(a, st);
     case 32: return by_group<ST, D, 32, AT>(a, st);
+    case 64: return by_group<ST, D, 64, AT>(a, st);
   }
   return hipErrorInvalidValue;
 }

@@ -106,7 +106,8 @@ def test_fp8_descriptor_validation():
     assert _decode(fp8(block_size=8)) == P.PA_EUNSUPPORTED
     assert _prefill(fp8(), num_seqs=0) == P.PA_OK  # FP8 pools are accepted (no rows: nothing to launch)
     assert _prefill(fp8(head_dim=64)) == P.PA_EUNSUPPORTED
-    assert _grouped(fp8(), num_seqs=0) == P.PA_OK  # FP8 pools are accepted (block_size 16 or 32)
+    assert _grouped(fp8(), num_seqs=0) == P.PA_OK  # FP8 pools are accepted
+    assert _grouped(fp8(block_size=64), num_seqs=0) == P.PA_OK
     # block sizes 8 and 64 pass the descriptor checks (then fail on max_ctx here)
     assert _decode(_cache(block_size=8), max_ctx=100) == P.PA_EINVAL
     assert _decode(_cache(block_size=64), num_seqs=0) == P.PA_OK
@@ -178,6 +179,8 @@ def test_grouped_decode_validation(kw, code):
 
 def test_grouped_decode_rejects_fp32_and_accepts_empty_batch():
     assert _grouped(_cache(dtype=P.PA_F32)) == P.PA_EUNSUPPORTED
+    assert _grouped(_cache(block_size=8), max_blocks=16) == P.PA_EUNSUPPORTED  # one block id per lane: 64 * 8 < 1024
+    assert _grouped(_cache(block_size=64), num_seqs=0) == P.PA_OK
     assert _grouped(_cache(), num_seqs=0) == P.PA_OK
 
 
