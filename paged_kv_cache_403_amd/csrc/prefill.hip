@@ -266,17 +266,28 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(
     const elem* kl = smem + buf * S::STAGE;
     const elem* vl = kl + S::K_ELEMS;
 
-    if (t * kKeys <= wave_pos) {  // some row of this wavefront sees a key of this tile
-      // S^T for the two 32-key subtiles
-      f32x16 sacc[2] = {f32x16{}, f32x16{}};
+    const bool active = t * kKeys <= wave_pos;  // some row of this wavefront sees a key of this tile
+    f32x16 sacc[2] = {f32x16{}, f32x16{}};
+    float mx = -INFINITY;
+    if (active) {
+      // S^T for the two 32-key subtiles.  All sixteen K operands are read
+      // from LDS before the products (the group barriers below keep the
+      // scheduler from pairing each read with its product): with every read
+      // in flight the wave waits once for LDS, not once per product.
+      u32x4 ka[S::KSTEPS][2];
 #pragma unroll
-      for (int kk = 0; kk < S::KSTEPS; ++kk) {
+      for (int kk = 0; kk < S::KSTEPS; ++kk)
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          const u32x4 a = *reinterpret_cast<const u32x4*>(kl + (ks * 32 + arow) * S::KPAD + kk * 16 + half * 8);
-          sacc[ks] = mfma32<ST>(a, qb[kk], sacc[ks]);
-        }
-      }
+        for (int ks = 0; ks < 2; ++ks)
+          ka[kk][ks] = *reinterpret_cast<const u32x4*>(kl + (ks * 32 + arow) * S::KPAD + kk * 16 + half * 8);
+#pragma unroll
+      for (int kk = 0; kk < S::KSTEPS; ++kk)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) sacc[ks] = mfma32<ST>(ka[kk][ks], qb[kk], sacc[ks]);
+      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 12, 0);
       // lane value j of subtile ks is key t*64 + 32 ks + 16 (j/8) + 8 half + j%8
       const int kbase = t * kKeys + half * 8;
       if (t * kKeys + kKeys - 1 > diag0) {
@@ -288,12 +299,17 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(
             sacc[ks][jj] = key <= pos ? sacc[ks][jj] : -INFINITY;
           }
       }
-      float mx = -INFINITY;
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
         for (int jj = 0; jj < 16; ++jj) mx = fmaxf(mx, sacc[ks][jj]);
       mx = halves_max(mx) * scale_log2;
+    }
+    // The next tile goes from registers to LDS between the score and the
+    // softmax phases: its buffer was released by the previous iteration's
+    // barrier, and LDS is otherwise idle while the exponentials run.
+    if (t + 1 < ntiles) stage(t + 1, buf ^ 1);
+    if (active) {
       // the reference max moves only when the tile's max passes it by kLazy
       const bool move = mx > m_run + kLazy;
       const bool rescale = move && m_run > -INFINITY;  // accumulators hold earlier keys
@@ -345,7 +361,6 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(
         }
       }
     }
-    if (t + 1 < ntiles) stage(t + 1, buf ^ 1);
     __syncthreads();
   }
 
