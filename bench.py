@@ -161,10 +161,28 @@ def settle(fn, seconds=SETTLE_S):
         torch.cuda.synchronize()
 
 
+def time_loop(fn, iters):
+    """Average time of `iters` back-to-back calls of fn, from one pair of
+    HIP events around the loop on the stream the library launches on
+    (torch's current stream), in ms."""
+    import torch
+
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(iters):
+        fn()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / iters
+
+
 def time_steps(st, steps, warmup):
-    """Time `steps` whole steps, plus each kernel group with events on the
-    stream the library launches on (torch's current stream), after
-    SETTLE_S seconds of the same step and `warmup` more steps."""
+    """Time `steps` whole steps between one pair of events, after SETTLE_S
+    seconds of the same step and `warmup` more steps; then each kernel group
+    alone over as many back-to-back repetitions (its average launch time).
+    Events between the groups of every step would add their own cost (each
+    record is a marker packet with a cache write-back) to the step time, so
+    the step loop carries none."""
     import torch
 
     def one():
@@ -176,38 +194,15 @@ def time_steps(st, steps, warmup):
 
     settle(one)
     for _ in range(warmup):
-        st.copy_append()
-        if len(st.pre):
-            st.prefill()
-        if len(st.dec):
-            st.decode()
+        one()
     torch.cuda.synchronize()
-    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
-    marks = []
     t0 = time.perf_counter()
-    start = ev()
-    start.record()
-    for _ in range(steps):
-        e = [ev(), ev(), ev(), ev()]
-        e[0].record()
-        st.copy_append()
-        e[1].record()
-        if len(st.pre):
-            st.prefill()
-        e[2].record()
-        if len(st.dec):
-            st.decode()
-        e[3].record()
-        marks.append(e)
-    end = ev()
-    end.record()
-    torch.cuda.synchronize()
+    total_ms = time_loop(one, steps)
     wall = time.perf_counter() - t0
-    total_ms = start.elapsed_time(end)
-    ca = sum(m[0].elapsed_time(m[1]) for m in marks) / steps
-    pf = sum(m[1].elapsed_time(m[2]) for m in marks) / steps
-    dc = sum(m[2].elapsed_time(m[3]) for m in marks) / steps
-    return total_ms / steps, wall * 1e3 / steps, ca, pf, dc
+    ca = time_loop(st.copy_append, steps)
+    pf = time_loop(st.prefill, steps) if len(st.pre) else 0.0
+    dc = time_loop(st.decode, steps) if len(st.dec) else 0.0
+    return total_ms, wall * 1e3 / steps, ca, pf, dc
 
 
 def cpu_baseline(wl, budget_s=15.0, min_s=10.0):
