@@ -153,7 +153,12 @@ int pa_decode(const pa_cache* cache, const void* q, void* out, int32_t num_seqs,
               int32_t max_context_len, float scale, int32_t partition_size, void* workspace,
               size_t workspace_bytes, void* stream);
 
-/* The partition size pa_decode uses for partition_size == -1 (host only). */
+/* The partition size pa_decode uses for partition_size == -1 (host only):
+ * 0 (one pass) for short contexts, or for contexts up to 4096 tokens when
+ * the batch has at least 512 (sequence, KV head) units; otherwise a power of
+ * two from 512 up to 2048 tokens (up to 16384 when there are fewer than 512
+ * units, i.e. a few long contexts), the largest that still yields about
+ * 1024 (512) work items. */
 int32_t pa_decode_choose_partition(const pa_cache* cache, int32_t num_seqs, int32_t num_q_heads,
                                    int32_t max_context_len);
 

@@ -163,14 +163,21 @@ int32_t pa_decode_choose_partition(const pa_cache* cache, int32_t num_seqs, int3
   const int64_t units = static_cast<int64_t>(num_seqs) * cache->num_kv_heads;
   // One pass when the batch gives the chip about two workgroups per compute
   // unit or more and no context is long: the one-pass grid starts the
-  // longest sequences first, so uneven lengths balance out.  Otherwise split
-  // into the longest partitions (up to 2048 tokens) that still give about a
-  // thousand work items, since every partition has a fixed start-up cost;
-  // long contexts beside short ones are then cut into pieces the short ones
-  // can fill in around.
+  // longest sequences first, so uneven lengths balance out.  Otherwise split,
+  // into the longest partitions that still give enough work items, since
+  // every partition has a fixed start-up cost and a share of the merge:
+  //  * a batch of fewer (sequence, KV head) units than two per compute unit
+  //    is a few long contexts: partitions up to 16384 tokens, down to about
+  //    two items per compute unit (measured on 4 x 131072 tokens, 8 KV heads:
+  //    2048 / 4096 / 8192 / 16384-token partitions ran 346-360 / 335-341 /
+  //    327-334 / 343 us);
+  //  * otherwise long contexts sit beside short ones: partitions of up to
+  //    2048 tokens, down to about a thousand items, so the short sequences
+  //    fill in around the pieces of the long ones.
   if (max_context_len <= 512 || (units >= 512 && max_context_len <= 4096)) return 0;
-  int32_t p = 2048;
-  while (p > 512 && units * ((max_context_len + p - 1) / p) < 1024) p /= 2;
+  int32_t p = units < 512 ? 16384 : 2048;
+  const int64_t want = units < 512 ? 512 : 1024;
+  while (p > 512 && units * ((max_context_len + p - 1) / p) < want) p /= 2;
   return p < cache->block_size ? cache->block_size : p;
 }
 
