@@ -10,9 +10,9 @@
 //
 // Pool layout: K tiles are [block_size][head_dim] (token rows), V tiles are
 // [head_dim][block_size] (V kept transposed inside each block, so the PV
-// contraction reads keys contiguously).  Both are HBM streams: each thread
-// moves one 16-byte chunk of a source row; a wavefront reads 1 KiB of
-// consecutive source bytes per instruction.
+// contraction reads keys contiguously).  Both are HBM streams: source rows
+// are read in 16-byte chunks, a wavefront covering 1 KiB of consecutive
+// source bytes per instruction.
 #include "common.h"
 #include "launch.h"
 
@@ -20,36 +20,56 @@ namespace pa {
 
 namespace {
 
-// One thread per 16-byte chunk of a (token, head) row; grid-stride.  The K
-// chunk is stored whole; the V chunk's elements go to VEC rows of the
-// transposed V tile, block_size elements apart.
+// One workgroup per (run of kAppendTok consecutive tokens, KV head).  K
+// rows are token rows of the tile, so each 16-byte chunk of a source row is
+// stored whole.  V goes to the transposed tile, where a token is one element
+// of each of head_dim rows: the run's V rows are staged in LDS and written
+// back column by column, consecutive lanes taking consecutive tokens of one
+// head_dim row.  Tokens with consecutive slots in a block (a prompt chunk, a
+// long context being filled) then land in one contiguous span of each row
+// per store instruction instead of one element per cache line; scattered
+// slots (one decode token per sequence) are no worse than element stores.
+constexpr int kAppendTok = 16;
+constexpr int kAppendMaxDim = 128;
+
 template <typename E>
-__global__ __launch_bounds__(256) void kv_append_kernel(const u32x4* __restrict__ k_new,
-                                                        const u32x4* __restrict__ v_new,
-                                                        const int64_t* __restrict__ slots, int64_t total_chunks,
-                                                        int chunks_per_row, int num_kv_heads, int block_size,
-                                                        int64_t num_slots, u32x4* __restrict__ kc,
-                                                        E* __restrict__ vc) {
+__global__ __launch_bounds__(256) void kv_append_kernel(const E* __restrict__ k_new, const E* __restrict__ v_new,
+                                                        const int64_t* __restrict__ slots, int num_tokens,
+                                                        int head_dim, int num_kv_heads, int block_size,
+                                                        int64_t num_slots, E* __restrict__ kc, E* __restrict__ vc) {
   constexpr int VEC = 16 / sizeof(E);
-  for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < total_chunks;
-       i += static_cast<int64_t>(gridDim.x) * blockDim.x) {
-    const int c = static_cast<int>(i % chunks_per_row);
-    const int64_t th = i / chunks_per_row;  // token * heads + head
-    const int h = static_cast<int>(th % num_kv_heads);
-    const int64_t t = th / num_kv_heads;
-    const int64_t slot = slots[t];
-    if (slot < 0 || slot >= num_slots) continue;
-    const int64_t blk = slot / block_size;
-    const int64_t off = slot % block_size;
-    const int64_t tile = blk * num_kv_heads + h;  // (block, head) tile index
-    kc[(tile * block_size + off) * chunks_per_row + c] = k_new[i];
-    const u32x4 v = v_new[i];
-    E e[VEC];
-    __builtin_memcpy(e, &v, 16);
-    const int64_t d0 = static_cast<int64_t>(c) * VEC;
-    E* vt = vc + (tile * (chunks_per_row * VEC) + d0) * block_size + off;
-#pragma unroll
-    for (int k = 0; k < VEC; ++k) vt[static_cast<int64_t>(k) * block_size] = e[k];
+  constexpr int PITCH = kAppendMaxDim + VEC;  // LDS row pitch (elements): 16-byte aligned rows
+  __shared__ __attribute__((aligned(16))) E vs[kAppendTok][PITCH];
+  __shared__ int64_t sl[kAppendTok];
+  const int h = blockIdx.y;
+  const int t0 = blockIdx.x * kAppendTok;
+  const int tid = threadIdx.x;
+  const int cpr = head_dim / VEC;  // 16-byte chunks per row
+  if (tid < kAppendTok) {
+    const int t = t0 + tid;
+    const int64_t slot = t < num_tokens ? slots[t] : -1;
+    sl[tid] = (slot >= 0 && slot < num_slots) ? slot : -1;
+  }
+  __syncthreads();
+  for (int c = tid; c < kAppendTok * cpr; c += blockDim.x) {
+    const int r = c / cpr, cc = c - r * cpr;
+    const int t = t0 + r;
+    if (t >= num_tokens) continue;
+    const int64_t src = (static_cast<int64_t>(t) * num_kv_heads + h) * head_dim + cc * VEC;
+    const u32x4 kv = load16(k_new + src);
+    store16(&vs[r][cc * VEC], load16(v_new + src));
+    const int64_t slot = sl[r];
+    if (slot < 0) continue;
+    const int64_t tile = (slot / block_size) * num_kv_heads + h;  // (block, head) tile index
+    store16(kc + (tile * block_size + slot % block_size) * head_dim + cc * VEC, kv);
+  }
+  __syncthreads();
+  for (int e = tid; e < kAppendTok * head_dim; e += blockDim.x) {
+    const int j = e % kAppendTok, d = e / kAppendTok;
+    const int64_t slot = sl[j];
+    if (slot < 0) continue;
+    const int64_t tile = (slot / block_size) * num_kv_heads + h;
+    vc[(tile * head_dim + d) * block_size + slot % block_size] = vs[j][d];
   }
 }
 
@@ -116,20 +136,19 @@ __global__ __launch_bounds__(256) void copy_blocks_kernel(const int32_t* __restr
 hipError_t launch_kv_append(const void* k_new, const void* v_new, const int64_t* slots, int32_t num_tokens,
                             void* k_cache, void* v_cache, int32_t num_blocks, int32_t num_kv_heads,
                             int32_t block_size, int32_t head_dim, int32_t elem_bytes, hipStream_t st) {
-  const int chunks_per_row = head_dim * elem_bytes / 16;
-  const int64_t total = static_cast<int64_t>(num_tokens) * num_kv_heads * chunks_per_row;
-  if (total == 0) return hipSuccess;
-  const int64_t want = (total + 255) / 256;
-  const int grid = static_cast<int>(want < 8192 ? want : 8192);
+  if (num_tokens <= 0 || num_kv_heads <= 0) return hipSuccess;
+  if (head_dim > kAppendMaxDim || head_dim * elem_bytes % 16 != 0 || num_kv_heads > 65535)
+    return hipErrorInvalidValue;
+  const dim3 grid((num_tokens + kAppendTok - 1) / kAppendTok, num_kv_heads);
   const int64_t num_slots = static_cast<int64_t>(num_blocks) * block_size;
   if (elem_bytes == 4) {
-    hipLaunchKernelGGL(kv_append_kernel<uint32_t>, dim3(grid), dim3(256), 0, st, static_cast<const u32x4*>(k_new),
-                       static_cast<const u32x4*>(v_new), slots, total, chunks_per_row, num_kv_heads, block_size,
-                       num_slots, static_cast<u32x4*>(k_cache), static_cast<uint32_t*>(v_cache));
+    hipLaunchKernelGGL(kv_append_kernel<uint32_t>, grid, dim3(256), 0, st, static_cast<const uint32_t*>(k_new),
+                       static_cast<const uint32_t*>(v_new), slots, num_tokens, head_dim, num_kv_heads, block_size,
+                       num_slots, static_cast<uint32_t*>(k_cache), static_cast<uint32_t*>(v_cache));
   } else {
-    hipLaunchKernelGGL(kv_append_kernel<uint16_t>, dim3(grid), dim3(256), 0, st, static_cast<const u32x4*>(k_new),
-                       static_cast<const u32x4*>(v_new), slots, total, chunks_per_row, num_kv_heads, block_size,
-                       num_slots, static_cast<u32x4*>(k_cache), static_cast<uint16_t*>(v_cache));
+    hipLaunchKernelGGL(kv_append_kernel<uint16_t>, grid, dim3(256), 0, st, static_cast<const uint16_t*>(k_new),
+                       static_cast<const uint16_t*>(v_new), slots, num_tokens, head_dim, num_kv_heads, block_size,
+                       num_slots, static_cast<uint16_t*>(k_cache), static_cast<uint16_t*>(v_cache));
   }
   return hipGetLastError();
 }
