@@ -73,43 +73,62 @@ __global__ __launch_bounds__(256) void kv_append_kernel(const E* __restrict__ k_
   }
 }
 
-// Append into an FP8 pool: one thread per 16 elements of a (token, head)
-// row (two 16-byte chunks of 16-bit activations), each multiplied by the
-// fp32 reciprocal of its scale and rounded to an E4M3 code; the K codes are
-// stored as one 16-byte chunk, the V codes go to 16 rows of the transposed
-// tile.
+// Append into an FP8 pool, laid out like kv_append_kernel: one workgroup
+// per (run of kAppendTok tokens, KV head).  Each thread takes 16 elements of
+// a (token, head) row (two 16-byte chunks of 16-bit activations), multiplies
+// them by the fp32 reciprocal of the scale and rounds them to E4M3 codes;
+// the K codes are stored as one 16-byte chunk, the V codes are staged in LDS
+// and written back by head_dim row, consecutive lanes taking consecutive
+// tokens.
 template <typename AT>
-__global__ __launch_bounds__(256) void kv_append_fp8_kernel(const u32x4* __restrict__ k_new,
-                                                            const u32x4* __restrict__ v_new,
-                                                            const int64_t* __restrict__ slots, int64_t total_groups,
-                                                            int groups_per_row, int num_kv_heads, int block_size,
+__global__ __launch_bounds__(256) void kv_append_fp8_kernel(const typename AT::elem* __restrict__ k_new,
+                                                            const typename AT::elem* __restrict__ v_new,
+                                                            const int64_t* __restrict__ slots, int num_tokens,
+                                                            int head_dim, int num_kv_heads, int block_size,
                                                             int64_t num_slots, float k_inv, float v_inv,
-                                                            u32x4* __restrict__ kc, uint8_t* __restrict__ vc) {
-  for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < total_groups;
-       i += static_cast<int64_t>(gridDim.x) * blockDim.x) {
-    const int c = static_cast<int>(i % groups_per_row);
-    const int64_t th = i / groups_per_row;  // token * heads + head
-    const int h = static_cast<int>(th % num_kv_heads);
-    const int64_t t = th / num_kv_heads;
-    const int64_t slot = slots[t];
-    if (slot < 0 || slot >= num_slots) continue;
-    const int64_t blk = slot / block_size;
-    const int64_t off = slot % block_size;
-    const int64_t tile = blk * num_kv_heads + h;
+                                                            uint8_t* __restrict__ kc, uint8_t* __restrict__ vc) {
+  __shared__ __attribute__((aligned(16))) uint8_t vs[kAppendTok][kAppendMaxDim + 16];
+  __shared__ int64_t sl[kAppendTok];
+  const int h = blockIdx.y;
+  const int t0 = blockIdx.x * kAppendTok;
+  const int tid = threadIdx.x;
+  const int gpr = head_dim / 16;  // 16-code groups per row
+  if (tid < kAppendTok) {
+    const int t = t0 + tid;
+    const int64_t slot = t < num_tokens ? slots[t] : -1;
+    sl[tid] = (slot >= 0 && slot < num_slots) ? slot : -1;
+  }
+  __syncthreads();
+  auto codes = [](const typename AT::elem* src, float inv) {
     float x[16];
-    widen16<AT>(k_new[2 * i], x);
-    widen16<AT>(k_new[2 * i + 1], x + 8);
-    u32x4 kq;
+    widen16<AT>(load16(src), x);
+    widen16<AT>(load16(src + 8), x + 8);
+    u32x4 q;
 #pragma unroll
     for (int w = 0; w < 4; ++w)
-      kq[w] = to_e4m3(x[4 * w] * k_inv) | (to_e4m3(x[4 * w + 1] * k_inv) << 8) |
-              (to_e4m3(x[4 * w + 2] * k_inv) << 16) | (to_e4m3(x[4 * w + 3] * k_inv) << 24);
-    kc[(tile * block_size + off) * groups_per_row + c] = kq;
-    widen16<AT>(v_new[2 * i], x);
-    widen16<AT>(v_new[2 * i + 1], x + 8);
-    uint8_t* vt = vc + (tile * (groups_per_row * 16) + c * 16) * block_size + off;
-#pragma unroll
-    for (int k = 0; k < 16; ++k) vt[static_cast<int64_t>(k) * block_size] = static_cast<uint8_t>(to_e4m3(x[k] * v_inv));
+      q[w] = to_e4m3(x[4 * w] * inv) | (to_e4m3(x[4 * w + 1] * inv) << 8) | (to_e4m3(x[4 * w + 2] * inv) << 16) |
+             (to_e4m3(x[4 * w + 3] * inv) << 24);
+    return q;
+  };
+  for (int c = tid; c < kAppendTok * gpr; c += blockDim.x) {
+    const int r = c / gpr, cc = c - r * gpr;
+    const int t = t0 + r;
+    if (t >= num_tokens) continue;
+    const int64_t src = (static_cast<int64_t>(t) * num_kv_heads + h) * head_dim + cc * 16;
+    const u32x4 kq = codes(k_new + src, k_inv);
+    store16(&vs[r][cc * 16], codes(v_new + src, v_inv));
+    const int64_t slot = sl[r];
+    if (slot < 0) continue;
+    const int64_t tile = (slot / block_size) * num_kv_heads + h;
+    store16(kc + (tile * block_size + slot % block_size) * head_dim + cc * 16, kq);
+  }
+  __syncthreads();
+  for (int e = tid; e < kAppendTok * head_dim; e += blockDim.x) {
+    const int j = e % kAppendTok, d = e / kAppendTok;
+    const int64_t slot = sl[j];
+    if (slot < 0) continue;
+    const int64_t tile = (slot / block_size) * num_kv_heads + h;
+    vc[(tile * head_dim + d) * block_size + slot % block_size] = vs[j][d];
   }
 }
 
@@ -157,16 +176,18 @@ hipError_t launch_kv_append_fp8(const void* k_new, const void* v_new, const int6
                                 void* k_cache, void* v_cache, int32_t num_blocks, int32_t num_kv_heads,
                                 int32_t block_size, int32_t head_dim, int32_t act_dtype, float k_inv, float v_inv,
                                 hipStream_t st) {
-  const int groups_per_row = head_dim / 16;
-  const int64_t total = static_cast<int64_t>(num_tokens) * num_kv_heads * groups_per_row;
-  if (total == 0) return hipSuccess;
-  const int64_t want = (total + 255) / 256;
-  const int grid = static_cast<int>(want < 8192 ? want : 8192);
+  if (num_tokens <= 0 || num_kv_heads <= 0) return hipSuccess;
+  if (head_dim > kAppendMaxDim || head_dim % 16 != 0 || num_kv_heads > 65535) return hipErrorInvalidValue;
+  const dim3 grid((num_tokens + kAppendTok - 1) / kAppendTok, num_kv_heads);
   const int64_t num_slots = static_cast<int64_t>(num_blocks) * block_size;
-  auto kern = act_dtype == 1 ? kv_append_fp8_kernel<F16> : kv_append_fp8_kernel<BF16>;
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(256), 0, st, static_cast<const u32x4*>(k_new),
-                     static_cast<const u32x4*>(v_new), slots, total, groups_per_row, num_kv_heads, block_size, num_slots,
-                     k_inv, v_inv, static_cast<u32x4*>(k_cache), static_cast<uint8_t*>(v_cache));
+  if (act_dtype == 1)
+    hipLaunchKernelGGL(kv_append_fp8_kernel<F16>, grid, dim3(256), 0, st, static_cast<const F16::elem*>(k_new),
+                       static_cast<const F16::elem*>(v_new), slots, num_tokens, head_dim, num_kv_heads, block_size,
+                       num_slots, k_inv, v_inv, static_cast<uint8_t*>(k_cache), static_cast<uint8_t*>(v_cache));
+  else
+    hipLaunchKernelGGL(kv_append_fp8_kernel<BF16>, grid, dim3(256), 0, st, static_cast<const BF16::elem*>(k_new),
+                       static_cast<const BF16::elem*>(v_new), slots, num_tokens, head_dim, num_kv_heads, block_size,
+                       num_slots, k_inv, v_inv, static_cast<uint8_t*>(k_cache), static_cast<uint8_t*>(v_cache));
   return hipGetLastError();
 }
 
