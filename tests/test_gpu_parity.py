@@ -154,3 +154,29 @@ def test_zero_length_context_gives_zeros():
     P.pa_decode(cache.desc, q, out, plan.block_tables, lens, int(plan.host_lens.max()), sp.scale, 0)
     o = to_host(out)
     assert (o[2] == 0).all() and np.isfinite(o).all()
+
+
+def test_decode_one_pass_beyond_ranked_batch():
+    """More sequences than the one-pass grid ranks by length (256): the grid
+    then maps workgroups to sequences by index."""
+    rng = np.random.default_rng(4031)
+    lens = [int(x) for x in rng.integers(1, 81, size=300)]
+    wl = workloads.custom(8, 2, 64, 16, "f16", lens, seed=5)
+    print("[gpu] decode one pass, 300 sequences", flush=True)
+    st, ref = _oracle(wl)
+    for part in (0, -1):
+        res = run_step(wl, partition_size=part, keep_pool=False)
+        assert _max_err(res, ref, "f16") <= TOL["f16"]
+
+
+def test_prefill_item_order_beyond_sorted_limit():
+    """More prefill work items per XCD than the kernel orders longest first
+    (4096): items then run in index order, with the same results."""
+    rng = np.random.default_rng(4032)
+    n = [int(x) for x in rng.integers(1, 5, size=4200)]
+    ctx = [k + int(x) for k, x in zip(n, rng.integers(0, 20, size=4200))]
+    wl = workloads.custom(8, 8, 64, 16, "f16", ctx, n_new=n, seed=6)
+    print("[gpu] prefill, 4200 chunks x 8 KV heads", flush=True)
+    st, ref = _oracle(wl)
+    res = run_step(wl, keep_pool=False, prefill_all=True)
+    assert _max_err(res, ref, "f16") <= TOL["f16"]
