@@ -134,6 +134,14 @@ def test_prefill_rejects_fp32():
     assert _prefill(_cache(dtype=P.PA_F32)) == P.PA_EUNSUPPORTED
 
 
+def test_prefill_rejects_contexts_whose_table_exceeds_lds():
+    """The chunk's block-table entries are staged in LDS next to the two K/V
+    tile buffers: a context whose table does not fit is refused before any
+    HIP call (about 364k tokens at block_size 16, head_dim 128)."""
+    assert _prefill(_cache(), max_ctx=400000, max_blocks=400000 // 16 + 1) == P.PA_EUNSUPPORTED
+    assert _prefill(_cache(block_size=8), max_ctx=200000, max_blocks=200000 // 8 + 1) == P.PA_EUNSUPPORTED
+
+
 def test_append_and_copy_validation():
     c = _cache()
     assert P.lib().pa_kv_append(ctypes.byref(c), FAKE, FAKE, FAKE, -1, None) == P.PA_EINVAL
