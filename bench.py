@@ -372,6 +372,102 @@ def time_prefill(st, iters, warmup):
     return a.elapsed_time(b) / iters * 1e3
 
 
+def measure_serving_loop(n_requests=1024, budget=8192, max_running=256):
+    """The host scheduler loop (pa_sched_*) driving the kernels over a
+    synthetic arrival trace, as a serving engine would each iteration: the
+    scheduler picks decode tokens and prompt chunks under a token budget and
+    hands out slots, then one pa_kv_append, one pa_prefill_chunk and one
+    pa_decode run on the iteration's batch.  Shapes of the mixed workload
+    (32 q / 8 KV heads, head_dim 128, bf16, block_size 16); prompts lognormal
+    around 512 tokens (cap 4096), 1..64 new tokens each; a pool that holds
+    every request.  K/V/q rows are synthetic values (their contents do not
+    change the work).  Reports tokens per second through the whole loop
+    (host scheduling, table uploads and kernels, wall clock) and the part of
+    that time the GPU was busy (events around each iteration's kernels)."""
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_403_amd as P
+    import workloads
+    from paged_kv_cache_403_amd.runtime import PagedKVCache
+
+    hq, hkv, d, bs, dt = 32, 8, 128, 16, "bf16"
+    trace = workloads.arrival_trace(n_requests, seed=3, median_prompt=512, max_prompt=4096, max_new=64,
+                                    mean_gap=0.25)
+    nb = sum(-(-(p + m) // bs) for _, _, p, m in trace) + 1
+    g = torch.Generator(device="cuda").manual_seed(403)
+    rows = budget + max_running
+    kbuf = torch.randn(rows, hkv, d, device="cuda", dtype=torch.bfloat16, generator=g)
+    vbuf = torch.randn(rows, hkv, d, device="cuda", dtype=torch.bfloat16, generator=g)
+    qbuf = torch.randn(rows, hq, d, device="cuda", dtype=torch.bfloat16, generator=g)
+    obuf = torch.empty_like(qbuf)
+    max_ctx = max(p + m for _, _, p, m in trace)
+    wsb = P.pa_decode_workspace_bytes(max_running, hq, d, max_ctx, -1)
+    ws = torch.empty(max(wsb, 4), dtype=torch.uint8, device="cuda")
+    scale = 1.0 / np.sqrt(d)
+
+    def run():
+        cache = PagedKVCache(nb, hkv, bs, d, dt, "cuda", np.arange(nb - 1, dtype=np.int32), fill_value=0.0)
+        sched = P.Scheduler(cache.bm, budget, max_running)
+        k, it, tokens = 0, 0, 0
+        cached = {}
+        events = []
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        while (k < len(trace) or sched.unfinished() > 0) and it < 100000:
+            while k < len(trace) and trace[k][0] <= it:
+                sched.add(*trace[k][1:])
+                k += 1
+            decodes, prefills, slots, pairs, finished, pre = sched.step()
+            it += 1
+            entries = [(rid, 1) for rid in decodes] + list(prefills)
+            if not entries:
+                continue
+            for rid in pre:  # preempted: prefilled again from the start
+                cached[rid] = 0
+            T = int(sum(n for _, n in entries))
+            tokens += T
+            ids = np.array([rid for rid, _ in entries], np.int32)
+            for rid, n in entries:
+                cached[rid] = cached.get(rid, 0) + n
+            lens = np.array([cached[rid] for rid, _ in entries], np.int32)
+            mb = int(max(-(-int(lens.max()) // bs), 1))
+            tables, _ = cache.bm.tables(ids, mb, nb - 1)
+            slots_d = torch.from_numpy(slots).cuda()
+            tables_d = torch.from_numpy(tables).cuda()
+            lens_d = torch.from_numpy(lens).cuda()
+            nd = len(decodes)
+            if prefills:
+                n_new = np.array([n for _, n in prefills], np.int32)
+                cu_d = torch.from_numpy(np.concatenate([[0], np.cumsum(n_new)]).astype(np.int32)).cuda()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            if len(pairs):
+                P.pa_copy_blocks(cache.desc, torch.from_numpy(pairs).cuda())
+            P.pa_kv_append(cache.desc, kbuf[:T], vbuf[:T], slots_d)
+            if nd:
+                P.pa_decode(cache.desc, qbuf[:nd], obuf[:nd], tables_d[:nd], lens_d[:nd], int(lens[:nd].max()),
+                            scale, -1, ws)
+            if prefills:
+                npre = int(n_new.sum())
+                P.pa_prefill_chunk(cache.desc, qbuf[nd:nd + npre], obuf[nd:nd + npre], cu_d, lens_d[nd:],
+                                   tables_d[nd:], int(n_new.max()), int(lens[nd:].max()), scale)
+            b.record()
+            events.append((a, b))
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        return it, tokens, wall, sum(x.elapsed_time(y) for x, y in events)
+
+    run()  # warm-up pass over the same trace
+    it, tokens, wall, gpu_ms = run()
+    res = {"requests": n_requests, "iterations": it, "tokens": tokens, "wall_s": round(wall, 4),
+           "tokens_per_s": round(tokens / wall, 1), "gpu_busy_ms": round(gpu_ms, 2),
+           "gpu_share": round(gpu_ms / (wall * 1e3), 3), "token_budget": budget, "max_running": max_running}
+    log(f"serving loop: {n_requests} requests, {it} iterations, {tokens} tokens in {wall:.3f} s = "
+        f"{tokens / wall:.0f} tokens/s (GPU busy {gpu_ms:.1f} ms)")
+    return res
+
+
 def measure_fp8(name, ref_us, iters, warmup, prefill_name=None):
     """Decode of the same batch with an FP8 (E4M3) pool and 16-bit
     activations: time, algorithmic bytes (1-byte K/V), rate, and the speedup
@@ -473,6 +569,7 @@ def main():
     ap.add_argument("--no-fp8", action="store_true", help="skip the FP8 KV-pool decode measurement")
     ap.add_argument("--no-block-sizes", action="store_true", help="skip the block-size sweep")
     ap.add_argument("--no-long", action="store_true", help="skip the long-context split-K measurement")
+    ap.add_argument("--no-serving", action="store_true", help="skip the scheduler-loop measurement")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB a few times (the known-size reference for "
                          "the HBM byte counters) and exit")
@@ -562,6 +659,8 @@ def main():
         result["block_sizes"] = measure_block_sizes(args.workload, max(10, args.steps // 2), 3)
     if not args.no_long:
         result["long_split"] = measure_long("long_splitk_decode", max(10, args.steps // 2), 3)
+    if not args.no_serving:
+        result["serving_loop"] = measure_serving_loop()
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a sample")
         result["cpu_baseline"] = cpu_baseline(wl)
