@@ -36,7 +36,7 @@
  *    num_q_heads a multiple of num_kv_heads with group size
  *    num_q_heads/num_kv_heads in {1, 2, 4, 8}.  pa_prefill_chunk needs f16
  *    or bf16 (its contractions run on the matrix cores); pa_decode_grouped
- *    needs f16 or bf16 and block_size 16, 32 or 64.  An FP8 pool (see pa_cache)
+ *    needs f16 or bf16 (any of the block sizes).  An FP8 pool (see pa_cache)
  *    has head_dim 128, block_size 16..64 and f16 or bf16 activations, and is
  *    supported by pa_kv_append, pa_copy_blocks, pa_decode,
  *    pa_prefill_chunk and pa_decode_grouped.
@@ -163,7 +163,8 @@ int32_t pa_decode_choose_partition(const pa_cache* cache, int32_t num_seqs, int3
                                    int32_t max_context_len);
 
 /* Bytes of device workspace pa_decode_grouped needs (partition_size as
- * passed to it; 0 = the default). */
+ * passed to it; 0 = the default, sized for the smaller default of 8-token
+ * blocks, so it covers every block size). */
 size_t pa_decode_grouped_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
                                          int32_t max_context_len, int32_t partition_size);
 
@@ -182,9 +183,10 @@ size_t pa_decode_grouped_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, 
  *                   tables how many leading full blocks each sequence has in
  *                   common with its chunk's longest sequence; any grouping
  *                   (NULL with num_groups 0 included) gives the same result
- *   partition_size  0 = 1024; else a multiple of 32 and of block_size, at
- *                   most 64 blocks: tokens per partition of both the shared
- *                   prefix and each sequence's own suffix
+ *   partition_size  0 = 1024 (512 for 8-token blocks); else a multiple of
+ *                   32 and of block_size, at most 64 blocks: tokens per
+ *                   partition of both the shared prefix and each sequence's
+ *                   own suffix
  *   workspace       device scratch of at least
  *                   pa_decode_grouped_workspace_bytes(); rewritten by each
  *                   call, so calls sharing it must be ordered on one stream

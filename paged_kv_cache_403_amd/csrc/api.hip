@@ -107,7 +107,15 @@ GroupedLayout grouped_layout(int64_t num_seqs, int64_t num_q_heads, int64_t head
   return g;
 }
 
-int32_t grouped_partition(int32_t requested) { return requested == 0 ? kGroupedDefaultPartition : requested; }
+// The partition pa_decode_grouped uses: the default is 1024 tokens, but a
+// prefix item keeps one block id per lane (at most 64 blocks), so 8-token
+// blocks default to 512.  The workspace for the default is sized for 512,
+// which covers both.
+int32_t grouped_partition(int32_t requested, int32_t block_size) {
+  if (requested != 0) return requested;
+  return block_size < 16 ? 64 * block_size : kGroupedDefaultPartition;
+}
+constexpr int32_t kGroupedSmallestDefault = 512;
 
 }  // namespace
 
@@ -305,7 +313,7 @@ extern "C" {
 
 size_t pa_decode_grouped_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
                                          int32_t max_context_len, int32_t partition_size) {
-  const int32_t part = grouped_partition(partition_size);
+  const int32_t part = partition_size == 0 ? kGroupedSmallestDefault : partition_size;
   if (num_seqs <= 0 || num_q_heads <= 0 || head_dim <= 0 || max_context_len < 0 || part <= 0) return 0;
   return grouped_layout(num_seqs, num_q_heads, head_dim, max_context_len, part).total;
 }
@@ -317,14 +325,13 @@ int pa_decode_grouped(const pa_cache* cache, const void* q, void* out, int32_t n
   int rc = check_cache(cache);
   if (rc != PA_OK) return rc;
   if (cache->dtype == PA_F32) return PA_EUNSUPPORTED;
-  if (cache->block_size == 8) return PA_EUNSUPPORTED;
   int32_t group = 0;
   if ((rc = check_group(cache, num_q_heads, &group)) != PA_OK) return rc;
   if ((rc = check_scale(scale)) != PA_OK) return rc;
   if (num_seqs < 0 || num_groups < 0 || max_blocks_per_seq <= 0 || max_context_len < 0) return PA_EINVAL;
   if (static_cast<int64_t>(max_context_len) > static_cast<int64_t>(max_blocks_per_seq) * cache->block_size)
     return PA_EINVAL;
-  const int32_t part = grouped_partition(partition_size);
+  const int32_t part = grouped_partition(partition_size, cache->block_size);
   if (part <= 0 || part % 32 != 0 || part % cache->block_size != 0 || part / cache->block_size > 64) return PA_EINVAL;
   if (num_seqs > pa::kGroupedMaxSeqs) return PA_EUNSUPPORTED;
   if (num_seqs == 0) return PA_OK;

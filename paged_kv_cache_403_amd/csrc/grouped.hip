@@ -305,7 +305,7 @@ template <typename ST, int D, int BS, int G, typename AT>
 __device__ __forceinline__ void prefix_item(PrefixLds<D>& sh, const GroupedParams& GP, int item, int kvh, int& first,
                                             int& members) {
   static_assert(D % 32 == 0 && D >= 64, "head_dim");
-  static_assert(BS == 16 || BS == 32 || BS == 64, "block size");
+  static_assert(BS == 8 || BS == 16 || BS == 32 || BS == 64, "block size");
   constexpr int KS = D / 16;      // contraction steps of S^T = K Q^T
   constexpr int DT = D / 32;      // 32-wide column tiles of O^T
   using elem = typename ST::elem;
@@ -725,6 +725,9 @@ hipError_t by_group(const GroupedArgs& a, hipStream_t st) {
 template <typename ST, int D, typename AT>
 hipError_t by_block(const GroupedArgs& a, hipStream_t st) {
   switch (a.d.block_size) {
+    case 8:
+      if constexpr (ST::bytes == 1) return hipErrorInvalidValue;  // FP8 pools hold blocks of 16 tokens or more
+      else return by_group<ST, D, 8, AT>(a, st);
     case 16: return by_group<ST, D, 16, AT>(a, st);
     case 32: return by_group<ST, D, 32, AT>(a, st);
     case 64: return by_group<ST, D, 64, AT>(a, st);

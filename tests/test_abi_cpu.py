@@ -187,7 +187,10 @@ def test_grouped_decode_validation(kw, code):
 
 def test_grouped_decode_rejects_fp32_and_accepts_empty_batch():
     assert _grouped(_cache(dtype=P.PA_F32)) == P.PA_EUNSUPPORTED
-    assert _grouped(_cache(block_size=8), max_blocks=16) == P.PA_EUNSUPPORTED  # one block id per lane: 64 * 8 < 1024
+    # 8-token blocks: the default partition is 512 tokens (one block id per
+    # lane, at most 64 blocks); an explicit partition over 64 blocks is refused
+    assert _grouped(_cache(block_size=8), max_blocks=16, num_seqs=0) == P.PA_OK
+    assert _grouped(_cache(block_size=8), max_blocks=16, part=1024) == P.PA_EINVAL
     assert _grouped(_cache(block_size=64), num_seqs=0) == P.PA_OK
     assert _grouped(_cache(), num_seqs=0) == P.PA_OK
 
@@ -203,7 +206,10 @@ def test_grouped_workspace_size_formula():
     want = (a16(S * hq * 2 * parts * 2 * 4) + a16(S * hq * 2 * parts * d * 4) + a16(S * parts * 2 * 4)
             + a16(S * parts * 4 * 4) + 3 * a16(S * 4) + a16(8))
     assert P.pa_decode_grouped_workspace_bytes(S, hq, d, C, part) == want
-    assert P.pa_decode_grouped_workspace_bytes(S, hq, d, C, 0) == want  # 0 = 1024 tokens
+    # 0 = the default partition, sized for the smaller default (512 tokens,
+    # 8-token blocks) so it covers every block size
+    assert P.pa_decode_grouped_workspace_bytes(S, hq, d, C, 0) == P.pa_decode_grouped_workspace_bytes(S, hq, d, C, 512)
+    assert P.pa_decode_grouped_workspace_bytes(S, hq, d, C, 0) > want
     assert P.pa_decode_grouped_workspace_bytes(0, hq, d, C, 0) == 0
 
 

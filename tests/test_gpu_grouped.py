@@ -55,6 +55,7 @@ def test_shared_prefix_reduced(part):
 GROUP_SHAPES = [  # (Hq, Hkv, D, BS, dtype): q heads per KV head 1, 2, 4, 8
     (8, 8, 128, 16, "bf16"), (8, 4, 64, 16, "f16"), (32, 8, 128, 16, "bf16"), (16, 2, 128, 32, "f16"),
     (4, 4, 64, 32, "bf16"), (8, 1, 64, 16, "bf16"), (32, 8, 128, 64, "bf16"), (8, 4, 64, 64, "f16"),
+    (32, 8, 128, 8, "bf16"), (8, 8, 64, 8, "f16"),  # 8-token blocks: 512-token default partitions
 ]
 
 
