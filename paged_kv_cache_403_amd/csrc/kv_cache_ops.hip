@@ -158,7 +158,8 @@ hipError_t launch_kv_append(const void* k_new, const void* v_new, const int64_t*
   if (num_tokens <= 0 || num_kv_heads <= 0) return hipSuccess;
   if (head_dim > kAppendMaxDim || head_dim * elem_bytes % 16 != 0 || num_kv_heads > 65535)
     return hipErrorInvalidValue;
-  const dim3 grid((num_tokens + kAppendTok - 1) / kAppendTok, num_kv_heads);
+  const dim3 grid(static_cast<unsigned>((static_cast<int64_t>(num_tokens) + kAppendTok - 1) / kAppendTok),
+                  static_cast<unsigned>(num_kv_heads));
   const int64_t num_slots = static_cast<int64_t>(num_blocks) * block_size;
   if (elem_bytes == 4) {
     hipLaunchKernelGGL(kv_append_kernel<uint32_t>, grid, dim3(256), 0, st, static_cast<const uint32_t*>(k_new),
@@ -178,7 +179,8 @@ hipError_t launch_kv_append_fp8(const void* k_new, const void* v_new, const int6
                                 hipStream_t st) {
   if (num_tokens <= 0 || num_kv_heads <= 0) return hipSuccess;
   if (head_dim > kAppendMaxDim || head_dim % 16 != 0 || num_kv_heads > 65535) return hipErrorInvalidValue;
-  const dim3 grid((num_tokens + kAppendTok - 1) / kAppendTok, num_kv_heads);
+  const dim3 grid(static_cast<unsigned>((static_cast<int64_t>(num_tokens) + kAppendTok - 1) / kAppendTok),
+                  static_cast<unsigned>(num_kv_heads));
   const int64_t num_slots = static_cast<int64_t>(num_blocks) * block_size;
   if (act_dtype == 1)
     hipLaunchKernelGGL(kv_append_fp8_kernel<F16>, grid, dim3(256), 0, st, static_cast<const F16::elem*>(k_new),
