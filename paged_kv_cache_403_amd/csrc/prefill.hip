@@ -270,10 +270,11 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(
     f32x16 sacc[2] = {f32x16{}, f32x16{}};
     float mx = -INFINITY;
     if (active) {
-      // S^T for the two 32-key subtiles.  All sixteen K operands are read
-      // from LDS before the products (the group barriers below keep the
-      // scheduler from pairing each read with its product): with every read
-      // in flight the wave waits once for LDS, not once per product.
+      // S^T for the two 32-key subtiles.  The sixteen K operands are read
+      // from LDS ahead of the products, in two batches of eight (the group
+      // barriers below hold the scheduler to that order instead of pairing
+      // each read with its product), so the wave waits for LDS twice per
+      // tile rather than once per product.
       u32x4 ka[S::KSTEPS][2];
 #pragma unroll
       for (int kk = 0; kk < S::KSTEPS; ++kk)
