@@ -50,16 +50,17 @@ __global__ __launch_bounds__(256) void kv_append_kernel(const E* __restrict__ k_
     const int64_t slot = t < num_tokens ? slots[t] : -1;
     sl[tid] = (slot >= 0 && slot < num_slots) ? slot : -1;
   }
-  __syncthreads();
+  // K needs no exchange: each thread reads its token's slot itself, so the
+  // slot, K and V loads are in flight together (sl[] serves the V phase)
   for (int c = tid; c < kAppendTok * cpr; c += blockDim.x) {
     const int r = c / cpr, cc = c - r * cpr;
     const int t = t0 + r;
     if (t >= num_tokens) continue;
     const int64_t src = (static_cast<int64_t>(t) * num_kv_heads + h) * head_dim + cc * VEC;
+    const int64_t slot = slots[t];
     const u32x4 kv = load16(k_new + src);
     store16(&vs[r][cc * VEC], load16(v_new + src));
-    const int64_t slot = sl[r];
-    if (slot < 0) continue;
+    if (slot < 0 || slot >= num_slots) continue;
     const int64_t tile = (slot / block_size) * num_kv_heads + h;  // (block, head) tile index
     store16(kc + (tile * block_size + slot % block_size) * head_dim + cc * VEC, kv);
   }
@@ -98,7 +99,6 @@ __global__ __launch_bounds__(256) void kv_append_fp8_kernel(const typename AT::e
     const int64_t slot = t < num_tokens ? slots[t] : -1;
     sl[tid] = (slot >= 0 && slot < num_slots) ? slot : -1;
   }
-  __syncthreads();
   auto codes = [](const typename AT::elem* src, float inv) {
     float x[16];
     widen16<AT>(load16(src), x);
@@ -115,10 +115,10 @@ __global__ __launch_bounds__(256) void kv_append_fp8_kernel(const typename AT::e
     const int t = t0 + r;
     if (t >= num_tokens) continue;
     const int64_t src = (static_cast<int64_t>(t) * num_kv_heads + h) * head_dim + cc * 16;
+    const int64_t slot = slots[t];
     const u32x4 kq = codes(k_new + src, k_inv);
     store16(&vs[r][cc * 16], codes(v_new + src, v_inv));
-    const int64_t slot = sl[r];
-    if (slot < 0) continue;
+    if (slot < 0 || slot >= num_slots) continue;
     const int64_t tile = (slot / block_size) * num_kv_heads + h;
     store16(kc + (tile * block_size + slot % block_size) * head_dim + cc * 16, kq);
   }
