@@ -119,8 +119,9 @@ def test_decode_shapes_and_ragged_lengths(shape):
         assert _max_err(res, ref, dt) <= TOL[dt]
 
 
-PREFILL_SHAPES = [  # (Hq, Hkv, D, BS, dtype)
+PREFILL_SHAPES = [  # (Hq, Hkv, D, BS, dtype): q heads per KV head 1, 4, 8, 1, 2, 2
     (8, 8, 128, 16, "bf16"), (8, 2, 64, 32, "f16"), (16, 2, 128, 32, "bf16"), (16, 16, 64, 16, "f16"),
+    (8, 4, 128, 16, "bf16"), (16, 8, 64, 64, "f16"),
 ]
 
 
