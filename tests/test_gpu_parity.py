@@ -101,9 +101,10 @@ def test_nan_in_unused_slots_does_not_leak(name):
     assert np.array_equal(a.out, b.out)
 
 
-SHAPES = [  # (Hq, Hkv, D, BS, dtype)
+SHAPES = [  # (Hq, Hkv, D, BS, dtype): q heads per KV head 1, 2, 8, 8, 2, 1, 8, 2, 4, 4
     (8, 8, 64, 16, "f32"), (8, 4, 128, 32, "f32"), (16, 2, 64, 16, "f16"), (8, 1, 128, 32, "f16"),
     (4, 2, 64, 32, "bf16"), (16, 16, 128, 16, "bf16"), (32, 4, 128, 16, "bf16"), (8, 4, 64, 16, "f16"),
+    (16, 4, 64, 16, "f16"), (32, 8, 128, 32, "bf16"),
 ]
 
 
