@@ -397,13 +397,12 @@ hipError_t launch_t(const PrefillArgs& a, hipStream_t st) {
                                               per_xcd <= kSortMax ? static_cast<size_t>(per_xcd) : 0);
   const size_t lds = 2 * S::STAGE * sizeof(elem) + tbl_entries * sizeof(int32_t);
   if (lds > kPrefillMaxLds) return hipErrorInvalidValue;
-  static bool lds_attr_set = false;  // above 64 KiB of dynamic LDS must be allowed explicitly
-  if (!lds_attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_kernel<ST, PT, D, BS, G>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(kPrefillMaxLds));
-    if (e != hipSuccess) return e;
-    lds_attr_set = true;
-  }
+  // above 64 KiB of dynamic LDS must be allowed explicitly; a function-local
+  // static is set once, also when several host threads launch at once
+  static const hipError_t lds_attr =
+      hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_kernel<ST, PT, D, BS, G>),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(kPrefillMaxLds));
+  if (lds_attr != hipSuccess) return lds_attr;
   using pelem = typename PT::elem;
   hipLaunchKernelGGL((prefill_kernel<ST, PT, D, BS, G>), dim3(static_cast<unsigned>(grid)), dim3(kThreads), lds, st,
                      static_cast<const elem*>(a.q), static_cast<const pelem*>(a.k_cache),
