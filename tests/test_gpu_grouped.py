@@ -217,3 +217,81 @@ def test_fp8_grouped_nan_codes_in_unused_slots_do_not_leak():
     b = run_step(wl, keep_pool=False, grouped=True, group_start=hint)
     assert np.isfinite(to_f64(a.out, wl.spec.dtype)).all()
     assert np.array_equal(a.out, b.out)
+
+
+def _max_batch(rng, num_seqs, block_size):
+    """Tables of `num_seqs` sequences in groups of 1..12 that share 0..6
+    leading blocks; a fifth of the members hold a private copy of one shared
+    block (a shorter shared length), most have private tails of 1..40
+    tokens (folded into the prefix items), a fifth 65..300 (suffix items),
+    and a few have no tokens at all."""
+    tables, lens, starts = [], [], []
+    next_blk = 0
+    while len(lens) < num_seqs:
+        size = min(int(rng.integers(1, 13)), num_seqs - len(lens))
+        pre = int(rng.integers(0, 7))
+        prefix = list(range(next_blk, next_blk + pre))
+        next_blk += pre
+        starts.append(len(lens))
+        for _ in range(size):
+            row = list(prefix)
+            if pre > 1 and rng.random() < 0.2:
+                row[int(rng.integers(1, pre))] = next_blk
+                next_blk += 1
+            own = int(rng.integers(65, 301)) if rng.random() < 0.2 else int(rng.integers(1, 41))
+            if rng.random() < 0.01:
+                row, own = [], 0
+            nown = (own + block_size - 1) // block_size
+            row += list(range(next_blk, next_blk + nown))
+            next_blk += nown
+            tables.append(row)
+            lens.append(len(row) * block_size - (nown * block_size - own) if row else 0)
+    max_blocks = max(len(r) for r in tables)
+    tab = np.zeros((num_seqs, max_blocks), np.int32)
+    for i, r in enumerate(tables):
+        tab[i, :len(r)] = r
+    return tab, np.array(lens, np.int32), np.array(starts + [num_seqs], np.int32), next_blk
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_largest_batch_the_planner_takes(dtype):
+    """4096 sequences, the most pa_decode_grouped takes: the planner's scans,
+    chunk cuts and table comparisons run over several passes of its
+    workgroup.  Every row against the oracle's paged attention, for the
+    natural hint, no hint and random cuts, at the default and at 64-token
+    partitions."""
+    import paged_kv_cache_403_amd as P
+    from paged_kv_cache_403_amd.runtime import PagedKVCache, to_device, to_host
+
+    Hq, Hkv, D, BS = 8, 2, 64, 16
+    rng = np.random.default_rng([403, 4096, len(dtype)])
+    tab, lens, starts, nblk = _max_batch(rng, 4096, BS)
+    S = len(lens)
+    print(f"[gpu] grouped {dtype}: {S} seqs, {nblk} blocks, max ctx {lens.max()}", flush=True)
+    td = {"f16": torch.float16, "bf16": torch.bfloat16}[dtype]
+    k = torch.randn((nblk, Hkv, BS, D)).to(td)
+    # V at half scale keeps every output below 4 in magnitude, where the
+    # tolerances cover a correctly rounded result
+    v = (0.5 * torch.randn((nblk, Hkv, BS, D))).to(td)
+    q = torch.randn((S, Hq, D)).to(td)
+    cache = PagedKVCache(nblk, Hkv, BS, D, dtype, "cuda")
+    cache.k.copy_(k)
+    cache.v.copy_(v.transpose(2, 3))  # the pool keeps V as [dim][slot] inside a block
+    scale = 1.0 / np.sqrt(D)
+    ref, _ = A.paged_attention(to_host(q), to_host(k), to_host(v), tab, lens, np.ones(S, np.int64), scale, dtype)
+    max_ctx = int(lens.max())
+    dq = q.to("cuda")
+    dtab = torch.from_numpy(tab).to("cuda")
+    dlens = torch.from_numpy(lens).to("cuda")
+    cuts = np.unique(np.concatenate([[0], rng.integers(1, S, size=S // 5), [S]])).astype(np.int32)
+    for part in (0, 64):
+        ws = torch.empty(P.pa_decode_grouped_workspace_bytes(S, Hq, D, max_ctx, part), dtype=torch.uint8,
+                         device="cuda")
+        for name, hint in (("natural", starts), ("none", None), ("random", cuts)):
+            out = torch.full_like(dq, 7.0)
+            h = None if hint is None else torch.from_numpy(hint).to("cuda")
+            P.pa_decode_grouped(cache.desc, dq, out, dtab, dlens, max_ctx, scale, h, part, ws)
+            torch.cuda.synchronize()
+            err = float(np.abs(to_f64(to_host(out), dtype) - ref).max())
+            print(f"[gpu]   part {part} hint {name}: max|err| = {err:.3e}", flush=True)
+            assert err <= TOL[dtype], (part, name, err)
