@@ -182,3 +182,19 @@ def test_prefill_item_order_beyond_sorted_limit():
     st, ref = _oracle(wl)
     res = run_step(wl, keep_pool=False, prefill_all=True)
     assert _max_err(res, ref, "f16") <= TOL["f16"]
+
+
+def test_split_decode_more_sequences_than_planner_threads():
+    """Split decode over 3000 sequences: the planner's counting sort takes
+    them over several passes of its 1024 threads; every row against the
+    oracle, for 32- and 64-token partitions and the library's choice."""
+    rng = np.random.default_rng(4033)
+    lens = [int(x) for x in rng.integers(1, 201, size=3000)]
+    wl = workloads.custom(4, 2, 128, 16, "bf16", lens, seed=7)
+    print("[gpu] split decode, 3000 sequences", flush=True)
+    st, ref = _oracle(wl)
+    for part in (32, 64, -1):
+        res = run_step(wl, partition_size=part, keep_pool=False)
+        err = _max_err(res, ref, "bf16")
+        print(f"[gpu]   partition {part}: max|err| = {err:.3e}", flush=True)
+        assert err <= TOL["bf16"]
