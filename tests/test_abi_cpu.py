@@ -140,6 +140,8 @@ def test_prefill_rejects_contexts_whose_table_exceeds_lds():
     HIP call (about 364k tokens at block_size 16, head_dim 128)."""
     assert _prefill(_cache(), max_ctx=400000, max_blocks=400000 // 16 + 1) == P.PA_EUNSUPPORTED
     assert _prefill(_cache(block_size=8), max_ctx=200000, max_blocks=200000 // 8 + 1) == P.PA_EUNSUPPORTED
+    # 364,544 tokens (22,784 entries) is the largest accepted at head_dim 128, block_size 16: one more is refused
+    assert _prefill(_cache(), max_ctx=364545, max_blocks=22785) == P.PA_EUNSUPPORTED
 
 
 def test_append_and_copy_validation():

@@ -198,3 +198,38 @@ def test_split_decode_more_sequences_than_planner_threads():
         err = _max_err(res, ref, "bf16")
         print(f"[gpu]   partition {part}: max|err| = {err:.3e}", flush=True)
         assert err <= TOL["bf16"]
+
+
+def test_prefill_at_the_largest_context_its_table_stages():
+    """A chunk of 40 rows at the end of a 364,544-token context, the longest
+    whose block table (22,784 entries at block_size 16) fits in LDS beside
+    the K/V tile buffers at head_dim 128 (one token more is refused).  Queries
+    at 4x scale make each row's softmax peak on a few keys scattered over the
+    whole context, so a mis-staged table entry or a skipped tile changes the
+    output by O(1); V at half scale keeps |out| < 2."""
+    import paged_kv_cache_403_amd as P
+    from paged_kv_cache_403_amd.runtime import PagedKVCache, to_host
+
+    Hq, Hkv, D, BS, L, n = 8, 1, 128, 16, 364544, 40
+    nblk = L // BS
+    print(f"[gpu] prefill at the largest staged table: context {L}, {n} rows", flush=True)
+    g = torch.Generator().manual_seed(4034)
+    k = torch.randn((nblk, Hkv, BS, D), generator=g).to(torch.bfloat16)
+    v = (0.5 * torch.randn((nblk, Hkv, BS, D), generator=g)).to(torch.bfloat16)
+    q = (4.0 * torch.randn((n, Hq, D), generator=g)).to(torch.bfloat16)
+    perm = torch.randperm(nblk, generator=g).to(torch.int32)  # blocks in random physical order
+    tab = perm.numpy()[None, :]
+    cache = PagedKVCache(nblk, Hkv, BS, D, "bf16", "cuda")
+    cache.k.copy_(k)
+    cache.v.copy_(v.transpose(2, 3))
+    scale = 1.0 / np.sqrt(D)
+    ref, _ = A.paged_attention(to_host(q), to_host(k), to_host(v), tab, np.array([L]), np.array([n]), scale, "bf16")
+    out = torch.full((n, Hq, D), 7.0, dtype=torch.bfloat16, device="cuda")
+    P.pa_prefill_chunk(cache.desc, q.to("cuda"), out, torch.tensor([0, n], dtype=torch.int32, device="cuda"),
+                       torch.tensor([L], dtype=torch.int32, device="cuda"), torch.from_numpy(tab).to("cuda"), n, L,
+                       scale)
+    torch.cuda.synchronize()
+    err = float(np.abs(to_f64(to_host(out), "bf16") - ref).max())
+    print(f"[gpu]   max|err| = {err:.3e} (max|ref| = {np.abs(ref).max():.3f})", flush=True)
+    assert np.abs(ref).max() > 0.5  # the peaked softmax keeps the outputs O(1)
+    assert err <= TOL["bf16"]
