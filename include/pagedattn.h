@@ -213,9 +213,10 @@ int pa_decode_grouped(const pa_cache* cache, const void* q, void* out, int32_t n
  *                 cu_q_lens[num_seqs] = total_q
  *   context_lens  device int32 [num_seqs]
  *   max_q_len, max_context_len  host bounds of n_s and context_lens
- * A workgroup stages its sequence's block-table entries in LDS, so contexts
- * whose table does not fit (about 360k tokens at block_size 16, head_dim
- * 128) return PA_EUNSUPPORTED.  With an FP8 pool the codes are widened
+ * A workgroup stages its sequence's block-table entries in LDS beside its
+ * K/V tile buffers (159 KiB in all), so contexts whose table does not fit
+ * return PA_EUNSUPPORTED: the longest accepted is 364,544 tokens at
+ * block_size 16 and head_dim 128.  With an FP8 pool the codes are widened
  * exactly to the activation type as the K/V tiles are staged, and the
  * scales enter in fp32 (k_scale folded into the softmax scale, v_scale into
  * the normalisation); the output is rounded to the activation type. */
