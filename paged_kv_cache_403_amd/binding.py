@@ -159,6 +159,53 @@ def _dev_ptr(t, what: str) -> int | None:
     return _ptr(t)
 
 
+def _act_torch_dtype(cache: pa_cache):
+    """torch dtype of q / out / appended rows for a pool descriptor."""
+    torch = _torch()
+    code = cache.act_dtype if cache.dtype == PA_FP8_E4M3 else cache.dtype
+    return {PA_F32: torch.float32, PA_F16: torch.float16, PA_BF16: torch.bfloat16}.get(code)
+
+
+def _need(t, what: str, dtype=None, shape=None, ndim=None):
+    """Host-side check of a tensor argument before anything is launched: the
+    kernels size every access from the descriptor and the counts, so a
+    tensor of another type or shape would be read or written past its end.
+    Raw integer pointers are passed through unchecked."""
+    if t is None or isinstance(t, int):
+        return
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{what} must be {dtype}, got {t.dtype}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{what} must have {ndim} dimensions, got shape {tuple(t.shape)}")
+    if shape is not None:
+        if t.dim() != len(shape) or any(w is not None and int(g) != int(w) for g, w in zip(t.shape, shape)):
+            want = tuple("*" if w is None else int(w) for w in shape)
+            raise ValueError(f"{what} must have shape {want}, got {tuple(t.shape)}")
+
+
+def _same_device(*ts):
+    devs = {t.device for t in ts if t is not None and not isinstance(t, int)}
+    if len(devs) > 1:
+        raise ValueError(f"tensor arguments on several devices: {sorted(str(d) for d in devs)}")
+
+
+def _check_rows(cache: pa_cache, q, out, what_q="q"):
+    """q and out: [rows][Hq][head_dim] of the pool's activation type."""
+    act = _act_torch_dtype(cache)
+    if isinstance(q, int):
+        return
+    _need(q, what_q, dtype=act, ndim=3)
+    _need(q, what_q, shape=(None, None, cache.head_dim))
+    _need(out, "out", dtype=act, shape=tuple(q.shape))
+
+
+def _check_tables(block_tables, context_lens, num_seqs):
+    torch = _torch()
+    _need(block_tables, "block_tables", dtype=torch.int32, ndim=2)
+    _need(block_tables, "block_tables", shape=(num_seqs, None))
+    _need(context_lens, "context_lens", dtype=torch.int32, shape=(num_seqs,))
+
+
 def _stream(stream, like) -> int | None:
     if stream is not None:
         return int(stream) if isinstance(stream, int) else stream.cuda_stream
@@ -188,7 +235,14 @@ def make_cache(k_cache, v_cache, act_dtype=None, k_scale=1.0, v_scale=1.0) -> pa
 # ---- device entry points ------------------------------------------------------------
 
 def pa_kv_append(cache: pa_cache, k_new, v_new, slot_mapping, stream=None):
+    torch = _torch()
     c = cache
+    _need(slot_mapping, "slot_mapping", dtype=torch.int64, ndim=1)
+    T = int(slot_mapping.shape[0])
+    act = _act_torch_dtype(c)
+    _need(k_new, "k_new", dtype=act, shape=(T, c.num_kv_heads, c.head_dim))
+    _need(v_new, "v_new", dtype=act, shape=(T, c.num_kv_heads, c.head_dim))
+    _same_device(k_new, v_new, slot_mapping)
     rc = lib().pa_kv_append(ctypes.byref(c), _dev_ptr(k_new, "k_new"), _dev_ptr(v_new, "v_new"),
                             _dev_ptr(slot_mapping, "slot_mapping"), int(slot_mapping.shape[0]),
                             _stream(stream, k_new))
@@ -196,6 +250,7 @@ def pa_kv_append(cache: pa_cache, k_new, v_new, slot_mapping, stream=None):
 
 
 def pa_copy_blocks(cache: pa_cache, pairs, stream=None):
+    _need(pairs, "pairs", dtype=_torch().int32, shape=(None, 2))
     n = int(pairs.shape[0])
     rc = lib().pa_copy_blocks(ctypes.byref(cache), _dev_ptr(pairs, "pairs") if n else None, n,
                               _stream(stream, pairs) if n else None)
@@ -212,7 +267,10 @@ def pa_decode_choose_partition(cache: pa_cache, num_seqs, num_q_heads, max_conte
 
 def pa_decode(cache: pa_cache, q, out, block_tables, context_lens, max_context_len, scale, partition_size=0,
               workspace=None, stream=None):
+    _check_rows(cache, q, out)
     num_seqs, num_q_heads = int(q.shape[0]), int(q.shape[1])
+    _check_tables(block_tables, context_lens, num_seqs)
+    _same_device(q, out, block_tables, context_lens, workspace)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     rc = lib().pa_decode(ctypes.byref(cache), _dev_ptr(q, "q"), _dev_ptr(out, "out"), num_seqs, num_q_heads,
                          _dev_ptr(block_tables, "block_tables"), int(block_tables.shape[1]),
@@ -229,7 +287,11 @@ def pa_decode_grouped_workspace_bytes(num_seqs, num_q_heads, head_dim, max_conte
 def pa_decode_grouped(cache: pa_cache, q, out, block_tables, context_lens, max_context_len, scale, group_start,
                       partition_size=0, workspace=None, stream=None):
     """group_start: device int32 [num_groups + 1] (or None for no grouping hint)."""
+    _check_rows(cache, q, out)
     num_seqs, num_q_heads = int(q.shape[0]), int(q.shape[1])
+    _check_tables(block_tables, context_lens, num_seqs)
+    _need(group_start, "group_start", dtype=_torch().int32, ndim=1)
+    _same_device(q, out, block_tables, context_lens, group_start, workspace)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     num_groups = 0 if group_start is None else max(int(group_start.shape[0]) - 1, 0)
     rc = lib().pa_decode_grouped(ctypes.byref(cache), _dev_ptr(q, "q"), _dev_ptr(out, "out"), num_seqs, num_q_heads,
@@ -242,7 +304,11 @@ def pa_decode_grouped(cache: pa_cache, q, out, block_tables, context_lens, max_c
 
 def pa_prefill_chunk(cache: pa_cache, q, out, cu_q_lens, context_lens, block_tables, max_q_len, max_context_len,
                      scale, stream=None):
+    _check_rows(cache, q, out)
     num_seqs = int(context_lens.shape[0])
+    _check_tables(block_tables, context_lens, num_seqs)
+    _need(cu_q_lens, "cu_q_lens", dtype=_torch().int32, shape=(num_seqs + 1,))
+    _same_device(q, out, cu_q_lens, context_lens, block_tables)
     rc = lib().pa_prefill_chunk(ctypes.byref(cache), _dev_ptr(q, "q"), _dev_ptr(out, "out"),
                                 _dev_ptr(cu_q_lens, "cu_q_lens"), _dev_ptr(context_lens, "context_lens"), num_seqs,
                                 int(q.shape[0]), int(q.shape[1]), _dev_ptr(block_tables, "block_tables"),

@@ -200,10 +200,19 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t 
   return workspace_for(num_seqs, num_q_heads, head_dim, parts);
 }
 
-int pa_decode(const pa_cache* cache, const void* q, void* out, int32_t num_seqs, int32_t num_q_heads,
-              const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
-              int32_t max_context_len, float scale, int32_t partition_size, void* workspace, size_t workspace_bytes,
-              void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Everything pa_decode checks and derives before it touches the GPU: the
+// launch arguments (workspace pointers still unset) and the workspace bytes
+// the launch needs (0 for one pass).  *nothing is set when the batch is
+// empty: a valid no-op.
+int decode_prepare(const pa_cache* cache, const void* q, void* out, int32_t num_seqs, int32_t num_q_heads,
+                   const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
+                   int32_t max_context_len, float scale, int32_t partition_size, pa::DecodeArgs* a, size_t* need,
+                   bool* nothing) {
+  *nothing = false;
   int rc = check_cache(cache);
   if (rc != PA_OK) return rc;
   int32_t group = 0;
@@ -215,46 +224,70 @@ int pa_decode(const pa_cache* cache, const void* q, void* out, int32_t num_seqs,
   if (num_seqs > kMaxGridYZ) return PA_EUNSUPPORTED;
   if (partition_size < -1) return PA_EINVAL;
   if (partition_size > 0 && partition_size % cache->block_size != 0) return PA_EINVAL;
-  if (num_seqs == 0) return PA_OK;
+  if (num_seqs == 0) {
+    *nothing = true;
+    return PA_OK;
+  }
   if (!q || !out || !block_tables || !context_lens) return PA_EINVAL;
   const int32_t chosen = pa_decode_choose_partition(cache, num_seqs, num_q_heads, max_context_len);
   const int32_t part_tokens = effective_partition(partition_size, cache->block_size, max_context_len, chosen);
   const int32_t num_parts =
       max_context_len > 0 ? static_cast<int32_t>((static_cast<int64_t>(max_context_len) + part_tokens - 1) / part_tokens)
                           : 1;
-  const size_t need = workspace_for(num_seqs, num_q_heads, cache->head_dim, num_parts);
-  if (need > 0 && (!workspace || workspace_bytes < need)) return PA_EWORKSPACE;
-
-  pa::DecodeArgs a{};
-  a.q = q;
-  a.out = out;
-  a.k_cache = cache->k_cache;
-  a.v_cache = cache->v_cache;
-  a.block_tables = block_tables;
-  a.context_lens = context_lens;
-  a.ws_ml = need > 0 ? static_cast<float*>(workspace) : nullptr;
-  a.ws_o = need > 0 ? a.ws_ml + static_cast<int64_t>(num_seqs) * num_q_heads * num_parts * 2 : nullptr;
-  a.ws_items = need > 0 ? reinterpret_cast<int32_t*>(a.ws_o + static_cast<int64_t>(num_seqs) * num_q_heads * num_parts *
-                                                                 cache->head_dim)
-                        : nullptr;
-  a.ws_count = need > 0 ? a.ws_items + static_cast<int64_t>(num_seqs) * num_parts * 2 : nullptr;
-  a.scale = scale;
+  *need = workspace_for(num_seqs, num_q_heads, cache->head_dim, num_parts);
+  *a = pa::DecodeArgs{};
+  a->q = q;
+  a->out = out;
+  a->k_cache = cache->k_cache;
+  a->v_cache = cache->v_cache;
+  a->block_tables = block_tables;
+  a->context_lens = context_lens;
+  a->scale = scale;
   if (is_fp8(cache)) {
-    a.k_scale = cache->k_scale;
-    a.v_scale = cache->v_scale;
+    a->k_scale = cache->k_scale;
+    a->v_scale = cache->v_scale;
   }
-  a.dtype = cache->dtype;
-  a.act_dtype = act_dtype(cache);
-  a.head_dim = cache->head_dim;
-  a.block_size = cache->block_size;
-  a.group = group;
-  a.num_seqs = num_seqs;
-  a.num_kv_heads = cache->num_kv_heads;
-  a.num_blocks = cache->num_blocks;
-  a.max_blocks_per_seq = max_blocks_per_seq;
-  a.max_context_len = max_context_len;
-  a.part_tokens = part_tokens;
-  a.num_parts = num_parts;
+  a->dtype = cache->dtype;
+  a->act_dtype = act_dtype(cache);
+  a->head_dim = cache->head_dim;
+  a->block_size = cache->block_size;
+  a->group = group;
+  a->num_seqs = num_seqs;
+  a->num_kv_heads = cache->num_kv_heads;
+  a->num_blocks = cache->num_blocks;
+  a->max_blocks_per_seq = max_blocks_per_seq;
+  a->max_context_len = max_context_len;
+  a->part_tokens = part_tokens;
+  a->num_parts = num_parts;
+  return PA_OK;
+}
+
+// Split-K partials [S][Hq][P][2] and [S][Hq][P][D] (fp32), then the work list
+// and its length, carved out of `workspace` (need > 0 only).
+void decode_carve(pa::DecodeArgs* a, void* workspace, int32_t num_q_heads) {
+  const int64_t rows = static_cast<int64_t>(a->num_seqs) * num_q_heads * a->num_parts;
+  a->ws_ml = static_cast<float*>(workspace);
+  a->ws_o = a->ws_ml + rows * 2;
+  a->ws_items = reinterpret_cast<int32_t*>(a->ws_o + rows * a->head_dim);
+  a->ws_count = a->ws_items + static_cast<int64_t>(a->num_seqs) * a->num_parts * 2;
+}
+
+}  // namespace
+
+extern "C" {
+
+int pa_decode(const pa_cache* cache, const void* q, void* out, int32_t num_seqs, int32_t num_q_heads,
+              const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
+              int32_t max_context_len, float scale, int32_t partition_size, void* workspace, size_t workspace_bytes,
+              void* stream) {
+  pa::DecodeArgs a{};
+  size_t need = 0;
+  bool nothing = false;
+  int rc = decode_prepare(cache, q, out, num_seqs, num_q_heads, block_tables, max_blocks_per_seq, context_lens,
+                          max_context_len, scale, partition_size, &a, &need, &nothing);
+  if (rc != PA_OK || nothing) return rc;
+  if (need > 0 && (!workspace || workspace_bytes < need)) return PA_EWORKSPACE;
+  if (need > 0) decode_carve(&a, workspace, num_q_heads);
   return hip_status(pa::launch_decode(a, static_cast<hipStream_t>(stream)));
 }
 
@@ -382,3 +415,4 @@ int pa_decode_grouped(const pa_cache* cache, const void* q, void* out, int32_t n
 }
 
 }  // extern "C"
+

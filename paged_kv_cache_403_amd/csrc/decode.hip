@@ -100,33 +100,63 @@ __global__ __launch_bounds__(kThreads) void decode_persistent_kernel(DecodeParam
 // zero output), largest first.  The persistent grid deals the list out round
 // robin, so putting the full partitions first and the short last ones after
 // them in falling size leaves short items for the end -- the same
-// longest-first rule as the one-pass grid.  A counting sort over kPlanBuckets
-// size classes of part_tokens / kPlanBuckets tokens (order inside a class is
-// whatever the atomics give; each pair is computed the same way wherever it
-// lands).
+// longest-first rule as the one-pass grid.  The full partitions come first in
+// sequence order; each sequence's last partition then goes into one of
+// kPlanBuckets size classes of part_tokens / kPlanBuckets tokens (a counting
+// sort; order inside a class is whatever the atomics give -- each pair is
+// computed the same way wherever it lands).  Every thread works: the full
+// partitions of kPlanThreads sequences at a time are laid out by a workgroup
+// prefix sum and written one pair per thread, so a few very long contexts
+// (hundreds of partitions each) do not leave a few threads writing them in
+// turn.
 constexpr int kPlanThreads = 1024;
+constexpr int kPlanWaves = kPlanThreads / 64;
 constexpr int kPlanBuckets = 32;
+
+// Inclusive prefix sum of x over the workgroup's kPlanThreads threads
+// (wsum: kPlanWaves ints of LDS, free again when this returns).
+__device__ __forceinline__ int plan_inclusive_scan(int x, int* wsum) {
+  const int lane = lane_id(), w = threadIdx.x >> 6;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) wsum[w] = x;
+  __syncthreads();
+  int add = 0;
+  for (int i = 0; i < w; ++i) add += wsum[i];
+  __syncthreads();
+  return x + add;
+}
 
 __global__ __launch_bounds__(kPlanThreads) void decode_plan_kernel(const int32_t* __restrict__ ctx_lens, int num_seqs,
                                                                    int max_context, int part_tokens,
                                                                    int32_t* __restrict__ items,
                                                                    int32_t* __restrict__ n_items) {
-  __shared__ int count[kPlanBuckets];
+  __shared__ int count[kPlanBuckets];  // last partitions per size class
   __shared__ int start[kPlanBuckets];
+  __shared__ int wsum[kPlanWaves];
+  __shared__ int incl[kPlanThreads];
+  __shared__ int nfull;
   const int tid = threadIdx.x;
   // size class of a partition of t tokens (t = 0 only for an empty sequence)
   auto bucket = [&](int t) { return t <= 0 ? 0 : static_cast<int>((static_cast<int64_t>(t - 1) * kPlanBuckets) / part_tokens); };
+  auto parts_of = [&](int L) { return L == 0 ? 1 : (L + part_tokens - 1) / part_tokens; };
   if (tid < kPlanBuckets) count[tid] = 0;
+  if (tid == 0) nfull = 0;
   __syncthreads();
+  int my_full = 0;
   for (int s = tid; s < num_seqs; s += kPlanThreads) {
     const int L = clamp_len(ctx_lens[s], max_context);
-    const int np = L == 0 ? 1 : (L + part_tokens - 1) / part_tokens;
-    if (np > 1) atomicAdd(&count[kPlanBuckets - 1], np - 1);
+    const int np = parts_of(L);
+    my_full += np - 1;
     atomicAdd(&count[bucket(L - (np - 1) * part_tokens)], 1);
   }
+  if (my_full) atomicAdd(&nfull, my_full);
   __syncthreads();
   if (tid == 0) {
-    int acc = 0;
+    int acc = nfull;  // the full partitions take [0, nfull)
     for (int k = kPlanBuckets - 1; k >= 0; --k) {
       start[k] = acc;
       acc += count[k];
@@ -134,16 +164,32 @@ __global__ __launch_bounds__(kPlanThreads) void decode_plan_kernel(const int32_t
     *n_items = acc;
   }
   __syncthreads();
+  // full partitions: sequence order, each sequence's partitions in order
+  int base = 0;
+  for (int c0 = 0; c0 < num_seqs; c0 += kPlanThreads) {
+    const int s = c0 + tid;
+    const int f = s < num_seqs ? parts_of(clamp_len(ctx_lens[s], max_context)) - 1 : 0;
+    incl[tid] = plan_inclusive_scan(f, wsum);
+    __syncthreads();
+    const int total = incl[kPlanThreads - 1];
+    for (int i = tid; i < total; i += kPlanThreads) {
+      int lo = 0, hi = kPlanThreads - 1;  // the first thread whose inclusive sum passes i
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (incl[mid] > i) hi = mid;
+        else lo = mid + 1;
+      }
+      const int first = lo == 0 ? 0 : incl[lo - 1];
+      items[2 * (base + i)] = c0 + lo;
+      items[2 * (base + i) + 1] = i - first;
+    }
+    base += total;
+    __syncthreads();  // incl is rewritten by the next chunk
+  }
+  // last partitions, by size class
   for (int s = tid; s < num_seqs; s += kPlanThreads) {
     const int L = clamp_len(ctx_lens[s], max_context);
-    const int np = L == 0 ? 1 : (L + part_tokens - 1) / part_tokens;
-    if (np > 1) {
-      const int first = atomicAdd(&start[kPlanBuckets - 1], np - 1);
-      for (int p = 0; p < np - 1; ++p) {
-        items[2 * (first + p)] = s;
-        items[2 * (first + p) + 1] = p;
-      }
-    }
+    const int np = parts_of(L);
     const int at = atomicAdd(&start[bucket(L - (np - 1) * part_tokens)], 1);
     items[2 * at] = s;
     items[2 * at + 1] = np - 1;
@@ -151,38 +197,79 @@ __global__ __launch_bounds__(kPlanThreads) void decode_plan_kernel(const int32_t
 }
 
 // Log-sum-exp merge of the partitions of one (sequence, q head); ST is the
-// output type.
+// output type.  M = max_p m_p, w_p = l_p 2^(m_p - M), out = sum_p w_p o_p /
+// sum_p w_p (partials hold normalised o_p and m in log2 units).  Each thread
+// takes 4 consecutive elements of the row (one 16-byte load per partition),
+// and the workgroup's kRedThreads / (D / 4) partition slots take the
+// partitions round robin, so many loads are in flight even for a few rows
+// with hundreds of partitions; the slots' sums are added in slot order at the
+// end (the same order on every run).  No LDS grows with the partition count.
+constexpr int kRedThreads = 256;
 template <typename ST, int D>
-__global__ __launch_bounds__(D) void decode_reduce_kernel(const float* __restrict__ ws_ml,
-                                                          const float* __restrict__ ws_o,
-                                                          const int32_t* __restrict__ ctx_lens, int max_context,
-                                                          int part_tokens, int max_parts, int num_q_heads,
-                                                          typename ST::elem* __restrict__ out) {
-  extern __shared__ float w_sh[];  // [max_parts]
-  __shared__ float M_sh;
-  const int h = blockIdx.x, s = blockIdx.y, d = threadIdx.x;
+__global__ __launch_bounds__(kRedThreads) void decode_reduce_kernel(const float* __restrict__ ws_ml,
+                                                                    const float* __restrict__ ws_o,
+                                                                    const int32_t* __restrict__ ctx_lens,
+                                                                    int max_context, int part_tokens, int max_parts,
+                                                                    int num_q_heads,
+                                                                    typename ST::elem* __restrict__ out) {
+  constexpr int LPP = D / 4;                // threads per partition row
+  constexpr int SLOTS = kRedThreads / LPP;  // partitions taken at once
+  __shared__ float wmax[kRedThreads / 64];
+  __shared__ float4 slot_num[SLOTS][LPP];
+  __shared__ float slot_den[SLOTS];
+  const int h = blockIdx.x, s = blockIdx.y, tid = threadIdx.x;
   const int L = clamp_len(ctx_lens[s], max_context);
   const int np = (L + part_tokens - 1) / part_tokens;
   if (np <= 1) return;  // written directly by the decode kernel
   const int64_t qh = static_cast<int64_t>(s) * num_q_heads + h;
   const float* ml = ws_ml + 2 * qh * max_parts;
-  if (d == 0) {
-    float M = -INFINITY;
-    for (int p = 0; p < np; ++p) M = fmaxf(M, ml[2 * p]);
-    M_sh = M;
-  }
+  float M = -INFINITY;
+  for (int p = tid; p < np; p += kRedThreads) M = fmaxf(M, ml[2 * p]);
+  M = fmaxf(M, xor_lane<1>(M));
+  M = fmaxf(M, xor_lane<2>(M));
+  M = fmaxf(M, xor_lane<4>(M));
+  M = fmaxf(M, xor_lane<8>(M));
+  M = fmaxf(M, xor_lane<16>(M));
+  M = fmaxf(M, xor_lane<32>(M));
+  if (lane_id() == 0) wmax[tid >> 6] = M;
   __syncthreads();
-  const float M = M_sh;
-  for (int p = d; p < np; p += D) w_sh[p] = ml[2 * p + 1] * __builtin_amdgcn_exp2f(ml[2 * p] - M);
-  __syncthreads();
-  const float* o = ws_o + qh * max_parts * D + d;
-  float num = 0.f, den = 0.f;
-  for (int p = 0; p < np; ++p) {
-    const float w = w_sh[p];
-    num = __builtin_fmaf(w, o[static_cast<int64_t>(p) * D], num);
+#pragma unroll
+  for (int w = 0; w < kRedThreads / 64; ++w) M = fmaxf(M, wmax[w]);
+  const int slot = tid / LPP, c = tid % LPP;
+  const float* o = ws_o + qh * max_parts * D + c * 4;
+  float4 num = {0.f, 0.f, 0.f, 0.f};
+  float den = 0.f;
+#pragma unroll 8
+  for (int p = slot; p < np; p += SLOTS) {
+    const float w = ml[2 * p + 1] * __builtin_amdgcn_exp2f(ml[2 * p] - M);
+    const float4 v = *reinterpret_cast<const float4*>(o + static_cast<int64_t>(p) * D);
+    num.x = __builtin_fmaf(w, v.x, num.x);
+    num.y = __builtin_fmaf(w, v.y, num.y);
+    num.z = __builtin_fmaf(w, v.z, num.z);
+    num.w = __builtin_fmaf(w, v.w, num.w);
     den += w;
   }
-  out[qh * D + d] = narrow<ST>(num / den);
+  slot_num[slot][c] = num;
+  if (c == 0) slot_den[slot] = den;
+  __syncthreads();
+  if (tid < LPP) {
+    float4 n = slot_num[0][tid];
+    float d = slot_den[0];
+#pragma unroll
+    for (int k = 1; k < SLOTS; ++k) {
+      const float4 x = slot_num[k][tid];
+      n.x += x.x;
+      n.y += x.y;
+      n.z += x.z;
+      n.w += x.w;
+      d += slot_den[k];
+    }
+    typename ST::elem* dst = out + qh * D + tid * 4;
+    dst[0] = narrow<ST>(n.x / d);
+    dst[1] = narrow<ST>(n.y / d);
+    dst[2] = narrow<ST>(n.z / d);
+    dst[3] = narrow<ST>(n.w / d);
+  }
 }
 
 // Workgroups of the persistent kernel: as many as fit on the device at once
@@ -243,8 +330,8 @@ hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t st) {
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int num_q_heads = a.num_kv_heads * G;
-  hipLaunchKernelGGL((decode_reduce_kernel<AT, D>), dim3(num_q_heads, a.num_seqs), dim3(D),
-                     a.num_parts * sizeof(float), st, a.ws_ml, a.ws_o, a.context_lens,
+  hipLaunchKernelGGL((decode_reduce_kernel<AT, D>), dim3(num_q_heads, a.num_seqs), dim3(kRedThreads), 0, st,
+                     a.ws_ml, a.ws_o, a.context_lens,
                      a.max_context_len, a.part_tokens, a.num_parts, num_q_heads,
                      static_cast<typename AT::elem*>(a.out));
   return hipGetLastError();

@@ -355,3 +355,4 @@ def test_workload_slot_mapping_bit_exact(name, reduced):
     assert np.array_equal(lens, ref.context_lens)
     if name == "gqa_shared_prefix":
         assert len(pairs) > 0  # the shared-prefix workload does exercise copy-on-write
+

@@ -12,6 +12,7 @@ import pytest
 import torch
 
 import workloads
+from fullsize_check import check_rows
 from gpu_harness import TOL, run_step
 from oracle import attention as A
 from oracle.cache import run_workload
@@ -75,26 +76,16 @@ def test_fp8_nan_codes_in_unused_slots_do_not_leak():
     assert np.array_equal(a.out, b.out)
 
 
-def test_fp8_fullsize_sampled():
+def test_fp8_fullsize_all_rows():
     """The 7B-shaped MHA decode batch at full size with an FP8 pool, in the
-    launch configuration bench.py times: sampled rows against attention over
-    the quantised logical K/V (fp64)."""
+    launch configuration bench.py times: every row (all q heads) against
+    attention over the quantised logical K/V (fp64)."""
     wl = workloads.with_fp8_kv(workloads.make("mha_decode_7b"))
     sp = wl.spec
     print("[gpu] fp8 full size mha_decode_7b", flush=True)
     res = run_step(wl, partition_size=-1, keep_pool=False)
-    rng = np.random.default_rng(8)
-    worst = 0.0
-    for r in sorted(set(int(x) for x in rng.integers(0, len(wl.batch), size=12))):
-        p = wl.batch[r]
-        h = int(rng.integers(sp.num_q_heads))
-        K, V = wl.logical_kv(p.seq_id)
-        kq, vq = kv_encode(K[:, h], sp.dtype, sp.k_scale), kv_encode(V[:, h], sp.dtype, sp.v_scale)
-        ref = A.attention_rows(wl.q[p.seq_id][0:1, h], kq, vq, [p.context_len - 1], sp.scale, sp.dtype, sp.kv)[0]
-        err = float(np.abs(to_f64(res.out[r, h], sp.dtype) - ref).max())
-        worst = max(worst, err)
-        assert err <= TOL[sp.dtype], (r, h, err)
-    print(f"[gpu]   sampled max|err| = {worst:.3e}", flush=True)
+    worst, n, where = check_rows(wl, res.out, TOL[sp.dtype])
+    print(f"[gpu]   {n} rows, max|err| = {worst:.3e} at {where}", flush=True)
 
 
 def test_fp8_mixed_prefill_reduced_parity():
@@ -141,32 +132,14 @@ def test_fp8_prefill_nan_codes_in_unused_slots_do_not_leak():
     assert np.array_equal(a.out, b.out)
 
 
-def test_fp8_mixed_fullsize_sampled():
+def test_fp8_mixed_fullsize_all_rows():
     """The mixed chunked-prefill step at full size on an FP8 pool, in the
-    launch configuration bench.py times: the first and last row of every
-    chunk and sampled decode rows against attention over the quantised
-    logical K/V (fp64)."""
+    launch configuration bench.py times: every chunk row and every decode
+    row (all q heads) against attention over the quantised logical K/V
+    (fp64)."""
     wl = workloads.with_fp8_kv(workloads.make("mixed_chunked_prefill"))
     sp = wl.spec
     print("[gpu] fp8 full size mixed_chunked_prefill", flush=True)
     res = run_step(wl, partition_size=-1, keep_pool=False)
-    rng = np.random.default_rng(9)
-    starts = np.concatenate([[0], np.cumsum([p.n_new for p in wl.batch])])
-    picks = []
-    for r, p in enumerate(wl.batch):
-        if p.n_new > 1:
-            picks += [(r, 0), (r, p.n_new - 1)]
-    picks += [(int(r), 0) for r in rng.integers(8, len(wl.batch), size=6)]
-    worst = 0.0
-    for r, i in sorted(set(picks)):
-        p = wl.batch[r]
-        h = int(rng.integers(sp.num_q_heads))
-        g = h // (sp.num_q_heads // sp.num_kv_heads)
-        K, V = wl.logical_kv(p.seq_id)
-        kq, vq = kv_encode(K[:, g], sp.dtype, sp.k_scale), kv_encode(V[:, g], sp.dtype, sp.v_scale)
-        a = p.context_len - p.n_new + i
-        ref = A.attention_rows(wl.q[p.seq_id][i:i + 1, h], kq, vq, [a], sp.scale, sp.dtype, sp.kv)[0]
-        err = float(np.abs(to_f64(res.out[starts[r] + i, h], sp.dtype) - ref).max())
-        worst = max(worst, err)
-        assert err <= TOL[sp.dtype], (r, i, h, err)
-    print(f"[gpu]   sampled max|err| = {worst:.3e}", flush=True)
+    worst, n, where = check_rows(wl, res.out, TOL[sp.dtype])
+    print(f"[gpu]   {n} rows, max|err| = {worst:.3e} at {where}", flush=True)

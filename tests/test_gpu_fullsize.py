@@ -1,88 +1,60 @@
-"""GPU parity at the full sizes of the five workloads, in the launch
-configuration bench.py times (decode partition chosen by the library).
+"""GPU parity at the full sizes of the five workloads, in every launch
+configuration bench.py times: the library's decode partition choice for
+each workload, and the long-context batch again at its stated 512-token
+partitions (256 partitions per row, so the log-sum-exp merge walks more
+partitions than it has threads).
 
 Bit-exact: the step's slot mapping, copy-on-write pairs, block tables and
 context lengths against the oracle's bookkeeping, and the pool contents at
-sampled positions of every sampled sequence (read back through the GPU's
-own tables) against the workload's logical K/V.  Within tolerance: sampled
-output rows against the plain definition -- attention of the row over its
-sequence's logical K/V, fp64 -- which the oracle pins elsewhere to equal the
-gather through the tables (tests/test_oracle_attention.py).  The full
-outputs of these sizes are too large for the fp64 oracle one by one, so
-rows are sampled with a fixed seed; the longest sequence and the first and
-last rows of every chunk are always included.
+sampled positions of every sequence (read back through the GPU's own
+tables) against the workload's logical K/V.  Within tolerance: every output
+row of the step (every q head of every decode row and of every chunk row)
+against the plain definition -- attention of the row over its sequence's
+logical K/V in fp64 -- which the oracle pins elsewhere to equal the gather
+through the tables (tests/test_oracle_attention.py).
 """
 import numpy as np
 import pytest
 import torch
 
 import workloads
+from fullsize_check import check_rows
 from gpu_harness import TOL, run_step
-from oracle import attention as A
 from oracle.cache import run_workload
-from oracle.storage import to_f64
 from paged_kv_cache_403_amd.runtime import to_host
 
 pytestmark = pytest.mark.gpu
 
-SAMPLE_ROWS = 24
+CASES = [(name, -1) for name in workloads.CONFIG_NAMES] + [("long_splitk_decode", 512)]
 
 
-def _samples(wl, rng):
-    """(batch index, row within the sequence, q head) triples."""
+def _check_pool(wl, res, rng):
     sp = wl.spec
-    batch = wl.batch
-    lens = np.array([p.context_len for p in batch])
-    out = set()
-    longest = int(np.argmax(lens))
-    out.add((longest, batch[longest].n_new - 1, int(rng.integers(sp.num_q_heads))))
-    for r, p in enumerate(batch):
-        if p.n_new > 1:  # a chunk: its first and last row
-            out.add((r, 0, int(rng.integers(sp.num_q_heads))))
-            out.add((r, p.n_new - 1, int(rng.integers(sp.num_q_heads))))
-    while len(out) < min(SAMPLE_ROWS, sum(p.n_new for p in batch) * sp.num_q_heads):
-        r = int(rng.integers(len(batch)))
-        out.add((r, int(rng.integers(batch[r].n_new)), int(rng.integers(sp.num_q_heads))))
-    return sorted(out)
+    kc, vc = res.cache.k, res.cache.v
+    for r, p in enumerate(wl.batch):
+        K, V = wl.logical_kv(p.seq_id)
+        L = p.context_len
+        pos = np.unique(np.concatenate([rng.integers(0, L, size=8), [L - 1, 0]]))
+        blk = torch.from_numpy(res.tables[r][pos // sp.block_size].astype(np.int64)).to(kc.device)
+        off = torch.from_numpy((pos % sp.block_size).astype(np.int64)).to(kc.device)
+        assert np.array_equal(to_host(kc[blk, :, off, :]), K[pos]), (sp.name, r)
+        assert np.array_equal(to_host(vc[blk, :, :, off]), V[pos]), (sp.name, r)
 
 
-@pytest.mark.parametrize("name", workloads.CONFIG_NAMES)
-def test_fullsize_sampled_parity(name):
-    print(f"[gpu] full size {name}", flush=True)
+@pytest.mark.parametrize("name,part", CASES)
+def test_fullsize_parity(name, part):
+    print(f"[gpu] full size {name} partition {part}", flush=True)
     wl = workloads.make(name)
     sp = wl.spec
     st = run_workload(wl, with_pool=False)  # oracle bookkeeping only
-    res = run_step(wl, partition_size=-1, keep_pool=False, return_cache=True)
+    res = run_step(wl, partition_size=part, keep_pool=False, return_cache=True)
     assert np.array_equal(res.setup_slots, st.setup_slots)
     assert np.array_equal(res.slots, st.slot_mapping)
     assert np.array_equal(res.pairs.reshape(-1, 2), st.cow_pairs)
     assert np.array_equal(res.tables, st.tables)
     assert np.array_equal(res.lens, st.context_lens)
-
     rng = np.random.default_rng(20261202)
-    batch = wl.batch
-    starts = np.concatenate([[0], np.cumsum([p.n_new for p in batch])])
-    G = sp.num_q_heads // sp.num_kv_heads
-    kc, vc = res.cache.k, res.cache.v
-    worst = 0.0
-    for r, i, h in _samples(wl, rng):
-        p = batch[r]
-        K, V = wl.logical_kv(p.seq_id)  # [L][Hkv][D] storage values
-        L = p.context_len
-        # pool contents through the GPU's table, at sampled positions
-        pos = np.unique(np.concatenate([rng.integers(0, L, size=8), [L - 1, 0]]))
-        blk = torch.from_numpy(res.tables[r][pos // sp.block_size].astype(np.int64)).to(kc.device)
-        off = torch.from_numpy((pos % sp.block_size).astype(np.int64)).to(kc.device)
-        kg = kc[blk, :, off, :]  # [n][Hkv][D]
-        vg = vc[blk, :, :, off]
-        assert np.array_equal(to_host(kg), K[pos]), (name, r)
-        assert np.array_equal(to_host(vg), V[pos]), (name, r)
-        # output row against the definition on the logical sequence
-        g = h // G
-        a = L - p.n_new + i
-        ref = A.attention_rows(wl.q[p.seq_id][i:i + 1, h], K[:, g], V[:, g], [a], sp.scale, sp.dtype)[0]
-        got = to_f64(res.out[starts[r] + i, h], sp.dtype)
-        err = float(np.abs(got - ref).max())
-        worst = max(worst, err)
-        assert err <= TOL[sp.dtype], (name, r, i, h, err)
-    print(f"[gpu]   {name}: sampled max|err| = {worst:.3e} (tol {TOL[sp.dtype]})", flush=True)
+    _check_pool(wl, res, rng)
+    worst, n, where = check_rows(wl, res.out, TOL[sp.dtype])
+    print(f"[gpu]   {name}: {n} rows (all), max|err| = {worst:.3e} at (row, token, head, |ref|) {where} "
+          f"(tol {TOL[sp.dtype]})", flush=True)

@@ -64,12 +64,16 @@ def test_reduced_config_parity(name):
     assert err <= TOL[wl.spec.dtype]
 
 
-@pytest.mark.parametrize("name", ["tiny_decode", "mha_decode_7b", "gqa_shared_prefix", "long_splitk_decode"])
-@pytest.mark.parametrize("part", [0, 16, 32, 64, 512, -1])
+# partitions must be a multiple of the block size (32 for the long-context
+# workload; other sizes are refused before any launch, tested on the CPU)
+_PART_CASES = [(name, part) for name in ("tiny_decode", "mha_decode_7b", "gqa_shared_prefix", "long_splitk_decode")
+               for part in (0, 16, 32, 64, 512, -1)
+               if part <= 0 or part % (32 if name == "long_splitk_decode" else 16) == 0]
+
+
+@pytest.mark.parametrize("name,part", _PART_CASES)
 def test_decode_partition_sizes(name, part):
     wl = workloads.make(name, reduced=True)
-    if part > 0 and part % wl.spec.block_size:
-        pytest.skip("partition not a multiple of block_size")
     print(f"[gpu] partitions {name} part={part}", flush=True)
     st, ref = _oracle(wl)
     res = run_step(wl, partition_size=part, keep_pool=False)
@@ -290,3 +294,24 @@ def test_calls_from_two_host_threads_on_their_own_streams():
         od, op = results[name]
         assert np.array_equal(od, res.out[starts[dec]]), name
         assert np.array_equal(op, res.out[rows]), name
+
+
+MERGE_CASES = [  # (Hq, Hkv, D, BS, dtype, context lengths, partition tokens)
+    (32, 8, 128, 32, "bf16", [5000, 4999, 37, 1], 32),  # 157 partitions: two passes of 128 merge threads
+    (8, 2, 64, 16, "f16", [5000, 3001, 16], 16),  # 313 partitions: five passes of 64 merge threads
+]
+
+
+@pytest.mark.parametrize("case", MERGE_CASES)
+def test_merge_of_more_partitions_than_threads(case):
+    """The log-sum-exp merge over more partitions per row than the merge
+    workgroup has threads (one per head_dim element), every row against the
+    oracle."""
+    hq, hkv, d, bs, dt, lens, part = case
+    wl = workloads.custom(hq, hkv, d, bs, dt, lens, seed=len(lens) * 31 + d)
+    print(f"[gpu] merge of {-(-max(lens) // part)} partitions, shape {case[:5]}", flush=True)
+    st, ref = _oracle(wl)
+    res = run_step(wl, partition_size=part, keep_pool=False)
+    err = _max_err(res, ref, dt)
+    print(f"[gpu]   max|err| = {err:.3e}", flush=True)
+    assert err <= TOL[dt]

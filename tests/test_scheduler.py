@@ -52,11 +52,22 @@ def test_library_schedule_matches_reference(case):
         assert x == y, f"iteration {i}"
 
 
+def _pool_state(bm, nb, lib):
+    """(free blocks, blocks with a reference) of either block manager."""
+    if lib:
+        return bm.num_free(), sum(bm.refcount(b) > 0 for b in range(nb))
+    return len(bm.free), sum(bm.ref.get(b, 0) > 0 for b in range(nb))
+
+
+@pytest.mark.parametrize("lib", [True, False], ids=["library", "oracle"])
 @pytest.mark.parametrize("case", CASES)
-def test_schedule_invariants(case):
+def test_schedule_invariants(case, lib):
+    """Invariants every schedule must keep, on the library's loop and on the
+    oracle's own loop (so the reference is pinned by more than its equality
+    with the library)."""
     n, seed, nb, bs, budget, mr = case
     trace = workloads.arrival_trace(n, seed=seed, max_prompt=min(1500, nb * bs // 4))
-    steps, bm = _run(trace, nb, bs, budget, mr, lib=True)
+    steps, bm = _run(trace, nb, bs, budget, mr, lib=lib)
     prompt = {rid: p for _, rid, p, _ in trace}
     new = {rid: m for _, rid, _, m in trace}
     cached, generated, finished = {}, {}, []
@@ -81,7 +92,8 @@ def test_schedule_invariants(case):
             finished.append(rid)
     assert sorted(finished) == sorted(prompt)
     # every block is back in the pool once the last finished request is freed
-    assert bm.num_free() + sum(bm.refcount(b) > 0 for b in range(nb)) == nb
+    free, held = _pool_state(bm, nb, lib)
+    assert free + held == nb
 
 
 def test_scheduler_abi_errors():
