@@ -16,7 +16,9 @@
  * Conventions for every call
  *  - Pointers marked "device" are HIP device (or managed) memory; "host"
  *    pointers are ordinary CPU memory.  The caller owns every buffer; the
- *    library keeps no pointer after a call returns and allocates nothing.
+ *    library keeps no caller pointer after a call returns and allocates
+ *    nothing (pa_decode_noalloc's fixed scratch array, below, is part of the
+ *    library's code object).
  *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).
  *    Device calls are asynchronous on that stream; a call returns once its
  *    kernels are enqueued.  Calls hold no global state and may be issued
@@ -162,6 +164,25 @@ int pa_decode(const pa_cache* cache, const void* q, void* out, int32_t num_seqs,
 int32_t pa_decode_choose_partition(const pa_cache* cache, int32_t num_seqs, int32_t num_q_heads,
                                    int32_t max_context_len);
 
+/* pa_decode for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation): the
+ * same arguments, kernels and result as pa_decode, but no workspace
+ * argument -- a split keeps its partial states and work list in a fixed
+ * device array of 32 MiB (33554432 bytes) inside the library.  Each device
+ * the library runs on holds its own copy of that array from the first call
+ * on it until the process ends; the call itself allocates nothing.
+ *   stream  must belong to the current device (else PA_EINVAL)
+ * A split whose pa_decode workspace would exceed the array returns
+ * PA_EWORKSPACE before anything is enqueued (pa_last_error() then states
+ * the bytes needed and the limit); one-pass decodes need no scratch.  Every
+ * call on a device shares that device's array and leaves its contents
+ * behind: calls that overlap on one device (several streams, or several
+ * host threads) race and must be ordered by the caller.  Nothing in the
+ * array has to start at zero. */
+int pa_decode_noalloc(const pa_cache* cache, const void* q, void* out, int32_t num_seqs, int32_t num_q_heads,
+                      const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
+                      int32_t max_context_len, float scale, int32_t partition_size, void* stream);
+
 /* Bytes of device workspace pa_decode_grouped needs (partition_size as
  * passed to it; 0 = the default, sized for the smaller default of 8-token
  * blocks, so it covers every block size). */
@@ -227,8 +248,9 @@ int pa_prefill_chunk(const pa_cache* cache, const void* q, void* out, const int3
 
 const char* pa_status_str(int status);
 
-/* HIP's text for the calling thread's most recent PA_EHIP ("" if none);
- * the string is static, owned by the HIP runtime. */
+/* HIP's text for the calling thread's most recent PA_EHIP, or the reason of
+ * pa_decode_noalloc's most recent refusal ("" if none); valid until the
+ * thread's next call into the library. */
 const char* pa_last_error(void);
 
 /* ---- host block manager (CPU only, no HIP calls) -------------------------

@@ -8,6 +8,7 @@ manager.  There is no CPU path: every computation runs in the library.
 from .binding import (  # noqa: F401
     PA_BF16, PA_FP8_E4M3, PA_EHIP, PA_EINVAL, PA_ENOMEM, PA_EUNSUPPORTED, PA_EWORKSPACE, PA_F16, PA_F32, PA_OK,
     BlockManager, PagedAttnError, Scheduler, lib, make_cache, pa_cache, pa_copy_blocks, pa_decode,
-    pa_decode_choose_partition, pa_decode_grouped, pa_decode_grouped_workspace_bytes, pa_decode_workspace_bytes,
+    pa_decode_choose_partition, pa_decode_grouped, pa_decode_grouped_workspace_bytes, pa_decode_noalloc,
+    pa_decode_workspace_bytes,
     pa_kv_append, pa_prefill_chunk, status_str,
 )

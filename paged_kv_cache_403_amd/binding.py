@@ -24,8 +24,9 @@ class PagedAttnError(RuntimeError):
     def __init__(self, status: int, where: str):
         self.status = status
         detail = ""
-        if status == PA_EHIP:
-            detail = f": {lib().pa_last_error().decode()}"
+        if status == PA_EHIP or where == "pa_decode_noalloc":
+            text = lib().pa_last_error().decode()
+            detail = f": {text}" if text else ""
         super().__init__(f"{where}: {status_str(status)} (status {status}){detail}")
 
 
@@ -57,6 +58,8 @@ _SIGNATURES = {
     "pa_decode": (ctypes.c_int, [_cp, _vp, _vp, _i32, _i32, _vp, _i32, _vp, _i32, ctypes.c_float, _i32, _vp,
                                  ctypes.c_size_t, _vp]),
     "pa_decode_choose_partition": (_i32, [_cp, _i32, _i32, _i32]),
+    "pa_decode_noalloc": (ctypes.c_int, [_cp, _vp, _vp, _i32, _i32, _vp, _i32, _vp, _i32, ctypes.c_float, _i32,
+                                         _vp]),
     "pa_decode_grouped_workspace_bytes": (ctypes.c_size_t, [_i32, _i32, _i32, _i32, _i32]),
     "pa_decode_grouped": (ctypes.c_int, [_cp, _vp, _vp, _i32, _i32, _vp, _i32, _vp, _i32, ctypes.c_float, _vp, _i32,
                                          _i32, _vp, ctypes.c_size_t, _vp]),
@@ -277,6 +280,21 @@ def pa_decode(cache: pa_cache, q, out, block_tables, context_lens, max_context_l
                          _dev_ptr(context_lens, "context_lens"), int(max_context_len), float(scale),
                          int(partition_size), _dev_ptr(workspace, "workspace"), ws_bytes, _stream(stream, q))
     _check(rc, "pa_decode")
+
+
+def pa_decode_noalloc(cache: pa_cache, q, out, block_tables, context_lens, max_context_len, scale,
+                      partition_size=0, stream=None):
+    """pa_decode with the split's scratch in the library's fixed device
+    array: no workspace argument, and nothing here allocates either."""
+    _check_rows(cache, q, out)
+    num_seqs, num_q_heads = int(q.shape[0]), int(q.shape[1])
+    _check_tables(block_tables, context_lens, num_seqs)
+    _same_device(q, out, block_tables, context_lens)
+    rc = lib().pa_decode_noalloc(ctypes.byref(cache), _dev_ptr(q, "q"), _dev_ptr(out, "out"), num_seqs, num_q_heads,
+                                 _dev_ptr(block_tables, "block_tables"), int(block_tables.shape[1]),
+                                 _dev_ptr(context_lens, "context_lens"), int(max_context_len), float(scale),
+                                 int(partition_size), _stream(stream, q))
+    _check(rc, "pa_decode_noalloc")
 
 
 def pa_decode_grouped_workspace_bytes(num_seqs, num_q_heads, head_dim, max_context_len, partition_size=0) -> int:

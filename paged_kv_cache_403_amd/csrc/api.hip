@@ -4,6 +4,8 @@
 #include <algorithm>
 #include <cmath>
 #include <cstdint>
+#include <cstdio>
+#include <mutex>
 
 #include "launch.h"
 #include "pagedattn.h"
@@ -46,7 +48,8 @@ int check_group(const pa_cache* c, int32_t num_q_heads, int32_t* group) {
 
 int check_scale(float scale) { return (std::isfinite(scale) && scale > 0.f) ? PA_OK : PA_EINVAL; }
 
-// Text of the calling thread's last HIP failure, for pa_last_error().
+// Text of the calling thread's last HIP failure (or of pa_decode_noalloc's
+// last refusal), for pa_last_error().
 thread_local const char* g_last_hip_error = "";
 
 int hip_status(hipError_t e) {
@@ -416,3 +419,84 @@ int pa_decode_grouped(const pa_cache* cache, const void* q, void* out, int32_t n
 
 }  // extern "C"
 
+// ---- split decode without a caller workspace ----------------------------------------
+//
+// For callers that cannot allocate device memory (code under graph capture,
+// tight serving loops, harnesses that forbid allocation): pa_decode with its
+// split-K partials and work list in a fixed device array of kScratchBytes
+// instead of a caller workspace.  Each device the library runs on holds its
+// own copy of the array from the first such call until the process ends; its
+// address on a device is looked up once, with that device current, and kept.
+// Calls that overlap on one device share the array and race.  Nothing in it
+// has to start at zero: the planner writes the work list and its length before
+// the walk reads them, and every partial is written before the merge reads it.
+namespace {
+
+constexpr size_t kScratchBytes = size_t(32) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kScratchMaxDev = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kScratchMaxDev];  // address of `scratch` on each device (null until looked up)
+thread_local char g_refusal[192];
+
+int refuse(int status, const char* fmt, long long a, long long b) {
+  std::snprintf(g_refusal, sizeof(g_refusal), fmt, a, b);
+  g_last_hip_error = g_refusal;
+  return status;
+}
+
+// Device address of the array on the current device, which must be the
+// stream's.
+int scratch_of_current_device(void* stream, void** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e);
+  if (dev < 0 || dev >= kScratchMaxDev)
+    return refuse(PA_EUNSUPPORTED, "pa_decode_noalloc: device %lld is beyond the %lld devices it keeps", dev,
+                  kScratchMaxDev);
+  if (stream) {
+    hipDevice_t sdev = 0;
+    e = hipStreamGetDevice(static_cast<hipStream_t>(stream), &sdev);
+    if (e != hipSuccess) return hip_status(e);
+    if (sdev != dev)
+      return refuse(PA_EINVAL, "pa_decode_noalloc: the stream is on device %lld, the current device is %lld",
+                    sdev, dev);
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e);
+    if (!p) return refuse(PA_EHIP, "pa_decode_noalloc: no address for the scratch array on device %lld%lld", dev, 0);
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return PA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int pa_decode_noalloc(const pa_cache* cache, const void* q, void* out, int32_t num_seqs, int32_t num_q_heads,
+                      const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
+                      int32_t max_context_len, float scale, int32_t partition_size, void* stream) {
+  pa::DecodeArgs a{};
+  size_t need = 0;
+  bool nothing = false;
+  int rc = decode_prepare(cache, q, out, num_seqs, num_q_heads, block_tables, max_blocks_per_seq, context_lens,
+                          max_context_len, scale, partition_size, &a, &need, &nothing);
+  if (rc != PA_OK || nothing) return rc;
+  if (need > kScratchBytes)
+    return refuse(PA_EWORKSPACE, "pa_decode_noalloc: the split needs %lld bytes of scratch, the fixed array holds %lld",
+                  static_cast<long long>(need), static_cast<long long>(kScratchBytes));
+  if (need > 0) {
+    void* ws = nullptr;
+    if ((rc = scratch_of_current_device(stream, &ws)) != PA_OK) return rc;
+    decode_carve(&a, ws, num_q_heads);
+  }
+  return hip_status(pa::launch_decode(a, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -356,3 +356,20 @@ def test_workload_slot_mapping_bit_exact(name, reduced):
     if name == "gqa_shared_prefix":
         assert len(pairs) > 0  # the shared-prefix workload does exercise copy-on-write
 
+
+def test_noalloc_refuses_an_oversize_split_before_any_hip_call():
+    """pa_decode_noalloc validates like pa_decode, and a split whose scratch
+    would not fit its fixed array is refused before anything touches the
+    GPU, with the bytes needed and the limit in pa_last_error()."""
+    c = _cache()
+    lib = P.lib()
+
+    def call(num_seqs=600, max_blocks=4096, max_ctx=4096 * 16, part=16, q=FAKE):
+        return lib.pa_decode_noalloc(ctypes.byref(c), q, FAKE, num_seqs, 32, FAKE, max_blocks, FAKE, max_ctx, 0.1,
+                                     part, None)
+    assert call() == P.PA_EWORKSPACE
+    msg = lib.pa_last_error().decode()
+    assert "needs" in msg and "33554432" in msg, msg
+    assert call(part=24) == P.PA_EINVAL
+    assert call(q=0) == P.PA_EINVAL
+    assert call(num_seqs=0) == P.PA_OK
