@@ -8,22 +8,35 @@ copy-on-write block copies, the KV append through the slot mapping, and the
 attention kernels (paged decode for one-token sequences, chunked prefill for
 chunks).  Inputs are resident in HBM before the timed region.
 
-Headline workload: 7B-shaped MHA decode (64 sequences, contexts U{128..2048},
-32 q = 32 KV heads, head_dim 128, fp16, block_size 16).  `value` is the
-step's algorithmic bytes (K/V read, q/out, tables, append) over the step time.
-Secondary measurements: chunked prefill on the mixed workload (8 chunks of
-512 tokens on cached contexts U{0..4096}, 32/8 heads, bf16) in TFLOP/s;
-plain vs prefix-grouped decode on the shared-prefix workload (256 sequences
-in groups of 8 forked from 512-token prompts, 32/8 heads, bf16), where the
-grouped path reads each shared block once; the headline decode batch again
-with an FP8 (E4M3) pool, whose K/V bytes are half; and that batch on pools
-of block size 8, 16, 32 and 64 with each pool's unused share.
+Headline workload: the long-context split-K decode batch (4 sequences of
+131072 tokens, 32 q / 8 KV heads, head_dim 128, bf16, block_size 32,
+partitions of 512 tokens merged by log-sum-exp): the largest of the five
+synthetic configurations, and one that fits one GPU.  `value` is the step's
+algorithmic bytes (K/V read, q/out, tables, lengths, append) over the median
+step time.
+
+Timing (every figure): each iteration has its own pair of HIP events on the
+stream the library launches on (torch's current stream); between iterations,
+outside the timed region, a 512 MiB scratch buffer is written and another
+512 MiB read, so no K/V byte of the previous iteration is left in the 256 MB
+Infinity Cache and no dirty flush line is written back during the next one;
+after 0.1 s of the same work (clocks settle) and W warm-up iterations, the
+median of K iterations is reported (back-to-back "warm" loop means are given
+beside the decode figures for comparison).
+
+Beside the headline: every configuration's step with its kernel times and
+rates (tiny decode latency; the 7B-shaped MHA decode; the shared-prefix batch
+through plain and prefix-grouped decode, rates on unique and logical bytes,
+and its copy-on-write copies; the long batch at the library's partition
+choice; the mixed chunked-prefill step), the FP8 pool, the block-size sweep,
+and the fp64 oracle's rate on the host cores for each configuration.
 
 Prints one JSON line on stdout; progress goes to stderr.
 """
 import argparse
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -33,6 +46,9 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2516.6  # MI355X dense bf16/fp16 matrix peak
 METRIC = "paged decode KV-read GB/s (% HBM peak) + seqs/s; prefill TFLOP/s (% MFMA)"
+HEADLINE = "long_splitk_decode"
+FLUSH_BYTES = 512 << 20
+SETTLE_S = 0.1  # untimed repetitions before any warm-up and timing
 
 
 def log(*a):
@@ -59,6 +75,73 @@ def prefill_flops(cached, n_new, num_q_heads, head_dim):
         c, n = int(c), int(n)
         tot += num_q_heads * 4 * head_dim * (n * c + n * (n + 1) // 2)
     return tot
+
+
+class Timer:
+    """Median of per-iteration HIP-event times with the cache flushed between
+    iterations (outside the timed region)."""
+
+    def __init__(self, device="cuda", flush=True):
+        import torch
+
+        self.torch = torch
+        self.flush_on = flush
+        if flush:
+            self.wbuf = torch.empty(FLUSH_BYTES // 4, dtype=torch.int32, device=device)
+            self.rbuf = torch.ones(FLUSH_BYTES // 4, dtype=torch.int32, device=device)
+            self.sink = torch.zeros((), dtype=torch.int64, device=device)
+            self.k = 0
+
+    def flush(self):
+        if self.flush_on:
+            self.k += 1
+            self.wbuf.fill_(self.k)
+            self.sink += self.rbuf.sum(dtype=self.torch.int64)
+
+    def settle(self, fn, seconds=SETTLE_S):
+        torch = self.torch
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < seconds:
+            for _ in range(8):
+                fn()
+            torch.cuda.synchronize()
+
+    def median_us(self, fn, iters, warmup, settle=True):
+        """Median and all per-iteration times (us) of fn."""
+        torch = self.torch
+        if settle:
+            self.settle(fn)
+        for _ in range(warmup):
+            self.flush()
+            fn()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(iters)]
+        torch.cuda.synchronize()
+        for a, b in ev:
+            self.flush()
+            a.record()
+            fn()
+            b.record()
+        torch.cuda.synchronize()
+        ts = [a.elapsed_time(b) * 1e3 for a, b in ev]
+        return statistics.median(ts), ts
+
+    def warm_us(self, fn, iters):
+        """Mean of a back-to-back loop between one event pair (no flush)."""
+        torch = self.torch
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        fn()
+        torch.cuda.synchronize()
+        a.record()
+        for _ in range(iters):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e3 / iters
+
+
+def spread(ts):
+    q = statistics.quantiles(ts, n=10) if len(ts) >= 10 else [min(ts), max(ts)]
+    return {"p10_us": round(q[0], 2), "p90_us": round(q[-1], 2), "min_us": round(min(ts), 2)}
 
 
 class Step:
@@ -91,6 +174,7 @@ class Step:
         pre = np.array([i for i in range(len(batch)) if n_new[i] > 1], dtype=np.int64)
         self.dec, self.pre = dec, pre
         self.partition_size = partition_size
+        self.part_used = None
         if len(dec):
             self.q_dec = to_device(q_all[starts[dec]], sp.dtype, device)
             self.out_dec = torch.empty_like(self.q_dec)
@@ -98,10 +182,7 @@ class Step:
             self.tab_dec = self.plan.block_tables[idx].contiguous()
             self.len_dec = self.plan.context_lens[idx].contiguous()
             self.max_dec = int(self.plan.host_lens[dec].max())
-            wsb = P.pa_decode_workspace_bytes(len(dec), sp.num_q_heads, sp.head_dim, self.max_dec, partition_size)
-            self.ws = torch.empty(max(wsb, 4), dtype=torch.uint8, device=device) if wsb else None
-            self.part_used = int(P.pa_decode_choose_partition(self.cache.desc, len(dec), sp.num_q_heads, self.max_dec)
-                              if partition_size == -1 else partition_size)
+            self.set_partition(partition_size)
             self.dec_bytes, self.dec_kv_bytes = decode_bytes(self.plan.host_lens[dec], sp.num_q_heads,
                                                              sp.num_kv_heads, sp.head_dim, sp.block_size,
                                                              sp.elem_bytes, sp.kv_elem_bytes)
@@ -125,15 +206,34 @@ class Step:
         T = int(n_new.sum())
         eb, kb = sp.elem_bytes, sp.kv_elem_bytes
         self.append_bytes = T * sp.num_kv_heads * sp.head_dim * (eb + kb) * 2 + T * 8
-        npairs = len(self.plan.host_pairs)
-        self.copy_bytes = npairs * sp.num_kv_heads * sp.block_size * sp.head_dim * kb * 4 + npairs * 8
+        self.npairs = len(self.plan.host_pairs)
+        self.copy_bytes = self.npairs * sp.num_kv_heads * sp.block_size * sp.head_dim * kb * 4 + self.npairs * 8
+        self.step_bytes = self.dec_bytes + self.append_bytes + self.copy_bytes
         torch.cuda.synchronize()
         log(f"{sp.name}: setup {time.time() - t0:.1f}s, {len(dec)} decode seqs, {len(pre)} chunks, "
-            f"{npairs} copy pairs")
+            f"{self.npairs} copy pairs")
+
+    def set_partition(self, partition_size):
+        import torch
+
+        sp = self.wl.spec
+        self.partition_size = partition_size
+        wsb = self.P.pa_decode_workspace_bytes(len(self.dec), sp.num_q_heads, sp.head_dim, self.max_dec,
+                                               partition_size)
+        self.ws = torch.empty(max(wsb, 4), dtype=torch.uint8, device="cuda") if wsb else None
+        self.part_used = int(self.P.pa_decode_choose_partition(self.cache.desc, len(self.dec), sp.num_q_heads,
+                                                               self.max_dec)
+                             if partition_size == -1 else partition_size)
+
+    def copy(self):
+        self.P.pa_copy_blocks(self.cache.desc, self.plan.cow_pairs)
+
+    def append(self):
+        self.P.pa_kv_append(self.cache.desc, self.k_new, self.v_new, self.plan.slot_mapping)
 
     def copy_append(self):
-        self.P.pa_copy_blocks(self.cache.desc, self.plan.cow_pairs)
-        self.P.pa_kv_append(self.cache.desc, self.k_new, self.v_new, self.plan.slot_mapping)
+        self.copy()
+        self.append()
 
     def decode(self):
         sp = self.wl.spec
@@ -145,134 +245,41 @@ class Step:
         self.P.pa_prefill_chunk(self.cache.desc, self.q_pre, self.out_pre, self.cu_pre, self.len_pre, self.tab_pre,
                                 self.maxq_pre, self.maxc_pre, sp.scale)
 
-
-SETTLE_S = 0.1  # untimed repetitions before any warm-up and timing
-
-
-def settle(fn, seconds=SETTLE_S):
-    """Repeat fn for `seconds` of wall time: the clocks take tens of ms of
-    sustained matrix work to reach their steady state."""
-    import torch
-
-    t0 = time.perf_counter()
-    while time.perf_counter() - t0 < seconds:
-        for _ in range(8):
-            fn()
-        torch.cuda.synchronize()
+    def step(self):
+        self.copy_append()
+        if len(self.pre):
+            self.prefill()
+        if len(self.dec):
+            self.decode()
 
 
-def time_loop(fn, iters):
-    """Average time of `iters` back-to-back calls of fn, from one pair of
-    HIP events around the loop on the stream the library launches on
-    (torch's current stream), in ms."""
-    import torch
-
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a.record()
-    for _ in range(iters):
-        fn()
-    b.record()
-    torch.cuda.synchronize()
-    return a.elapsed_time(b) / iters
+def gbs(nbytes, us):
+    return nbytes / (us * 1e-6) / 1e9
 
 
-def time_steps(st, steps, warmup):
-    """Time `steps` whole steps between one pair of events, after SETTLE_S
-    seconds of the same step and `warmup` more steps; then each kernel group
-    alone over as many back-to-back repetitions (its average launch time).
-    Events between the groups of every step would add their own cost (each
-    record is a marker packet with a cache write-back) to the step time, so
-    the step loop carries none."""
-    import torch
-
-    def one():
-        st.copy_append()
-        if len(st.pre):
-            st.prefill()
-        if len(st.dec):
-            st.decode()
-
-    settle(one)
-    for _ in range(warmup):
-        one()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    total_ms = time_loop(one, steps)
-    wall = time.perf_counter() - t0
-    ca = time_loop(st.copy_append, steps)
-    pf = time_loop(st.prefill, steps) if len(st.pre) else 0.0
-    dc = time_loop(st.decode, steps) if len(st.dec) else 0.0
-    return total_ms, wall * 1e3 / steps, ca, pf, dc
+def decode_entry(st, timer, iters, warmup, name="decode"):
+    """Flushed median of the decode launch (planner, walk and merge for a
+    split), its rate, and the back-to-back warm mean."""
+    us, ts = timer.median_us(st.decode, iters, warmup)
+    warm = timer.warm_us(st.decode, max(10, iters // 2))
+    rate = gbs(st.dec_bytes, us)
+    log(f"{st.wl.spec.name}: {name} {us:.1f} us = {rate:.0f} GB/s ({rate / HBM_PEAK_GBS:.1%}); warm {warm:.1f} us")
+    return {"us": round(us, 2), **spread(ts), "warm_us": round(warm, 2), "bytes": st.dec_bytes,
+            "kv_bytes": st.dec_kv_bytes, "gbs": round(rate, 1), "frac": round(rate / HBM_PEAK_GBS, 4),
+            "seqs_per_s": round(len(st.dec) / (us * 1e-6), 1), "partition_tokens": st.part_used}
 
 
-def cpu_baseline(wl, budget_s=15.0, min_s=10.0):
-    """The fp64 oracle on the host cores, on the same workload: sequences of
-    the batch in order (the whole batch again, if it takes less than min_s)
-    until about budget_s of work, in GB/s of the same algorithmic decode
-    bytes."""
-    import numpy as np
-
-    from oracle import attention as A
-    from oracle.cache import run_workload
-
-    sp = wl.spec
-    st = run_workload(wl)
-    q = wl.step_q()
-    rows = np.concatenate([[0], np.cumsum(st.q_lens)])
-    nseq = len(st.context_lens)
-    done, t_used, byts = 0, 0.0, 0
-    while t_used < (budget_s if done < nseq else min_s):
-        s = done % nseq
-        t0 = time.perf_counter()
-        A.paged_attention(q[rows[s]:rows[s + 1]], st.pool.k, st.pool.v, st.tables[s:s + 1],
-                          st.context_lens[s:s + 1], st.q_lens[s:s + 1], sp.scale, sp.dtype)
-        t_used += time.perf_counter() - t0
-        b, _ = decode_bytes(st.context_lens[s:s + 1], sp.num_q_heads, sp.num_kv_heads, sp.head_dim,
-                            sp.block_size, sp.elem_bytes)
-        byts += b
-        done += 1
-    try:
-        threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
-    except Exception:
-        threads = os.cpu_count()
-    return {"value": round(byts / t_used / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "sample": f"{done} sequence passes over the {nseq} sequences of {sp.name} (fp64 NumPy oracle, "
-                      f"{t_used:.1f}s of oracle time), decode bytes of those sequences over that time"}
+def unique_kv_bytes(st):
+    """K/V bytes of the decode batch counting each physical block once."""
+    sp = st.wl.spec
+    tabs, lens = st.plan.host_tables[st.dec], st.plan.host_lens[st.dec]
+    blocks = set()
+    for row, L in zip(tabs, lens):
+        blocks.update(int(b) for b in row[:(int(L) + sp.block_size - 1) // sp.block_size])
+    return len(blocks) * sp.num_kv_heads * sp.block_size * sp.head_dim * sp.kv_elem_bytes * 2
 
 
-DECODE_KERNEL_SOURCES = ("paged_kv_cache_403_amd/csrc/decode.hip", "paged_kv_cache_403_amd/csrc/decode_item.h",
-                         "paged_kv_cache_403_amd/csrc/common.h")
-
-
-def sources_sha256(paths):
-    """One SHA-256 over the files a kernel is compiled from, in order."""
-    import hashlib
-
-    h = hashlib.sha256()
-    for p in paths:
-        with open(os.path.join(ROOT, p), "rb") as f:
-            h.update(f.read())
-    return h.hexdigest()
-
-
-def counter_traffic(kernel_sources):
-    """HBM bytes per launch of the dominant kernel from the committed
-    rocprofv3 counter summary (FETCH_SIZE and WRITE_SIZE, each scaled by
-    what the counter reads for a plain device copy of known size), or None
-    when the kernel's sources have changed since the counters were taken."""
-    path = os.path.join(ROOT, "profiles", "decode_kernel_mha_decode_7b_hbm_counters.json")
-    try:
-        with open(path) as f:
-            rec = json.load(f)
-        sha = sources_sha256(kernel_sources)
-    except OSError:
-        return None
-    if rec.get("kernel_sources_sha256") != sha:
-        return None
-    return int(rec["hbm_bytes_per_launch"])
-
-
-def decode_group_starts(wl, dec):
+def group_starts(wl, dec):
     """Runs of consecutive decode sequences forked from one prompt (or a
     prompt followed by its forks): the grouping hint of grouped decode."""
     import numpy as np
@@ -283,24 +290,74 @@ def decode_group_starts(wl, dec):
     return np.array(starts, dtype=np.int32)
 
 
-def time_decode(st, iters, warmup):
-    """Average decode launch time (HIP events on the library's stream), us."""
+def grouped_entry(st, timer, iters, warmup, part=1024):
+    """Prefix-grouped decode of the step's decode batch: flushed median, the
+    rate on unique K/V bytes (each physical block once: what the method must
+    move) and on logical bytes, and the largest difference from plain decode."""
     import torch
 
-    settle(st.decode)
-    for _ in range(warmup):
-        st.decode()
+    sp = st.wl.spec
+    P = st.P
+    hint = torch.from_numpy(group_starts(st.wl, st.dec)).to("cuda")
+    n = len(st.dec)
+    wsb = P.pa_decode_grouped_workspace_bytes(n, sp.num_q_heads, sp.head_dim, st.max_dec, part)
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(st.q_dec)
+
+    def grouped():
+        P.pa_decode_grouped(st.cache.desc, st.q_dec, out, st.tab_dec, st.len_dec, st.max_dec, sp.scale, hint, part,
+                            ws)
+
+    us, ts = timer.median_us(grouped, iters, warmup)
+    warm = timer.warm_us(grouped, max(10, iters // 2))
+    st.decode()
     torch.cuda.synchronize()
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a.record()
-    for _ in range(iters):
-        st.decode()
-    b.record()
-    torch.cuda.synchronize()
-    return a.elapsed_time(b) / iters * 1e3
+    diff = float((out.float() - st.out_dec.float()).abs().max())
+    uniq = unique_kv_bytes(st)
+    meta = st.dec_bytes - st.dec_kv_bytes
+    rate = gbs(uniq + meta, us)
+    log(f"{sp.name}: grouped decode {us:.1f} us, {rate:.0f} GB/s on unique bytes ({rate / HBM_PEAK_GBS:.1%}); "
+        f"warm {warm:.1f} us")
+    return {"us": round(us, 2), **spread(ts), "warm_us": round(warm, 2), "partition_tokens": part,
+            "unique_kv_bytes": uniq, "unique_bytes": uniq + meta, "unique_gbs": round(rate, 1),
+            "unique_frac": round(rate / HBM_PEAK_GBS, 4), "logical_gbs": round(gbs(st.dec_bytes, us), 1),
+            "max_abs_diff_vs_plain": diff}
 
 
-def measure_block_sizes(name, iters, warmup, sizes=(8, 16, 32, 64)):
+def run_config(name, timer, iters, warmup, partition=-1, fp8=False):
+    """One configuration's step and its parts, all flushed medians."""
+    import workloads
+
+    wl = workloads.make(name)
+    if fp8:
+        wl = workloads.with_fp8_kv(wl)
+    sp = wl.spec
+    st = Step(wl, partition)
+    step_us, ts = timer.median_us(st.step, iters, warmup)
+    res = {"workload": sp.name, "num_seqs": len(wl.batch), "dtype": sp.dtype,
+           "kv_dtype": sp.kv_dtype or sp.dtype, "block_size": sp.block_size,
+           "step_us": round(step_us, 2), **{"step_" + k: v for k, v in spread(ts).items()},
+           "step_bytes": st.step_bytes, "step_gbs": round(gbs(st.step_bytes, step_us), 1)}
+    if st.npairs:
+        cus, _ = timer.median_us(st.copy, iters, warmup, settle=False)
+        res["cow_copy"] = {"pairs": st.npairs, "bytes": st.copy_bytes, "us": round(cus, 2),
+                           "gbs": round(gbs(st.copy_bytes, cus), 1)}
+    aus, _ = timer.median_us(st.append, iters, warmup, settle=False)
+    res["append"] = {"tokens": int(st.plan.n_new.sum()), "bytes": st.append_bytes, "us": round(aus, 2)}
+    if len(st.pre):
+        pus, pts = timer.median_us(st.prefill, iters, warmup)
+        tf = st.pre_flops / (pus * 1e-6) / 1e12
+        res["prefill"] = {"chunks": len(st.pre), "us": round(pus, 2), **spread(pts), "flops": st.pre_flops,
+                          "tflops": round(tf, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                          "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4)}
+        log(f"{sp.name}: prefill {pus:.1f} us = {tf:.1f} TFLOP/s ({tf / MFMA_BF16_PEAK_TFLOPS:.1%})")
+    if len(st.dec):
+        res["decode"] = decode_entry(st, timer, iters, warmup)
+    log(f"{sp.name}: step {step_us:.1f} us")
+    return res, st
+
+
+def measure_block_sizes(name, timer, iters, warmup, sizes=(8, 16, 32, 64)):
     """The same decode batch on pools of several block sizes: decode time
     and rate, and the pool's unused share from the library's block manager
     (1 - filled slots / slots of the blocks held) next to what reserving the
@@ -315,261 +372,149 @@ def measure_block_sizes(name, iters, warmup, sizes=(8, 16, 32, 64)):
         wl = base if bs == base.spec.block_size else workloads.with_block_size(base, bs)
         st = Step(wl, -1)
         st.copy_append()
-        us = time_decode(st, iters, warmup)
+        d = decode_entry(st, timer, iters, warmup)
         held, used = st.cache.bm.usage()
-        rows.append({"block_size": bs, "decode_us": round(us, 2),
-                     "achieved_gbs": round(st.dec_bytes / (us * 1e-6) / 1e9, 1),
-                     "decode_partition_tokens": st.part_used, "blocks_in_use": held,
-                     "paged_waste": round(1.0 - used / (held * bs), 5)})
-        log(f"{name} block_size {bs}: decode {us:.1f} us, unused share {rows[-1]['paged_waste']:.4f}")
+        rows.append({"block_size": bs, "decode_us": d["us"], "gbs": d["gbs"], "partition_tokens": st.part_used,
+                     "blocks_in_use": held, "paged_waste": round(1.0 - used / (held * bs), 5)})
+        log(f"{name} block_size {bs}: unused share {rows[-1]['paged_waste']:.4f}")
     lens = np.array([p.context_len for p in base.batch], dtype=np.int64)
     static = 1.0 - float(lens.sum()) / float(len(lens) * lens.max())
     return {"workload": name, "sizes": rows, "static_reservation_waste": round(static, 4),
             "static_reservation_tokens": int(lens.max())}
 
 
-def measure_long(name, iters, warmup):
-    """Split-K decode of a few very long sequences: the library's partition
-    choice and 512-token partitions, HIP-event launch times (planner, walk
-    and merge together) and the rate of the decode's algorithmic bytes."""
-    import torch
+# ---- the fp64 oracle on the host -----------------------------------------------------
 
-    import workloads
-
-    wl = workloads.make(name)
-    st = Step(wl, -1)
-    st.copy_append()
-    rows = []
-    for part in (-1, 512):
-        st.partition_size = part
-        if part != -1:
-            st.part_used = part
-        wsb = st.P.pa_decode_workspace_bytes(len(st.dec), wl.spec.num_q_heads, wl.spec.head_dim, st.max_dec,
-                                             part)
-        st.ws = torch.empty(max(wsb, 4), dtype=torch.uint8, device="cuda") if wsb else None
-        us = time_decode(st, iters, warmup)
-        rows.append({"partition_tokens": st.part_used, "decode_us": round(us, 2),
-                     "achieved_gbs": round(st.dec_bytes / (us * 1e-6) / 1e9, 1),
-                     "frac": round(st.dec_bytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)})
-        log(f"{name}: {st.part_used}-token partitions, decode {us:.1f} us = {rows[-1]['achieved_gbs']:.0f} GB/s")
-    return {"workload": name, "bytes_per_launch": st.dec_bytes, "runs": rows}
-
-
-def time_prefill(st, iters, warmup):
-    """Average prefill launch time (HIP events on the library's stream), us."""
-    import torch
-
-    settle(st.prefill)
-    for _ in range(warmup):
-        st.prefill()
-    torch.cuda.synchronize()
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a.record()
-    for _ in range(iters):
-        st.prefill()
-    b.record()
-    torch.cuda.synchronize()
-    return a.elapsed_time(b) / iters * 1e3
-
-
-def measure_serving_loop(n_requests=1024, budget=8192, max_running=256):
-    """The host scheduler loop (pa_sched_*) driving the kernels over a
-    synthetic arrival trace, as a serving engine would each iteration: the
-    scheduler picks decode tokens and prompt chunks under a token budget and
-    hands out slots, then one pa_kv_append, one pa_prefill_chunk and one
-    pa_decode run on the iteration's batch.  Shapes of the mixed workload
-    (32 q / 8 KV heads, head_dim 128, bf16, block_size 16); prompts lognormal
-    around 512 tokens (cap 4096), 1..64 new tokens each; a pool that holds
-    every request.  K/V/q rows are synthetic values (their contents do not
-    change the work).  Reports tokens per second through the whole loop
-    (host scheduling, table uploads and kernels, wall clock) and the part of
-    that time the GPU was busy (events around each iteration's kernels)."""
+def host_info():
+    """CPU model, threads the oracle's BLAS uses, and the BLAS build."""
     import numpy as np
-    import torch
 
-    import paged_kv_cache_403_amd as P
-    import workloads
-    from paged_kv_cache_403_amd.runtime import PagedKVCache
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    threads = None
+    try:
+        import threadpoolctl
 
-    hq, hkv, d, bs, dt = 32, 8, 128, 16, "bf16"
-    trace = workloads.arrival_trace(n_requests, seed=3, median_prompt=512, max_prompt=4096, max_new=64,
-                                    mean_gap=0.25)
-    nb = sum(-(-(p + m) // bs) for _, _, p, m in trace) + 1
-    g = torch.Generator(device="cuda").manual_seed(403)
-    rows = budget + max_running
-    kbuf = torch.randn(rows, hkv, d, device="cuda", dtype=torch.bfloat16, generator=g)
-    vbuf = torch.randn(rows, hkv, d, device="cuda", dtype=torch.bfloat16, generator=g)
-    qbuf = torch.randn(rows, hq, d, device="cuda", dtype=torch.bfloat16, generator=g)
-    obuf = torch.empty_like(qbuf)
-    max_ctx = max(p + m for _, _, p, m in trace)
-    wsb = P.pa_decode_workspace_bytes(max_running, hq, d, max_ctx, -1)
-    ws = torch.empty(max(wsb, 4), dtype=torch.uint8, device="cuda")
-    scale = 1.0 / np.sqrt(d)
-
-    def run():
-        cache = PagedKVCache(nb, hkv, bs, d, dt, "cuda", np.arange(nb - 1, dtype=np.int32), fill_value=0.0)
-        sched = P.Scheduler(cache.bm, budget, max_running)
-        k, it, tokens = 0, 0, 0
-        cached = {}
-        events = []
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        while (k < len(trace) or sched.unfinished() > 0) and it < 100000:
-            while k < len(trace) and trace[k][0] <= it:
-                sched.add(*trace[k][1:])
-                k += 1
-            decodes, prefills, slots, pairs, finished, pre = sched.step()
-            it += 1
-            entries = [(rid, 1) for rid in decodes] + list(prefills)
-            if not entries:
-                continue
-            for rid in pre:  # preempted: prefilled again from the start
-                cached[rid] = 0
-            T = int(sum(n for _, n in entries))
-            tokens += T
-            ids = np.array([rid for rid, _ in entries], np.int32)
-            for rid, n in entries:
-                cached[rid] = cached.get(rid, 0) + n
-            lens = np.array([cached[rid] for rid, _ in entries], np.int32)
-            mb = int(max(-(-int(lens.max()) // bs), 1))
-            tables, _ = cache.bm.tables(ids, mb, nb - 1)
-            slots_d = torch.from_numpy(slots).cuda()
-            tables_d = torch.from_numpy(tables).cuda()
-            lens_d = torch.from_numpy(lens).cuda()
-            nd = len(decodes)
-            if prefills:
-                n_new = np.array([n for _, n in prefills], np.int32)
-                cu_d = torch.from_numpy(np.concatenate([[0], np.cumsum(n_new)]).astype(np.int32)).cuda()
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record()
-            if len(pairs):
-                P.pa_copy_blocks(cache.desc, torch.from_numpy(pairs).cuda())
-            P.pa_kv_append(cache.desc, kbuf[:T], vbuf[:T], slots_d)
-            if nd:
-                P.pa_decode(cache.desc, qbuf[:nd], obuf[:nd], tables_d[:nd], lens_d[:nd], int(lens[:nd].max()),
-                            scale, -1, ws)
-            if prefills:
-                npre = int(n_new.sum())
-                P.pa_prefill_chunk(cache.desc, qbuf[nd:nd + npre], obuf[nd:nd + npre], cu_d, lens_d[nd:],
-                                   tables_d[nd:], int(n_new.max()), int(lens[nd:].max()), scale)
-            b.record()
-            events.append((a, b))
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
-        return it, tokens, wall, sum(x.elapsed_time(y) for x, y in events)
-
-    run()  # warm-up pass over the same trace
-    it, tokens, wall, gpu_ms = run()
-    res = {"requests": n_requests, "iterations": it, "tokens": tokens, "wall_s": round(wall, 4),
-           "tokens_per_s": round(tokens / wall, 1), "gpu_busy_ms": round(gpu_ms, 2),
-           "gpu_share": round(gpu_ms / (wall * 1e3), 3), "token_budget": budget, "max_running": max_running}
-    log(f"serving loop: {n_requests} requests, {it} iterations, {tokens} tokens in {wall:.3f} s = "
-        f"{tokens / wall:.0f} tokens/s (GPU busy {gpu_ms:.1f} ms)")
-    return res
+        info = [x for x in threadpoolctl.threadpool_info() if x.get("user_api") == "blas"]
+        if info:
+            threads = int(info[0]["num_threads"])
+    except Exception:
+        pass
+    if threads is None:
+        threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
+    blas = {}
+    try:
+        b = np.show_config(mode="dicts")["Build Dependencies"]["blas"]
+        blas = {"name": b.get("name"), "version": b.get("version"),
+                "config": (b.get("openblas configuration") or "")[:120]}
+    except Exception:
+        pass
+    return {"cpu_model": model, "threads": threads, "affinity_cpus": len(os.sched_getaffinity(0)), "blas": blas}
 
 
-def measure_fp8(name, ref_us, iters, warmup, prefill_name=None):
-    """Decode of the same batch with an FP8 (E4M3) pool and 16-bit
-    activations: time, algorithmic bytes (1-byte K/V), rate, and the speedup
-    over the 16-bit pool's decode time ref_us."""
-    import workloads
-
-    wl = workloads.with_fp8_kv(workloads.make(name))
-    st = Step(wl, -1)
-    st.copy_append()
-    us = time_decode(st, iters, warmup)
-    gbs = st.dec_bytes / (us * 1e-6) / 1e9
-    log(f"{wl.spec.name}: decode {us:.1f} us, {gbs:.0f} GB/s, x{ref_us / us:.2f} over the 16-bit pool")
-    res = {"workload": wl.spec.name, "kv_dtype": "fp8 e4m3", "act_dtype": wl.spec.dtype,
-           "k_scale": wl.spec.k_scale, "v_scale": wl.spec.v_scale, "decode_us": round(us, 2),
-           "bytes_per_launch": st.dec_bytes, "achieved_gbs": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4),
-           "speedup_vs_16bit_pool": round(ref_us / us, 3), "decode_partition_tokens": st.part_used}
-    if prefill_name:
-        # chunked prefill over an FP8 pool (the codes widened while staging)
-        wlp = workloads.with_fp8_kv(workloads.make(prefill_name))
-        stp = Step(wlp, -1)
-        stp.copy_append()
-        pus = time_prefill(stp, max(5, iters // 2), warmup)
-        tf = stp.pre_flops / (pus * 1e-6) / 1e12
-        log(f"{wlp.spec.name}: prefill {pus:.1f} us = {tf:.1f} TFLOP/s")
-        res["prefill"] = {"workload": wlp.spec.name, "prefill_us": round(pus, 2), "tflops": round(tf, 2),
-                          "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4)}
-    return res
-
-
-def measure_grouped(name, iters, warmup, fp8=False):
-    """Plain split decode against prefix-grouped decode on one workload's
-    decode batch: HIP-event times on the library's stream, and the K/V bytes
-    each must read (logical: every sequence's context; unique: each
-    physical block once)."""
-    import torch
+def oracle_rate(name, budget_s):
+    """The fp64 NumPy oracle (gather through the tables, then plain softmax
+    attention) over the configuration's sequences in batch order until about
+    budget_s seconds of oracle time: decode rows in GB/s of the same
+    algorithmic bytes, chunk rows in GFLOP/s of the same algorithmic flops."""
+    import numpy as np
 
     import workloads
+    from oracle import attention as A
+    from oracle.cache import run_workload
 
     wl = workloads.make(name)
-    if fp8:
-        wl = workloads.with_fp8_kv(wl)
-    st = Step(wl, -1)
     sp = wl.spec
-    P = st.P
-    st.copy_append()
-    hint = torch.from_numpy(decode_group_starts(wl, st.dec)).to("cuda")
-    n = len(st.dec)
-    part = 1024
-    wsb = P.pa_decode_grouped_workspace_bytes(n, sp.num_q_heads, sp.head_dim, st.max_dec, part)
-    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
-    out = torch.empty_like(st.q_dec)
+    st = run_workload(wl)
+    q = wl.step_q()
+    rows = np.concatenate([[0], np.cumsum(st.q_lens)])
+    nseq = len(st.context_lens)
+    t_dec = t_pre = 0.0
+    b_dec = f_pre = 0
+    done = 0
+    while t_dec + t_pre < budget_s and done < 64 * nseq:
+        s = done % nseq
+        t0 = time.perf_counter()
+        A.paged_attention(q[rows[s]:rows[s + 1]], st.pool.k, st.pool.v, st.tables[s:s + 1],
+                          st.context_lens[s:s + 1], st.q_lens[s:s + 1], sp.scale, sp.dtype)
+        dt = time.perf_counter() - t0
+        n, L = int(st.q_lens[s]), int(st.context_lens[s])
+        if n == 1:
+            t_dec += dt
+            b_dec += decode_bytes([L], sp.num_q_heads, sp.num_kv_heads, sp.head_dim, sp.block_size,
+                                  sp.elem_bytes)[0]
+        else:
+            t_pre += dt
+            f_pre += prefill_flops([L - n], [n], sp.num_q_heads, sp.head_dim)
+        done += 1
+    res = {"workload": name, "sequence_passes": done, "of_sequences": nseq,
+           "oracle_s": round(t_dec + t_pre, 2)}
+    if t_dec:
+        res["decode_gbs"] = round(b_dec / t_dec / 1e9, 4)
+    if t_pre:
+        res["prefill_gflops"] = round(f_pre / t_pre / 1e9, 3)
+    log(f"oracle {name}: {done} sequence passes in {t_dec + t_pre:.1f} s")
+    return res
 
-    def grouped():
-        P.pa_decode_grouped(st.cache.desc, st.q_dec, out, st.tab_dec, st.len_dec, st.max_dec, sp.scale, hint, part,
-                            ws)
 
-    def timed(fn):
-        settle(fn)
-        for _ in range(warmup):
-            fn()
-        torch.cuda.synchronize()
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record()
-        for _ in range(iters):
-            fn()
-        b.record()
-        torch.cuda.synchronize()
-        return a.elapsed_time(b) / iters * 1e3
+# ---- HBM traffic from the committed counter summary ------------------------------------
 
-    plain_us = timed(st.decode)
-    grouped_us = timed(grouped)
-    torch.cuda.synchronize()
-    diff = float((out.float() - st.out_dec.float()).abs().max())
-    tabs, lens = st.plan.host_tables[st.dec], st.plan.host_lens[st.dec]
-    blocks = set()
-    for row, L in zip(tabs, lens):
-        blocks.update(int(b) for b in row[:(int(L) + sp.block_size - 1) // sp.block_size])
-    unique = len(blocks) * sp.num_kv_heads * sp.block_size * sp.head_dim * sp.kv_elem_bytes * 2
-    log(f"{sp.name}: plain decode {plain_us:.1f} us, grouped decode {grouped_us:.1f} us "
-        f"(unique K/V {unique / 1e6:.1f} MB of {st.dec_kv_bytes / 1e6:.1f} MB logical)")
-    return {"workload": sp.name, "plain_decode_us": round(plain_us, 2), "plain_partition_tokens": st.part_used,
-            "grouped_decode_us": round(grouped_us, 2), "grouped_partition_tokens": part,
-            "speedup": round(plain_us / grouped_us, 3), "logical_kv_bytes": st.dec_kv_bytes,
-            "unique_kv_bytes": unique, "grouped_unique_gbs": round(unique / (grouped_us * 1e-6) / 1e9, 1),
-            "plain_logical_gbs": round(st.dec_kv_bytes / (plain_us * 1e-6) / 1e9, 1),
-            "max_abs_diff_vs_plain": diff}
+DECODE_KERNEL_SOURCES = ("paged_kv_cache_403_amd/csrc/decode.hip", "paged_kv_cache_403_amd/csrc/decode_item.h",
+                         "paged_kv_cache_403_amd/csrc/common.h")
+COUNTERS = "profiles/split_decode_long_splitk_decode_p512_hbm_counters.json"
+
+
+def sources_sha256(paths):
+    """One SHA-256 over the files a kernel is compiled from, in order."""
+    import hashlib
+
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def counter_traffic():
+    """HBM bytes per launch of the headline decode (its three kernels) from
+    the committed rocprofv3 counter summary (FETCH_SIZE and WRITE_SIZE, each
+    scaled by what the counter reads for a plain device copy of known size),
+    or None when the kernels' sources have changed since the counters were
+    taken."""
+    try:
+        with open(os.path.join(ROOT, COUNTERS)) as f:
+            rec = json.load(f)
+        sha = sources_sha256(DECODE_KERNEL_SOURCES)
+    except OSError:
+        return None
+    if rec.get("kernel_sources_sha256") != sha:
+        return None
+    return int(rec["hbm_bytes_per_launch"])
 
 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="mha_decode_7b")
-    ap.add_argument("--partition", type=int, default=-1, help="decode partition tokens (0 one pass, -1 auto)")
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=HEADLINE)
+    ap.add_argument("--partition", type=int, default=None,
+                    help="decode partition tokens (0 one pass, -1 library choice; default: the workload's "
+                         "stated partitions, else -1)")
+    ap.add_argument("--headline-only", action="store_true", help="time the headline step only")
+    ap.add_argument("--no-flush", action="store_true", help="no cache flush between timed iterations")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-prefill", action="store_true", help="skip the chunked-prefill measurement")
-    ap.add_argument("--no-grouped", action="store_true", help="skip the plain vs grouped decode measurement")
-    ap.add_argument("--no-fp8", action="store_true", help="skip the FP8 KV-pool decode measurement")
+    ap.add_argument("--no-configs", action="store_true", help="skip the other configurations")
+    ap.add_argument("--no-fp8", action="store_true", help="skip the FP8 KV-pool measurements")
     ap.add_argument("--no-block-sizes", action="store_true", help="skip the block-size sweep")
-    ap.add_argument("--no-long", action="store_true", help="skip the long-context split-K measurement")
-    ap.add_argument("--no-serving", action="store_true", help="skip the scheduler-loop measurement")
+    ap.add_argument("--oracle-s", type=float, default=12.0, help="oracle seconds for the headline baseline")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB a few times (the known-size reference for "
                          "the HBM byte counters) and exit")
@@ -594,25 +539,34 @@ def main():
         torch.cuda.synchronize()
         log(f"copied {n} bytes 3 times")
         return
+    timer = Timer(flush=not args.no_flush)
     wl = workloads.make(args.workload)
     sp = wl.spec
-    st = Step(wl, args.partition)
-    ms, wall_ms, ca_ms, pf_ms, dc_ms = time_steps(st, args.steps, args.warmup)
-    step_bytes = st.dec_bytes + st.append_bytes + st.copy_bytes
-    value = step_bytes / (ms * 1e-3) / 1e9
+    part = args.partition if args.partition is not None else (sp.partition_size or -1)
+    st = Step(wl, part)
+    K, W = args.steps, args.warmup
+    # the timed steps: W warm-ups, then K steps each between its own events
+    timer.settle(st.step)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    step_us, ts = timer.median_us(st.step, K, W, settle=False)
+    wall = time.perf_counter() - t0
+    value = gbs(st.step_bytes, step_us)
     n_seqs = len(wl.batch)
-    log(f"{sp.name}: {ms * 1e3:.1f} us/step (wall {wall_ms * 1e3:.1f}), decode {dc_ms * 1e3:.1f} us, "
-        f"copy+append {ca_ms * 1e3:.1f} us, {value:.0f} GB/s")
-    dom_bytes, dom_ms, bound = st.dec_bytes, dc_ms, "hbm"
+    log(f"{sp.name}: step {step_us:.1f} us median of {K} (wall {wall * 1e3 / K:.1f} ms per step with flush), "
+        f"{value:.0f} GB/s")
+    head = decode_entry(st, timer, K, W) if len(st.dec) else None
     result = {
         "metric": METRIC,
         "value": round(value, 2),
         "unit": "GB/s",
         "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
+        "steps": K,
+        "warmup": W,
         "settle_s": SETTLE_S,
-        "ms_per_step": round(ms, 5),
+        "ms_per_step": round(step_us / 1e3, 5),
+        "step_timing": {"statistic": "median", **spread(ts),
+                        "flush": None if args.no_flush else "write 512 MiB + read 512 MiB between iterations"},
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -622,48 +576,60 @@ def main():
             "workload": sp.name, "num_seqs": n_seqs, "num_q_heads": sp.num_q_heads,
             "num_kv_heads": sp.num_kv_heads, "head_dim": sp.head_dim, "block_size": sp.block_size,
             "context_tokens": int(st.plan.host_lens.sum()), "max_context": int(st.plan.host_lens.max()),
-            "decode_partition_tokens": getattr(st, "part_used", None), "parallelism": "none (1 GPU)",
+            "decode_partition_tokens": st.part_used, "parallelism": "none (1 GPU)",
         },
-        "seqs_per_s": round(n_seqs / (ms * 1e-3), 1),
-        "breakdown_us": {"copy_append": round(ca_ms * 1e3, 2), "prefill": round(pf_ms * 1e3, 2),
-                         "decode": round(dc_ms * 1e3, 2)},
-        "roofline": {"bound": bound, "achieved": round(dom_bytes / (dom_ms * 1e-3) / 1e9, 1),
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(dom_bytes / (dom_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                     "traffic": counter_traffic(DECODE_KERNEL_SOURCES),
-                     "kernel": "decode_kernel", "bytes_per_launch": dom_bytes},
+        "seqs_per_s": round(n_seqs / (step_us * 1e-6), 1),
+        "step_bytes": st.step_bytes,
     }
-    if not args.no_prefill:
-        wl5 = workloads.make("mixed_chunked_prefill")
-        st5 = Step(wl5, -1)
-        ms5, _, ca5, pf5, dc5 = time_steps(st5, max(5, args.steps // 5), 2)
-        tf = st5.pre_flops / (pf5 * 1e-3) / 1e12
-        dec_gbs = st5.dec_bytes / (dc5 * 1e-3) / 1e9
-        log(f"mixed_chunked_prefill: step {ms5 * 1e3:.1f} us, prefill {pf5 * 1e3:.1f} us = {tf:.1f} TFLOP/s, "
-            f"decode {dc5 * 1e3:.1f} us = {dec_gbs:.0f} GB/s")
-        result["prefill"] = {
-            "workload": "mixed_chunked_prefill", "ms_per_step": round(ms5, 5),
-            "prefill_us": round(pf5 * 1e3, 2), "flops": st5.pre_flops,
-            "tflops": round(tf, 2), "peak": MFMA_BF16_PEAK_TFLOPS, "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
-            "decode_us": round(dc5 * 1e3, 2), "decode_gbs": round(dec_gbs, 1), "copy_append_us": round(ca5 * 1e3, 2),
-        }
-    if not args.no_grouped:
-        result["shared_prefix"] = measure_grouped("gqa_shared_prefix", max(10, args.steps // 2), 3)
+    if head is not None:
+        result["decode"] = head
+        result["roofline"] = {
+            "bound": "hbm", "achieved": head["gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": head["frac"],
+            "traffic": counter_traffic(),
+            "kernel": ("pa_decode: decode_plan_kernel + decode_persistent_kernel + decode_reduce_kernel"
+                       if st.part_used and st.part_used < st.max_dec else "pa_decode: decode_kernel"),
+            "bytes_per_launch": st.dec_bytes, "launch_us": head["us"]}
+    if not args.headline_only:
+        configs = {}
+        if not args.no_configs:
+            for name in workloads.CONFIG_NAMES:
+                if name == sp.name:
+                    continue
+                res, cst = run_config(name, timer, K, W)
+                if name == "gqa_shared_prefix":
+                    res["grouped"] = grouped_entry(cst, timer, K, W)
+                configs[name] = res
+                del cst
+                torch.cuda.empty_cache()
+            if sp.name == HEADLINE and "partition_tokens" in (head or {}):
+                st.set_partition(-1)
+                configs[HEADLINE + "_library_partition"] = {"decode": decode_entry(st, timer, K, W)}
+        result["configs"] = configs
         if not args.no_fp8:
-            result["shared_prefix"]["fp8_kv"] = measure_grouped("gqa_shared_prefix", max(10, args.steps // 2), 3,
-                                                                fp8=True)
-    if not args.no_fp8 and sp.dtype in ("f16", "bf16"):
-        result["fp8_kv"] = measure_fp8(args.workload, dc_ms * 1e3, max(10, args.steps // 2), 3,
-                                       None if args.no_prefill else "mixed_chunked_prefill")
-    if not args.no_block_sizes:
-        result["block_sizes"] = measure_block_sizes(args.workload, max(10, args.steps // 2), 3)
-    if not args.no_long:
-        result["long_split"] = measure_long("long_splitk_decode", max(10, args.steps // 2), 3)
-    if not args.no_serving:
-        result["serving_loop"] = measure_serving_loop()
+            fp8 = {}
+            for name in ("mha_decode_7b", "gqa_shared_prefix", "mixed_chunked_prefill"):
+                res, cst = run_config(name, timer, K, W, fp8=True)
+                if name == "gqa_shared_prefix":
+                    res["grouped"] = grouped_entry(cst, timer, K, W)
+                fp8[name] = res
+                del cst
+                torch.cuda.empty_cache()
+            result["fp8_kv"] = fp8
+        if not args.no_block_sizes:
+            result["block_sizes"] = measure_block_sizes("mha_decode_7b", timer, max(20, K // 2), W)
     if not args.no_cpu_baseline:
-        log("timing the CPU oracle on a sample")
-        result["cpu_baseline"] = cpu_baseline(wl)
+        log("timing the CPU oracle")
+        hi = host_info()
+        base = oracle_rate(sp.name, args.oracle_s)
+        result["cpu_baseline"] = {
+            "value": base.get("decode_gbs"), "unit": "GB/s", "cores": hi["threads"], "kind": "oracle",
+            "sample": f"{base['sequence_passes']} sequence passes over the {base['of_sequences']} sequences of "
+                      f"{sp.name} (fp64 NumPy oracle, {base['oracle_s']} s of oracle time), decode bytes of those "
+                      f"sequences over that time",
+            "host": hi}
+        if not args.headline_only and not args.no_configs:
+            result["cpu_baseline"]["per_config"] = [oracle_rate(n, 4.0) for n in workloads.CONFIG_NAMES
+                                                    if n != sp.name]
     print(json.dumps(result), flush=True)
 
 
