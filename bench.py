@@ -88,15 +88,15 @@ class Timer:
         self.flush_on = flush
         if flush:
             self.wbuf = torch.empty(FLUSH_BYTES // 4, dtype=torch.int32, device=device)
-            self.rbuf = torch.ones(FLUSH_BYTES // 4, dtype=torch.int32, device=device)
-            self.sink = torch.zeros((), dtype=torch.int64, device=device)
+            self.rbuf = torch.ones(FLUSH_BYTES // 4, dtype=torch.float32, device=device)
+            self.sink = torch.zeros((), dtype=torch.float32, device=device)
             self.k = 0
 
     def flush(self):
         if self.flush_on:
             self.k += 1
             self.wbuf.fill_(self.k)
-            self.sink += self.rbuf.sum(dtype=self.torch.int64)
+            self.sink += self.rbuf.sum()
 
     def settle(self, fn, seconds=SETTLE_S):
         torch = self.torch

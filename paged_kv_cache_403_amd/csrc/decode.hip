@@ -79,8 +79,19 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams P) {
 // one cost nothing for the partitions they do not have.  Consecutive items
 // are the KV heads of one (sequence, partition), which read neighbouring
 // tiles of the same blocks.
+// Wavefronts per SIMD the persistent kernel is held to: three for the
+// 16-bit instances with 32-token key tiles and up to 4 q heads per KV head
+// (168 registers fit without spills, against 186 unconstrained, one more
+// resident workgroup per compute unit to keep loads in flight); otherwise
+// what the compiler gives.
+template <typename ST, int D, int BS, int G>
+constexpr int persistent_waves_per_eu() {
+  return (ST::bytes == 2 && D == 128 && decode_tile<ST, D, G>(BS) == 32 && G == 4) ? 3 : 1;
+}
+
 template <typename ST, int D, int BS, int G, typename AT = ST>
-__global__ __launch_bounds__(kThreads) void decode_persistent_kernel(DecodeParams P) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(persistent_waves_per_eu<ST, D, BS, G>(), 8)))
+void decode_persistent_kernel(DecodeParams P) {
   __shared__ DecodeLds<G, D, BS> sh;
   const int hk = P.num_kv_heads;
   const int n = __builtin_amdgcn_readfirstlane(*P.n_items) * hk;
@@ -239,15 +250,32 @@ __global__ __launch_bounds__(kRedThreads) void decode_reduce_kernel(const float*
   const float* o = ws_o + qh * max_parts * D + c * 4;
   float4 num = {0.f, 0.f, 0.f, 0.f};
   float den = 0.f;
-#pragma unroll 8
-  for (int p = slot; p < np; p += SLOTS) {
-    const float w = ml[2 * p + 1] * __builtin_amdgcn_exp2f(ml[2 * p] - M);
-    const float4 v = *reinterpret_cast<const float4*>(o + static_cast<int64_t>(p) * D);
+  auto add = [&](float w, const float4& v) __attribute__((always_inline)) {
     num.x = __builtin_fmaf(w, v.x, num.x);
     num.y = __builtin_fmaf(w, v.y, num.y);
     num.z = __builtin_fmaf(w, v.z, num.z);
     num.w = __builtin_fmaf(w, v.w, num.w);
     den += w;
+  };
+  // eight of the slot's partitions per step: their loads are all issued
+  // before the first is used (the sums still run in partition order)
+  constexpr int U = 8;
+  int p = slot;
+  for (; p + (U - 1) * SLOTS < np; p += U * SLOTS) {
+    float w[U];
+    float4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int pu = p + u * SLOTS;
+      w[u] = ml[2 * pu + 1] * __builtin_amdgcn_exp2f(ml[2 * pu] - M);
+      v[u] = *reinterpret_cast<const float4*>(o + static_cast<int64_t>(pu) * D);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) add(w[u], v[u]);
+  }
+  for (; p < np; p += SLOTS) {
+    const float w = ml[2 * p + 1] * __builtin_amdgcn_exp2f(ml[2 * p] - M);
+    add(w, *reinterpret_cast<const float4*>(o + static_cast<int64_t>(p) * D));
   }
   slot_num[slot][c] = num;
   if (c == 0) slot_den[slot] = den;
@@ -272,10 +300,10 @@ __global__ __launch_bounds__(kRedThreads) void decode_reduce_kernel(const float*
   }
 }
 
-// Workgroups of the persistent kernel: as many as fit on the device at once
-// (queried once per kernel instance and device).
-template <typename ST, int D, int BS, int G, typename AT = ST>
-int persistent_grid() {
+// Workgroups of a persistent kernel: as many as fit on the device at once
+// (queried once per kernel and device).
+template <typename KernelTag>
+int resident_grid(const void* kernel) {
   constexpr int kMaxDev = 64;
   static std::atomic<int> cached[kMaxDev];  // 0 = not yet queried; racing writers store the same value
   int dev = 0;
@@ -284,16 +312,16 @@ int persistent_grid() {
   if (n == 0) {
     int cus = 0, per_cu = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &per_cu, reinterpret_cast<const void*>(&decode_persistent_kernel<ST, D, BS, G, AT>), kThreads, 0) !=
-            hipSuccess ||
-        per_cu <= 0)
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kThreads, 0) != hipSuccess || per_cu <= 0)
       per_cu = 2;
     n = cus * per_cu;
     cached[dev].store(n, std::memory_order_relaxed);
   }
   return n;
 }
+
+template <typename ST, int D, int BS, int G, typename AT>
+struct PersistentTag {};
 
 template <typename ST, int D, int BS, int G, typename AT = ST>
 hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t st) {
@@ -325,7 +353,9 @@ hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t st) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t upper = static_cast<int64_t>(a.num_seqs) * a.num_parts * a.num_kv_heads;
-  const int grid = static_cast<int>(std::min<int64_t>(upper, persistent_grid<ST, D, BS, G, AT>()));
+  const int grid = static_cast<int>(std::min<int64_t>(
+      upper, resident_grid<PersistentTag<ST, D, BS, G, AT>>(
+                 reinterpret_cast<const void*>(&decode_persistent_kernel<ST, D, BS, G, AT>))));
   hipLaunchKernelGGL((decode_persistent_kernel<ST, D, BS, G, AT>), dim3(grid), dim3(kThreads), 0, st, P);
   e = hipGetLastError();
   if (e != hipSuccess) return e;

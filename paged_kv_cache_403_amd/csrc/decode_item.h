@@ -20,6 +20,8 @@ constexpr float kLog2e = 1.4426950408889634f;
 #define PA_DECODE_NBUF32 1
 #endif
 
+
+
 template <typename ST, int D, int BS, int G>
 struct DecodeShape {
   static constexpr int VEC = 16 / ST::bytes;  // elements per 16-byte chunk
@@ -176,9 +178,266 @@ __device__ __forceinline__ int clamp_len(int L, int max_context) {
   return L < 0 ? 0 : (L > max_context ? max_context : L);
 }
 
+// One wavefront's part of a decode work item: the G q heads of one KV head
+// against the key tiles first, first + kWaves, first + 2 kWaves, ... of one
+// sequence.  The lane geometry of the QK butterfly and of the PV token
+// groups, the q registers, the online softmax state and the tile walk.  (The
+// state is kept free of lane-dependent indexing -- a lane's own head is
+// picked by selects -- so the compiler keeps it in registers.)
+template <typename ST, int D, int BS, int G, typename AT = ST>
+struct DecodeWave {
+  static constexpr int TS = decode_tile<ST, D, G>(BS);  // tokens per key tile
+  static constexpr int SUB = BS / TS;                   // tiles per block
+  using S = DecodeShape<ST, D, TS, G>;
+  static constexpr int VEC = S::VEC, LPR = S::LPR, RPI = S::RPI, NI = S::NI, NV = S::NV, NRED = S::NRED,
+                       CPD = S::CPD;
+  static constexpr int QCH = VEC * AT::bytes / 16;  // 16-byte q chunks per K chunk
+  static_assert(ST::bytes == AT::bytes || (ST::bytes == 1 && AT::bytes == 2), "pool / activation types");
+  using elem = typename ST::elem;
+  using aelem = typename AT::elem;
+
+  int lane, seg, row, tg, h_own, i_own;
+  bool owner;
+  u32x4 qv[G][QCH];
+  float m[G], acc[G][NI];
+  float l_own;
+
+  __device__ __forceinline__ DecodeWave() {
+    lane = lane_id();
+    seg = lane % LPR;  // 16-byte chunk of a K row
+    row = lane / LPR;  // K row within a load instruction
+    tg = lane % CPD;   // V token group: tokens tg*VEC .. tg*VEC+VEC-1
+    // where this lane's reduced scores sit: head h_own, tokens i*RPI + row
+    int off = 0;
+#pragma unroll
+    for (int t = 0; t < S::HALV; ++t) off += (seg & (LPR >> (t + 1))) ? (NV >> (t + 1)) : 0;
+    h_own = off / NI;
+    i_own = off % NI;
+    owner = true;  // one lane per distinct reduced value counts it in l
+#pragma unroll
+    for (int t = S::HALV; t < ilog2(LPR); ++t) owner = owner && !(seg & (LPR >> (t + 1)));
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      m[h] = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < NI; ++i) acc[h][i] = 0.f;
+    }
+    l_own = 0.f;
+  }
+
+  __device__ __forceinline__ void load_q(const DecodeParams& P, int s, int kvh) {
+    const aelem* __restrict__ q = static_cast<const aelem*>(P.q);
+    const aelem* qrow = q + (static_cast<int64_t>(s) * P.num_kv_heads * G + kvh * G) * D + seg * VEC;
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int c = 0; c < QCH; ++c) qv[h][c] = load16(qrow + h * D + c * (16 / AT::bytes));
+  }
+
+  // Tiles first, first + stride, ... (count of them; absolute tile indices
+  // of the sequence, TS tokens each) of KV head kvh of sequence s; keys at
+  // or past tok_end are masked out.  pw: this wavefront's G * TS floats of
+  // LDS for the probabilities.
+  __device__ __forceinline__ void walk(const DecodeParams& P, float* pw, int s, int kvh, int first, int stride,
+                                       int count, int tok_end) {
+    const elem* __restrict__ kc = static_cast<const elem*>(P.kc);
+    const elem* __restrict__ vc = static_cast<const elem*>(P.vc);
+    const float scale_log2 = P.scale_log2;
+    const int32_t* trow = P.tables + static_cast<int64_t>(s) * P.max_blocks;
+    const int64_t head_off = static_cast<int64_t>(kvh) * BS * D;
+    const int64_t blk_stride = static_cast<int64_t>(P.num_kv_heads) * BS * D;
+    const int lane_off = lane * VEC;
+    // a V^T tile part is TS keys of each of D rows (rows BS apart)
+    const int v_lane_off = SUB == 1 ? lane_off : (lane / CPD) * BS + (lane % CPD) * VEC;
+    const int num_blocks = P.num_blocks;
+
+    // address of a tile from its physical block id (never dereferenced out
+    // of range); the K chunks are issued before the V chunks so the scores
+    // can start while V is still arriving
+    auto tile_base = [&](int b) __attribute__((always_inline)) -> int64_t {
+      b = (b >= 0 && b < num_blocks) ? b : 0;
+      return static_cast<int64_t>(b) * blk_stride + head_off;
+    };
+    auto load_k = [&](int b, int sub, u32x4* kr) __attribute__((always_inline)) {
+      const int64_t kbase = tile_base(b) + sub * TS * D + lane_off;
+#pragma unroll
+      for (int i = 0; i < NI; ++i) kr[i] = load16_nt(kc + kbase + i * 64 * VEC);
+    };
+    auto load_v = [&](int b, int sub, u32x4* vr) __attribute__((always_inline)) {
+      const int64_t vbase = tile_base(b) + sub * TS + v_lane_off;
+#pragma unroll
+      for (int i = 0; i < NI; ++i) vr[i] = load16_nt(vc + vbase + i * (64 / CPD) * BS);
+    };
+    auto load_tile = [&](int b, int sub, u32x4* kr, u32x4* vr) __attribute__((always_inline)) {
+      load_k(b, sub, kr);
+      load_v(b, sub, vr);
+    };
+
+    // QK, the online-softmax update and the tile's probabilities in LDS;
+    // each head's rescale factor is left in alpha
+    auto scores = [&](int t, const u32x4* kr, float* alpha) __attribute__((always_inline)) {
+      const int t0 = t * TS;  // first token of the tile
+      const bool partial = t0 + TS > tok_end;
+      // QK partial dot products, index h*NI + i
+      float v[NV];
+#pragma unroll
+      for (int h = 0; h < G; ++h)
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+          if constexpr (ST::bytes == 1)
+            v[h * NI + i] = dot_fp8<AT>(qv[h], kr[i], 0.f);
+          else
+            v[h * NI + i] = dot16<ST>(qv[h][0], kr[i], 0.f);
+        }
+      RowReduce<NV, LPR, 0>::run(v, seg);
+      float bm = -INFINITY;
+#pragma unroll
+      for (int j2 = 0; j2 < NRED; ++j2) {
+        float x = v[j2] * scale_log2;
+        if (partial) x = (t0 + (i_own + j2) * RPI + row < tok_end) ? x : -INFINITY;
+        v[j2] = x;
+        bm = fmaxf(bm, x);
+      }
+      // block max of each head, known to every lane
+      bm = max_steps<LPR, S::LOG_G, S::HALV>(bm);
+      bm = rows_max<LPR>(bm);
+      float bmh[G];
+      bmh[0] = bm;
+      if constexpr (S::LOG_G > 0) RowBroadcast<G, LPR, S::LOG_G - 1>::run(bmh, seg);
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const float mn = fmaxf(m[h], bmh[h]);
+        alpha[h] = __builtin_amdgcn_exp2f(m[h] - mn);
+        m[h] = mn;
+      }
+      // this lane's head's max and rescale factor, by selects (a lane-dependent
+      // index into the state would keep it out of registers)
+      float m_own = m[0], alpha_own = alpha[0];
+#pragma unroll
+      for (int h = 1; h < G; ++h) {
+        m_own = h_own == h ? m[h] : m_own;
+        alpha_own = h_own == h ? alpha[h] : alpha_own;
+      }
+      // probabilities of this lane's scores, shared through LDS
+      float ps = 0.f;
+#pragma unroll
+      for (int j2 = 0; j2 < NRED; ++j2) {
+        const float p = __builtin_amdgcn_exp2f(v[j2] - m_own);
+        ps += p;
+        pw[h_own * TS + (i_own + j2) * RPI + row] = p;
+      }
+      l_own = l_own * alpha_own + (owner ? ps : 0.f);
+      wave_lds_sync();
+    };
+
+    // PV of the tile's probabilities (V rows past tok_end zeroed: a zero
+    // probability would not cancel a NaN)
+    auto accumulate = [&](int t, const u32x4* vr, const float* alpha) __attribute__((always_inline)) {
+      const int t0 = t * TS;
+      const bool partial = t0 + TS > tok_end;
+      float vt[NI][VEC];
+#pragma unroll
+      for (int i = 0; i < NI; ++i) widen16<ST>(vr[i], vt[i]);
+      if (partial) {
+#pragma unroll
+        for (int c = 0; c < VEC; ++c) {
+          const bool ok = t0 + tg * VEC + c < tok_end;
+#pragma unroll
+          for (int i = 0; i < NI; ++i) vt[i][c] = ok ? vt[i][c] : 0.f;
+        }
+      }
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        float p[VEC];
+#pragma unroll
+        for (int c = 0; c < VEC; c += 4) {
+          const float4 x = *reinterpret_cast<const float4*>(pw + h * TS + tg * VEC + c);
+          p[c] = x.x;
+          p[c + 1] = x.y;
+          p[c + 2] = x.z;
+          p[c + 3] = x.w;
+        }
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+          float a = acc[h][i] * alpha[h];
+#pragma unroll
+          for (int c = 0; c < VEC; ++c) a = __builtin_fmaf(p[c], vt[i][c], a);
+          acc[h][i] = a;
+        }
+      }
+      wave_lds_sync();  // the next tile's probabilities overwrite pw
+    };
+
+    auto process = [&](int t, const u32x4* kr, const u32x4* vr) __attribute__((always_inline)) {
+      float alpha[G];
+      scores(t, kr, alpha);
+      accumulate(t, vr, alpha);
+    };
+
+    // The tiles in chunks of 64: one vector load brings the chunk's
+    // block-table entries into a VGPR (read back with v_readlane), then a
+    // software pipeline over NBUF register buffers keeps the loads of tile
+    // j + NBUF - 1 in flight while tile j is processed.  In the steady state
+    // every prefetched tile exists, so no load is conditional and each wait
+    // covers only the tile about to be used; the last tiles of a chunk run in
+    // an unrolled tail.  (Reloading K of tile j + 1 as soon as tile j's
+    // scores are done, before its PV, keeps both halves of a tile live at
+    // once: 256 registers and one wavefront per SIMD at 4 q heads per KV
+    // head, against 168 and three.)
+    for (int c0 = 0; c0 < count; c0 += 64) {
+      const int cn = min(64, count - c0);
+      const int tv = lane < cn ? trow[(first + (c0 + lane) * stride) / SUB] : 0;
+      auto block_id = [&](int j) __attribute__((always_inline)) -> int { return __builtin_amdgcn_readlane(tv, j); };
+      auto sub_of = [&](int j) __attribute__((always_inline)) -> int { return SUB == 1 ? 0 : (first + (c0 + j) * stride) % SUB; };
+      auto tile_of = [&](int j) __attribute__((always_inline)) -> int { return first + (c0 + j) * stride; };
+      constexpr int NB = S::NBUF;
+      u32x4 kb[NB][NI], vb[NB][NI];
+#pragma unroll
+      for (int b = 0; b < NB - 1; ++b)
+        if (b < cn) load_tile(block_id(b), sub_of(b), kb[b], vb[b]);
+      int j0 = 0;
+      for (; j0 + 2 * NB - 2 < cn; j0 += NB) {
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+          load_tile(block_id(j0 + b + NB - 1), sub_of(j0 + b + NB - 1), kb[(b + NB - 1) % NB],
+                    vb[(b + NB - 1) % NB]);
+          process(tile_of(j0 + b), kb[b], vb[b]);
+        }
+      }
+#pragma unroll
+      for (int b = 0; b < 2 * NB - 1; ++b) {
+        const int j = j0 + b;
+        if (j < cn) {
+          if (j + NB - 1 < cn)
+            load_tile(block_id(j + NB - 1), sub_of(j + NB - 1), kb[(b + NB - 1) % NB], vb[(b + NB - 1) % NB]);
+          process(tile_of(j), kb[b % NB], vb[b % NB]);
+        }
+      }
+    }
+  }
+
+  // Row sums of every head (sum over the lanes holding that head's tokens,
+  // then the G heads gathered), and the PV partial sums of each V row
+  // combined over its token groups (valid in lanes with tg == 0).
+  __device__ __forceinline__ void finish(float* lh) {
+    float x = sum_steps<LPR, S::LOG_G, ilog2(LPR)>(l_own);
+    x = rows_sum<LPR>(x);
+    lh[0] = x;
+    if constexpr (S::LOG_G > 0) RowBroadcast<G, LPR, S::LOG_G - 1>::run(lh, seg);
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int i = 0; i < NI; ++i) acc[h][i] = groups_sum<1, CPD>(acc[h][i]);
+  }
+
+  // head_dim index of acc[h][i] in a lane with tg == 0
+  __device__ __forceinline__ int dim_of(int i) const { return (i * 64 + lane) / CPD; }
+};
+
 // One work item: the G q heads of KV head `kvh` of sequence `s` over the
-// tokens of partition `part` (the whole context when it is the only one).
-// L is the sequence's clamped context length.  With one partition the
+// tokens of partition `part` (the whole context when it is the only one),
+// read by the workgroup's four wavefronts taking the partition's tiles round
+// robin.  L is the sequence's clamped context length.  With one partition the
 // normalised rows are written to `out`, otherwise (m, l, o) partials go to
 // the workspace.  Prefix-grouped decode passes the first token of the
 // sequence's own part as `start` (the partitions then cover start..L-1) and
@@ -189,30 +448,14 @@ __device__ __forceinline__ int clamp_len(int L, int max_context) {
 template <typename ST, int D, int BS, int G, typename AT = ST>
 __device__ __forceinline__ void decode_item(DecodeLds<G, D, BS>& sh, const DecodeParams& P, int s, int kvh,
                                             int part, int L, int start = 0, int slot0 = 0, bool partial = false) {
-  constexpr int TS = decode_tile<ST, D, G>(BS);  // tokens per key tile
-  constexpr int SUB = BS / TS;         // tiles per block
-  using S = DecodeShape<ST, D, TS, G>;
-  constexpr int VEC = S::VEC, LPR = S::LPR, RPI = S::RPI, NI = S::NI, NV = S::NV, NRED = S::NRED,
-                CPD = S::CPD;
-  constexpr int QCH = VEC * AT::bytes / 16;  // 16-byte q chunks per K chunk
-  static_assert(ST::bytes == AT::bytes || (ST::bytes == 1 && AT::bytes == 2), "pool / activation types");
-  using elem = typename ST::elem;
+  using W = DecodeWave<ST, D, BS, G, AT>;
+  constexpr int TS = W::TS, NI = W::NI;
   using aelem = typename AT::elem;
-  const aelem* __restrict__ q = static_cast<const aelem*>(P.q);
-  const elem* __restrict__ kc = static_cast<const elem*>(P.kc);
-  const elem* __restrict__ vc = static_cast<const elem*>(P.vc);
   aelem* __restrict__ out = static_cast<aelem*>(P.out);
-  const int num_kv_heads = P.num_kv_heads;
-  const int num_q_heads = num_kv_heads * G;
+  const int num_q_heads = P.num_kv_heads * G;
   const int part_tokens = P.part_tokens;
-  const float scale_log2 = P.scale_log2;
-
   const int tid = threadIdx.x;
-  const int lane = lane_id();
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int seg = lane % LPR;  // 16-byte chunk of a K row
-  const int row = lane / LPR;  // K row within a load instruction
-  const int tg = lane % CPD;   // V token group: tokens tg*VEC .. tg*VEC+VEC-1
 
   const int nparts = L > start ? (L - start + part_tokens - 1) / part_tokens : 0;
   if (L == 0 && !partial) {
@@ -226,201 +469,25 @@ __device__ __forceinline__ void decode_item(DecodeLds<G, D, BS>& sh, const Decod
 
   const int tok_begin = start + part * part_tokens;  // a multiple of BS
   const int tok_end = min(L, tok_begin + part_tokens);
-  const int blk_begin = tok_begin / BS;
   const int tile_begin = tok_begin / TS;                 // a multiple of SUB
   const int nb = (tok_end + TS - 1) / TS - tile_begin;  // key tiles in this partition
+  const int my_tiles = nb > wave ? (nb - wave + kWaves - 1) / kWaves : 0;
 
-  // where this lane's reduced scores sit: head h_own, tokens i*RPI + row
-  int off = 0;
-#pragma unroll
-  for (int t = 0; t < S::HALV; ++t) off += (seg & (LPR >> (t + 1))) ? (NV >> (t + 1)) : 0;
-  const int h_own = off / NI;
-  const int i_own = off % NI;
-  bool owner = true;  // one lane per distinct reduced value counts it in l
-#pragma unroll
-  for (int t = S::HALV; t < ilog2(LPR); ++t) owner = owner && !(seg & (LPR >> (t + 1)));
-
-  u32x4 qv[G][QCH];
-  const aelem* qrow = q + (static_cast<int64_t>(s) * num_q_heads + kvh * G) * D + seg * VEC;
-#pragma unroll
-  for (int h = 0; h < G; ++h)
-#pragma unroll
-    for (int c = 0; c < QCH; ++c) qv[h][c] = load16(qrow + h * D + c * (16 / AT::bytes));
-
-  float m[G], acc[G][NI];
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    m[h] = -INFINITY;
-#pragma unroll
-    for (int i = 0; i < NI; ++i) acc[h][i] = 0.f;
-  }
-  float l_own = 0.f;
-
-  const int32_t* trow = P.tables + static_cast<int64_t>(s) * P.max_blocks + blk_begin;
-  const int64_t head_off = static_cast<int64_t>(kvh) * BS * D;
-  const int64_t blk_stride = static_cast<int64_t>(num_kv_heads) * BS * D;
-  const int lane_off = lane * VEC;
-  // a V^T tile part is TS keys of each of D rows (rows BS apart)
-  const int v_lane_off = SUB == 1 ? lane_off : (lane / CPD) * BS + (lane % CPD) * VEC;
-  const int num_blocks = P.num_blocks;
-
-  const int my_blocks = nb > wave ? (nb - wave + kWaves - 1) / kWaves : 0;
-
-  // address of a tile from its physical block id (never dereferenced out of range)
-  auto load_tile = [&](int b, int sub, u32x4* kr, u32x4* vr) {
-    b = (b >= 0 && b < num_blocks) ? b : 0;
-    const int64_t base = static_cast<int64_t>(b) * blk_stride + head_off;
-    const int64_t kbase = base + sub * TS * D + lane_off;
-    const int64_t vbase = base + sub * TS + v_lane_off;
-#pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      kr[i] = load16_nt(kc + kbase + i * 64 * VEC);
-      vr[i] = load16_nt(vc + vbase + i * (64 / CPD) * BS);
-    }
-  };
-
-  float* pw = &sh.p_lds[wave][0][0];
-
-  auto process = [&](int j, const u32x4* kr, const u32x4* vr) {
-    const int t0 = (tile_begin + wave + j * kWaves) * TS;  // first token of the tile
-    const bool partial = t0 + TS > tok_end;
-    // QK partial dot products, index h*NI + i
-    float v[NV];
-#pragma unroll
-    for (int h = 0; h < G; ++h)
-#pragma unroll
-      for (int i = 0; i < NI; ++i) {
-        if constexpr (ST::bytes == 1)
-          v[h * NI + i] = dot_fp8<AT>(qv[h], kr[i], 0.f);
-        else
-          v[h * NI + i] = dot16<ST>(qv[h][0], kr[i], 0.f);
-      }
-    RowReduce<NV, LPR, 0>::run(v, seg);
-    float bm = -INFINITY;
-#pragma unroll
-    for (int j2 = 0; j2 < NRED; ++j2) {
-      float x = v[j2] * scale_log2;
-      if (partial) x = (t0 + (i_own + j2) * RPI + row < tok_end) ? x : -INFINITY;
-      v[j2] = x;
-      bm = fmaxf(bm, x);
-    }
-    // block max of each head, known to every lane
-    bm = max_steps<LPR, S::LOG_G, S::HALV>(bm);
-    bm = rows_max<LPR>(bm);
-    float bmh[G];
-    bmh[0] = bm;
-    if constexpr (S::LOG_G > 0) RowBroadcast<G, LPR, S::LOG_G - 1>::run(bmh, seg);
-    float alpha[G];
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const float mn = fmaxf(m[h], bmh[h]);
-      alpha[h] = __builtin_amdgcn_exp2f(m[h] - mn);
-      m[h] = mn;
-    }
-    // probabilities of this lane's scores, shared through LDS
-    float ps = 0.f;
-#pragma unroll
-    for (int j2 = 0; j2 < NRED; ++j2) {
-      const float p = __builtin_amdgcn_exp2f(v[j2] - m[h_own]);
-      ps += p;
-      pw[h_own * TS + (i_own + j2) * RPI + row] = p;
-    }
-    l_own = l_own * alpha[h_own] + (owner ? ps : 0.f);
-    wave_lds_sync();
-
-    float vt[NI][VEC];
-#pragma unroll
-    for (int i = 0; i < NI; ++i) widen16<ST>(vr[i], vt[i]);
-    if (partial) {
-#pragma unroll
-      for (int c = 0; c < VEC; ++c) {
-        const bool ok = t0 + tg * VEC + c < tok_end;
-#pragma unroll
-        for (int i = 0; i < NI; ++i) vt[i][c] = ok ? vt[i][c] : 0.f;
-      }
-    }
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      float p[VEC];
-#pragma unroll
-      for (int c = 0; c < VEC; c += 4) {
-        const float4 x = *reinterpret_cast<const float4*>(pw + h * TS + tg * VEC + c);
-        p[c] = x.x;
-        p[c + 1] = x.y;
-        p[c + 2] = x.z;
-        p[c + 3] = x.w;
-      }
-#pragma unroll
-      for (int i = 0; i < NI; ++i) {
-        float a = acc[h][i] * alpha[h];
-#pragma unroll
-        for (int c = 0; c < VEC; ++c) a = __builtin_fmaf(p[c], vt[i][c], a);
-        acc[h][i] = a;
-      }
-    }
-    wave_lds_sync();  // the next tile's probabilities overwrite pw
-  };
-
-  // The wave's tiles in chunks of 64: one vector load brings the chunk's
-  // block-table entries into a VGPR (read back with v_readlane), then a
-  // software pipeline over NBUF register buffers keeps the loads of tile
-  // j + NBUF - 1 in flight while tile j is processed.  In the steady state
-  // every prefetched tile exists, so no load is conditional and each wait
-  // covers only the tile about to be used; the last tiles of a chunk run in
-  // an unrolled tail.
-  for (int c0 = 0; c0 < my_blocks; c0 += 64) {
-    const int cn = min(64, my_blocks - c0);
-    const int tv = lane < cn ? trow[(wave + (c0 + lane) * kWaves) / SUB] : 0;
-    auto block_id = [&](int j) -> int { return __builtin_amdgcn_readlane(tv, j); };
-    auto sub_of = [&](int j) -> int { return SUB == 1 ? 0 : (wave + (c0 + j) * kWaves) % SUB; };
-    constexpr int NB = S::NBUF;
-    u32x4 kb[NB][NI], vb[NB][NI];
-#pragma unroll
-    for (int b = 0; b < NB - 1; ++b)
-      if (b < cn) load_tile(block_id(b), sub_of(b), kb[b], vb[b]);
-    int j0 = 0;
-    for (; j0 + 2 * NB - 2 < cn; j0 += NB) {
-#pragma unroll
-      for (int b = 0; b < NB; ++b) {
-        load_tile(block_id(j0 + b + NB - 1), sub_of(j0 + b + NB - 1), kb[(b + NB - 1) % NB], vb[(b + NB - 1) % NB]);
-        process(c0 + j0 + b, kb[b], vb[b]);
-      }
-    }
-#pragma unroll
-    for (int b = 0; b < 2 * NB - 1; ++b) {
-      const int j = j0 + b;
-      if (j < cn) {
-        if (j + NB - 1 < cn)
-          load_tile(block_id(j + NB - 1), sub_of(j + NB - 1), kb[(b + NB - 1) % NB], vb[(b + NB - 1) % NB]);
-        process(c0 + j, kb[b % NB], vb[b % NB]);
-      }
-    }
-  }
-
-  // l of every head: sum over the lanes holding that head's tokens, then
-  // gather the G heads
+  W w;
+  w.load_q(P, s, kvh);
+  w.walk(P, &sh.p_lds[wave][0][0], s, kvh, tile_begin + wave, kWaves, my_tiles, tok_end);
   float lh[G];
-  {
-    float x = sum_steps<LPR, S::LOG_G, ilog2(LPR)>(l_own);
-    x = rows_sum<LPR>(x);
-    lh[0] = x;
-    if constexpr (S::LOG_G > 0) RowBroadcast<G, LPR, S::LOG_G - 1>::run(lh, seg);
-  }
-  // PV partial sums: combine the token groups of each V row
-#pragma unroll
-  for (int h = 0; h < G; ++h)
-#pragma unroll
-    for (int i = 0; i < NI; ++i) acc[h][i] = groups_sum<1, CPD>(acc[h][i]);
-  if (tg == 0) {
+  w.finish(lh);
+  if (w.tg == 0) {
 #pragma unroll
     for (int h = 0; h < G; ++h)
 #pragma unroll
-      for (int i = 0; i < NI; ++i) sh.red_acc[wave][h][(i * 64 + lane) / CPD] = acc[h][i];
+      for (int i = 0; i < NI; ++i) sh.red_acc[wave][h][w.dim_of(i)] = w.acc[h][i];
   }
-  if (lane == 0) {
+  if (w.lane == 0) {
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      sh.red_m[wave][h] = m[h];
+      sh.red_m[wave][h] = w.m[h];
       sh.red_l[wave][h] = lh[h];
     }
   }
@@ -431,15 +498,15 @@ __device__ __forceinline__ void decode_item(DecodeLds<G, D, BS>& sh, const Decod
     const int h = e / D, d = e % D;
     float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w)
-      if (sh.red_l[w][h] > 0.f) M = fmaxf(M, sh.red_m[w][h]);
+    for (int wv = 0; wv < kWaves; ++wv)
+      if (sh.red_l[wv][h] > 0.f) M = fmaxf(M, sh.red_m[wv][h]);
     float num = 0.f, den = 0.f;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      if (sh.red_l[w][h] > 0.f) {
-        const float sc = __builtin_amdgcn_exp2f(sh.red_m[w][h] - M);
-        num = __builtin_fmaf(sh.red_acc[w][h][d], sc, num);
-        den = __builtin_fmaf(sh.red_l[w][h], sc, den);
+    for (int wv = 0; wv < kWaves; ++wv) {
+      if (sh.red_l[wv][h] > 0.f) {
+        const float sc = __builtin_amdgcn_exp2f(sh.red_m[wv][h] - M);
+        num = __builtin_fmaf(sh.red_acc[wv][h][d], sc, num);
+        den = __builtin_fmaf(sh.red_l[wv][h], sc, den);
       }
     }
     const int64_t qh = static_cast<int64_t>(s) * num_q_heads + kvh * G + h;

@@ -299,14 +299,17 @@ def test_calls_from_two_host_threads_on_their_own_streams():
 MERGE_CASES = [  # (Hq, Hkv, D, BS, dtype, context lengths, partition tokens)
     (32, 8, 128, 32, "bf16", [5000, 4999, 37, 1], 32),  # 157 partitions: two passes of 128 merge threads
     (8, 2, 64, 16, "f16", [5000, 3001, 16], 16),  # 313 partitions: five passes of 64 merge threads
+    # 16875 partitions in one row: more weights than 64 KiB of LDS would hold
+    # (the merge keeps no per-partition LDS, so there is no such bound)
+    (8, 2, 64, 16, "f16", [270000, 7], 16),
 ]
 
 
 @pytest.mark.parametrize("case", MERGE_CASES)
 def test_merge_of_more_partitions_than_threads(case):
     """The log-sum-exp merge over more partitions per row than the merge
-    workgroup has threads (one per head_dim element), every row against the
-    oracle."""
+    workgroup has threads, up to more partitions than 64 KiB of LDS could
+    hold one weight for; every row against the oracle."""
     hq, hkv, d, bs, dt, lens, part = case
     wl = workloads.custom(hq, hkv, d, bs, dt, lens, seed=len(lens) * 31 + d)
     print(f"[gpu] merge of {-(-max(lens) // part)} partitions, shape {case[:5]}", flush=True)
