@@ -212,9 +212,9 @@ size_t pa_decode_grouped_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, 
  *                   pa_decode_grouped_workspace_bytes(); rewritten by each
  *                   call, so calls sharing it must be ordered on one stream
  * PA_EUNSUPPORTED above 4096 sequences, or when (num_q_heads /
- * num_kv_heads) * 2 * ceil(max_context_len / partition) exceeds 16384 (the
- * merge's per-head slot weights live in 64 KiB of LDS; with 1024-token
- * partitions that is 1048576 tokens of context at 8 q heads per KV head).  Runs four kernels
+ * num_kv_heads) * 2 * ceil(max_context_len / partition) exceeds 14336 (the
+ * merge's per-head slot weights live in 56 KiB of LDS; with 1024-token
+ * partitions that is 917504 tokens of context at 8 q heads per KV head).  Runs four kernels
  * on `stream`: a one-workgroup planner, the shared-prefix kernel (matrix
  * cores, one chunk's rows per workgroup), the suffix partitions of the split
  * decode kernel, and the log-sum-exp merge. */

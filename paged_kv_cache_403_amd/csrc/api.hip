@@ -78,7 +78,7 @@ size_t workspace_for(int64_t num_seqs, int64_t num_q_heads, int64_t head_dim, in
 // Prefix-grouped decode: partitions of `part` tokens, 2 * ceil(C / part)
 // slots per row (prefix slots of the chunk, then the sequence's own).
 constexpr int32_t kGroupedDefaultPartition = 1024;
-constexpr int64_t kGroupedMergeLds = 64 * 1024;
+constexpr int64_t kGroupedMergeLds = 56 * 1024;  // slot weights (dynamic); the merge kernel also holds 4 KiB of its own
 
 struct GroupedLayout {
   int64_t parts, slots;

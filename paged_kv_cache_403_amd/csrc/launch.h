@@ -37,7 +37,7 @@ struct GroupedArgs {
   int32_t* seq_start;   // [S]  shared tokens of each sequence (its own part starts there)
   int32_t* slot_base;   // [S]  prefix slots of its chunk
   int32_t* nslots;      // [S]
-  int32_t* pre_items;   // [S * ceil(max_context / part)][4]  (first member, members, partition, reference)
+  int32_t* pre_items;   // [S * ceil(max_context / part) / 2][8]  (first member, members, partition, reference, shared length)
   int32_t* pre_count;   // [1]
 };
 

@@ -181,7 +181,7 @@ def _grouped(cache, num_seqs=4, num_q_heads=32, max_blocks=8, max_ctx=100, scale
     (dict(q=0), P.PA_EINVAL),
     (dict(ws=0), P.PA_EWORKSPACE),
     (dict(ws_bytes=64), P.PA_EWORKSPACE),
-    (dict(num_q_heads=64, max_blocks=80000, max_ctx=1200000), P.PA_EUNSUPPORTED),  # merge weights over 64 KiB
+    (dict(num_q_heads=64, max_blocks=80000, max_ctx=1200000), P.PA_EUNSUPPORTED),  # merge weights over 56 KiB
 ])
 def test_grouped_decode_validation(kw, code):
     assert _grouped(_cache(), **kw) == code
