@@ -509,6 +509,8 @@ def main():
                     help="decode partition tokens (0 one pass, -1 library choice; default: the workload's "
                          "stated partitions, else -1)")
     ap.add_argument("--headline-only", action="store_true", help="time the headline step only")
+    ap.add_argument("--grouped", action="store_true",
+                    help="also time prefix-grouped decode of the workload's decode batch")
     ap.add_argument("--no-flush", action="store_true", help="no cache flush between timed iterations")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-configs", action="store_true", help="skip the other configurations")
@@ -589,6 +591,8 @@ def main():
             "kernel": ("pa_decode: decode_plan_kernel + decode_persistent_kernel + decode_reduce_kernel"
                        if st.part_used and st.part_used < st.max_dec else "pa_decode: decode_kernel"),
             "bytes_per_launch": st.dec_bytes, "launch_us": head["us"]}
+    if args.grouped:
+        result["grouped"] = grouped_entry(st, timer, K, W)
     if not args.headline_only:
         configs = {}
         if not args.no_configs:
