@@ -253,6 +253,35 @@ const char* pa_status_str(int status);
  * thread's next call into the library. */
 const char* pa_last_error(void);
 
+/* ---- checking build ------------------------------------------------------
+ * libpagedattn_debug.so is this library compiled with PA_DEBUG.  Its kernels
+ * behave as the product's and also count, in counters each device holds,
+ * the device metadata that the trust rule above has them clamp or skip:
+ *   PA_DBG_BLOCK_ID     a block-table entry inside a sequence's length that
+ *                       is outside [0, num_blocks) (read as block 0)
+ *   PA_DBG_CONTEXT_LEN  a context length outside [0, max_context_len), or,
+ *                       in pa_prefill_chunk, shorter than its query rows
+ *   PA_DBG_SLOT         pa_kv_append: a slot >= num_blocks * block_size
+ *                       (skipped; a negative slot is the documented skip
+ *                       and is not counted)
+ *   PA_DBG_COPY_PAIR    pa_copy_blocks: a pair whose src or dst is outside
+ *                       [0, num_blocks) (skipped)
+ * Slots and pairs are counted once each; the attention kinds count the
+ * lanes that met the case, a figure that depends on the launch shape, so
+ * zero versus nonzero is what they tell.
+ * pa_debug_counters waits for the current device to go idle, writes the
+ * counters of that device into counts (host uint64 [PA_DBG_KINDS]) and, when
+ * reset is nonzero, clears them.  PA_EINVAL for a NULL counts; the product
+ * library returns PA_EUNSUPPORTED and writes nothing. */
+typedef enum {
+  PA_DBG_BLOCK_ID = 0,
+  PA_DBG_CONTEXT_LEN = 1,
+  PA_DBG_SLOT = 2,
+  PA_DBG_COPY_PAIR = 3,
+  PA_DBG_KINDS = 4
+} pa_debug_kind;
+int pa_debug_counters(uint64_t* counts, int32_t reset);
+
 /* ---- host block manager (CPU only, no HIP calls) -------------------------
  * Bookkeeping of the paged cache (lshu.cn/news/11644, "方案：页式内存管理" and
  * "收益分析"): one global pool; a FIFO free pool (blocks handed out from the

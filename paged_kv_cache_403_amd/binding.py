@@ -8,6 +8,7 @@ no CPU fallback, and loading fails loudly when the shared library is missing.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 
@@ -15,11 +16,13 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 # PAGEDATTN_LIB names another build of this same library (the sanitizer
-# build, libpagedattn_san.so, which the CPU tests load)
+# build, libpagedattn_san.so, which the CPU tests load, or the checking build
+# libpagedattn_debug.so)
 LIB_PATH = os.environ.get("PAGEDATTN_LIB") or os.path.join(_HERE, "libpagedattn.so")
 
 PA_F32, PA_F16, PA_BF16, PA_FP8_E4M3 = 0, 1, 2, 3
 PA_OK, PA_EINVAL, PA_EUNSUPPORTED, PA_EWORKSPACE, PA_ENOMEM, PA_EHIP = range(6)
+PA_DBG_BLOCK_ID, PA_DBG_CONTEXT_LEN, PA_DBG_SLOT, PA_DBG_COPY_PAIR, PA_DBG_KINDS = range(5)
 
 
 class PagedAttnError(RuntimeError):
@@ -69,6 +72,7 @@ _SIGNATURES = {
                                         ctypes.c_float, _vp]),
     "pa_status_str": (ctypes.c_char_p, [ctypes.c_int]),
     "pa_last_error": (ctypes.c_char_p, []),
+    "pa_debug_counters": (ctypes.c_int, [_vp, _i32]),
     "pa_bm_create": (_vp, [_i32, _i32, _vp, _i32]),
     "pa_bm_destroy": (None, [_vp]),
     "pa_bm_add_seq": (ctypes.c_int, [_vp, _i32]),
@@ -102,20 +106,39 @@ class pa_sched_batch(ctypes.Structure):
     ]
 
 
+def load(path: str):
+    """A handle on the build of this library at `path`, every entry point's
+    signature set; raises if it has not been built."""
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python __graft_entry__.py` "
+                           "or paged_kv_cache_403_amd.build.build()")
+    h = ctypes.CDLL(path)
+    for name, (res, args) in _SIGNATURES.items():
+        f = getattr(h, name)
+        f.restype = res
+        f.argtypes = args
+    return h
+
+
 def lib():
-    """The loaded library; raises if it has not been built."""
+    """The loaded library (the build at LIB_PATH unless `using` says else)."""
     global _lib
     if _lib is None:
-        if not os.path.exists(LIB_PATH):
-            raise RuntimeError(f"{LIB_PATH} is missing: build it with `python __graft_entry__.py` "
-                               "or paged_kv_cache_403_amd.build.build()")
-        h = ctypes.CDLL(LIB_PATH)
-        for name, (res, args) in _SIGNATURES.items():
-            f = getattr(h, name)
-            f.restype = res
-            f.argtypes = args
-        _lib = h
+        _lib = load(LIB_PATH)
     return _lib
+
+
+@contextlib.contextmanager
+def using(handle):
+    """Route every wrapper of this module through `handle` (a `load` of
+    another build, such as the checking build) inside the block."""
+    global _lib
+    prev = lib()
+    _lib = handle
+    try:
+        yield handle
+    finally:
+        _lib = prev
 
 
 def exported_symbols():
@@ -129,6 +152,15 @@ def status_str(status: int) -> str:
 def _check(rc: int, where: str):
     if rc != PA_OK:
         raise PagedAttnError(rc, where)
+
+
+def pa_debug_counters(reset: bool = False) -> np.ndarray:
+    """The checking build's counters of the current device (uint64
+    [PA_DBG_KINDS], indexed by PA_DBG_*); raises PagedAttnError with
+    PA_EUNSUPPORTED on the product library."""
+    out = np.zeros(PA_DBG_KINDS, dtype=np.uint64)
+    _check(lib().pa_debug_counters(out.ctypes.data, int(bool(reset))), "pa_debug_counters")
+    return out
 
 
 # ---- tensor marshalling -------------------------------------------------------------

@@ -12,6 +12,11 @@ UndefinedBehaviorSanitizer (clang's runtimes; the device kernels are the
 unchanged objects of the normal build, and no device code is instrumented).
 The CPU tests load it with the ASan runtime preloaded (see
 tests/test_sanitized_host.py); it is a checking build, never the product.
+
+build(debug=True) additionally builds libpagedattn_debug.so: every HIP source
+compiled with -DPA_DEBUG, so that the kernels count the device metadata
+(block ids, context lengths, slots, copy pairs) they clamp or skip, read back
+with pa_debug_counters.  Also a checking build, loaded through PAGEDATTN_LIB.
 """
 import os
 import shutil
@@ -25,8 +30,10 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(HERE, "_build")
 BUILD_SAN = os.path.join(HERE, "_build_san")
+BUILD_DEBUG = os.path.join(HERE, "_build_debug")
 LIB = os.path.join(HERE, "libpagedattn.so")
 LIB_SAN = os.path.join(HERE, "libpagedattn_san.so")
+LIB_DEBUG = os.path.join(HERE, "libpagedattn_debug.so")
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
@@ -75,7 +82,7 @@ def asan_runtime() -> str:
     return r.stdout.strip()
 
 
-def build(verbose: bool = False, jobs: int | None = None, sanitize: bool = True) -> str:
+def build(verbose: bool = False, jobs: int | None = None, sanitize: bool = True, debug: bool = True) -> str:
     os.makedirs(BUILD, exist_ok=True)
     hip_srcs = sorted(f for f in os.listdir(CSRC) if f.endswith(".hip"))
     cpp_srcs = sorted(f for f in os.listdir(CSRC) if f.endswith(".cpp"))
@@ -99,6 +106,13 @@ def build(verbose: bool = False, jobs: int | None = None, sanitize: bool = True)
             o = os.path.join(BUILD_SAN, f + ".o")
             cmds.append([CLANGXX, *CXX_SAN_FLAGS, "-c", os.path.join(CSRC, f), "-o", o])
             san_objs.append(o)
+    debug_objs = []
+    if debug:
+        os.makedirs(BUILD_DEBUG, exist_ok=True)
+        for f in hip_srcs:
+            o = os.path.join(BUILD_DEBUG, f + ".o")
+            cmds.append([HIPCC, *HIP_FLAGS, "-DPA_DEBUG", "-c", os.path.join(CSRC, f), "-o", o])
+            debug_objs.append(o)
     jobs = jobs or min(8, len(os.sched_getaffinity(0)))
     with ThreadPoolExecutor(jobs) as ex:
         list(ex.map(lambda c: _run(c, verbose), cmds))
@@ -106,6 +120,8 @@ def build(verbose: bool = False, jobs: int | None = None, sanitize: bool = True)
     if sanitize:
         plain = [o for o in objs if not any(os.path.basename(o).startswith(f) for f in SAN_HIP + tuple(cpp_srcs))]
         _link(plain + san_objs, LIB_SAN, verbose)
+    if debug:
+        _link(debug_objs + [o for o in objs if o.endswith(".cpp.o")], LIB_DEBUG, verbose)
     return LIB
 
 

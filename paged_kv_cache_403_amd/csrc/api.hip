@@ -138,6 +138,25 @@ const char* pa_status_str(int status) {
 
 const char* pa_last_error(void) { return g_last_hip_error; }
 
+int pa_debug_counters(uint64_t* counts, int32_t reset) {
+#ifdef PA_DEBUG
+  if (!counts) return PA_EINVAL;
+  hipError_t e = hipDeviceSynchronize();
+  if (e != hipSuccess) return hip_status(e);
+  unsigned long long acc[PA_DBG_KINDS] = {};
+  const bool r = reset != 0;
+  if ((e = pa::debug_counts_decode(acc, r)) != hipSuccess || (e = pa::debug_counts_grouped(acc, r)) != hipSuccess ||
+      (e = pa::debug_counts_prefill(acc, r)) != hipSuccess || (e = pa::debug_counts_kv_cache_ops(acc, r)) != hipSuccess)
+    return hip_status(e);
+  for (int k = 0; k < PA_DBG_KINDS; ++k) counts[k] = acc[k];
+  return PA_OK;
+#else
+  (void)counts;
+  (void)reset;
+  return PA_EUNSUPPORTED;
+#endif
+}
+
 int pa_kv_append(const pa_cache* cache, const void* k_new, const void* v_new, const int64_t* slot_mapping,
                  int32_t num_tokens, void* stream) {
   int rc = check_cache(cache);

@@ -6,6 +6,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "pagedattn.h"
+
 namespace pa {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -218,5 +220,37 @@ struct XorLane {
 };
 
 constexpr int ilog2(int x) { return x <= 1 ? 0 : 1 + ilog2(x / 2); }
+
+// Checking build (PA_DEBUG): the kernels count the device metadata they
+// clamp or skip (PA_DEBUG_COUNT, kinds pa_debug_kind; in the product build it
+// expands to no code at all) in counters of their own translation
+// unit -- the library is linked without relocatable device code, so each
+// unit's code object holds its own copy -- and PA_DEBUG_UNIT(name) gives the
+// unit a host function debug_counts_<name> that adds them into a host array
+// and optionally clears them.
+#ifdef PA_DEBUG
+namespace dbg {
+static __device__ unsigned long long counts[PA_DBG_KINDS];
+}
+#define PA_DEBUG_COUNT(kind, hit)                                 \
+  do {                                                            \
+    if (hit) atomicAdd(&::pa::dbg::counts[kind], 1ull);           \
+  } while (0)
+#define PA_DEBUG_UNIT(name)                                                                            \
+  hipError_t debug_counts_##name(unsigned long long* acc, bool reset) {                               \
+    unsigned long long v[PA_DBG_KINDS];                                                                \
+    hipError_t e = hipMemcpyFromSymbol(v, HIP_SYMBOL(dbg::counts), sizeof(v), 0, hipMemcpyDeviceToHost); \
+    if (e != hipSuccess) return e;                                                                     \
+    for (int k = 0; k < PA_DBG_KINDS; ++k) acc[k] += v[k];                                             \
+    if (!reset) return hipSuccess;                                                                     \
+    const unsigned long long z[PA_DBG_KINDS] = {};                                                     \
+    return hipMemcpyToSymbol(HIP_SYMBOL(dbg::counts), z, sizeof(z), 0, hipMemcpyHostToDevice);        \
+  }
+#else
+#define PA_DEBUG_COUNT(kind, hit) \
+  do {                            \
+  } while (0)
+#define PA_DEBUG_UNIT(name)
+#endif
 
 }  // namespace pa

@@ -422,4 +422,6 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t st) {
   return hipErrorInvalidValue;
 }
 
+PA_DEBUG_UNIT(decode)
+
 }  // namespace pa

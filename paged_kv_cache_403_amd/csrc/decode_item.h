@@ -175,6 +175,7 @@ struct DecodeLds {
 };
 
 __device__ __forceinline__ int clamp_len(int L, int max_context) {
+  PA_DEBUG_COUNT(PA_DBG_CONTEXT_LEN, L < 0 || L > max_context);
   return L < 0 ? 0 : (L > max_context ? max_context : L);
 }
 
@@ -387,6 +388,7 @@ struct DecodeWave {
     for (int c0 = 0; c0 < count; c0 += 64) {
       const int cn = min(64, count - c0);
       const int tv = lane < cn ? trow[(first + (c0 + lane) * stride) / SUB] : 0;
+      PA_DEBUG_COUNT(PA_DBG_BLOCK_ID, tv < 0 || tv >= P.num_blocks);
       auto block_id = [&](int j) __attribute__((always_inline)) -> int { return __builtin_amdgcn_readlane(tv, j); };
       auto sub_of = [&](int j) __attribute__((always_inline)) -> int { return SUB == 1 ? 0 : (first + (c0 + j) * stride) % SUB; };
       auto tile_of = [&](int j) __attribute__((always_inline)) -> int { return first + (c0 + j) * stride; };

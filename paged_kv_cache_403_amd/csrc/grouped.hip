@@ -456,6 +456,7 @@ __device__ __forceinline__ void prefix_item(PrefixLds<ST, D, BS>& sh, const Grou
     if (lane >= o) incl += y;
   }
   const int ntail = __builtin_amdgcn_readlane(incl, 63);
+  PA_DEBUG_COUNT(PA_DBG_BLOCK_ID, bid < 0 || bid >= P.num_blocks);
   bid = (bid >= 0 && bid < P.num_blocks) ? bid : 0;
   const int total = ntiles + ntail;
   const int my_tiles = total > wave ? (total - wave + kWaves - 1) / kWaves : 0;
@@ -650,6 +651,7 @@ __device__ __forceinline__ void prefix_item(PrefixLds<ST, D, BS>& sh, const Grou
 #pragma unroll
         for (int b = 0; b < PrefixLds<ST, D, BS>::NBT; ++b) {
           const int id = mrow[min(k0 + b * BS, Lm - 1) / BS];
+          PA_DEBUG_COUNT(PA_DBG_BLOCK_ID, id < 0 || id >= P.num_blocks);
           sh.tail_blk[e][b] = (id >= 0 && id < P.num_blocks) ? id : 0;
         }
       }
@@ -1038,5 +1040,7 @@ hipError_t launch_decode_grouped(const GroupedArgs& a, hipStream_t st) {
   }
   return hipErrorInvalidValue;
 }
+
+PA_DEBUG_UNIT(grouped)
 
 }  // namespace pa

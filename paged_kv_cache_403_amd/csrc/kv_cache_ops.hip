@@ -48,6 +48,7 @@ __global__ __launch_bounds__(256) void kv_append_kernel(const E* __restrict__ k_
   if (tid < kAppendTok) {
     const int t = t0 + tid;
     const int64_t slot = t < num_tokens ? slots[t] : -1;
+    PA_DEBUG_COUNT(PA_DBG_SLOT, h == 0 && slot >= num_slots);
     sl[tid] = (slot >= 0 && slot < num_slots) ? slot : -1;
   }
   // K needs no exchange: each thread reads its token's slot itself, so the
@@ -97,6 +98,7 @@ __global__ __launch_bounds__(256) void kv_append_fp8_kernel(const typename AT::e
   if (tid < kAppendTok) {
     const int t = t0 + tid;
     const int64_t slot = t < num_tokens ? slots[t] : -1;
+    PA_DEBUG_COUNT(PA_DBG_SLOT, h == 0 && slot >= num_slots);
     sl[tid] = (slot >= 0 && slot < num_slots) ? slot : -1;
   }
   auto codes = [](const typename AT::elem* src, float inv) {
@@ -138,6 +140,8 @@ __global__ __launch_bounds__(256) void copy_blocks_kernel(const int32_t* __restr
                                                           u32x4* __restrict__ vc) {
   const int p = blockIdx.y;
   const int src = pairs[2 * p], dst = pairs[2 * p + 1];
+  PA_DEBUG_COUNT(PA_DBG_COPY_PAIR, (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks) && blockIdx.x == 0 &&
+                                     threadIdx.x == 0);
   if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks) return;
   const u32x4* ks = kc + src * chunks_per_block;
   const u32x4* vs = vc + src * chunks_per_block;
@@ -208,5 +212,7 @@ hipError_t launch_copy_blocks(const int32_t* pairs, int32_t num_pairs, void* k_c
   }
   return hipSuccess;
 }
+
+PA_DEBUG_UNIT(kv_cache_ops)
 
 }  // namespace pa

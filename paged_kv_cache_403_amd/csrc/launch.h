@@ -88,4 +88,13 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st);
 constexpr size_t kPrefillMaxLds = 159 * 1024;
 size_t prefill_lds_bytes(int32_t dtype, int32_t head_dim, int32_t block_size, int32_t max_context_len);
 
+#ifdef PA_DEBUG
+// Checking build: each kernel unit's counters (common.h, PA_DEBUG_UNIT),
+// added into acc[PA_DBG_KINDS] on the current device, then cleared if reset.
+hipError_t debug_counts_decode(unsigned long long* acc, bool reset);
+hipError_t debug_counts_grouped(unsigned long long* acc, bool reset);
+hipError_t debug_counts_prefill(unsigned long long* acc, bool reset);
+hipError_t debug_counts_kv_cache_ops(unsigned long long* acc, bool reset);
+#endif
+
 }  // namespace pa

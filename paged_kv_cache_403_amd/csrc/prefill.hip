@@ -137,6 +137,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(
   const int q0 = cu_q[s];
   const int n = cu_q[s + 1] - q0;
   int L = ctx_lens[s];
+  PA_DEBUG_COUNT(PA_DBG_CONTEXT_LEN, n > 0 && tile * S::TOK < n && (L > max_context || L < n));
   L = L > max_context ? max_context : L;
   const int tok0 = tile * S::TOK;
   if (n <= 0 || tok0 >= n || L < n) return;
@@ -163,6 +164,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(
     const int nt = ntiles * S::BLOCKS;
     for (int i = tid; i < nt; i += kThreads) {
       int b = i < nblk_valid ? trow[i] : 0;
+      PA_DEBUG_COUNT(PA_DBG_BLOCK_ID, b < 0 || b >= num_blocks);
       tbl[i] = (b >= 0 && b < num_blocks) ? b : 0;
     }
   }
@@ -475,5 +477,7 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st) {
   }
   return hipErrorInvalidValue;
 }
+
+PA_DEBUG_UNIT(prefill)
 
 }  // namespace pa

@@ -1,0 +1,204 @@
+"""The checking build (libpagedattn_debug.so, compiled with PA_DEBUG), loaded
+beside the product library in this process and called through the same C
+ABI:
+
+- on valid metadata -- block tables padded with -1 past each sequence's
+  blocks, negative (skipped) slots, in-range copy pairs -- every counter
+  stays zero and every output (decode, split decode, prefix-grouped decode,
+  chunked prefill, append, copy) is bit for bit the product library's;
+- each kind of metadata that the kernels clamp or skip is counted: a block
+  id out of range inside a sequence's length (decode, grouped decode,
+  prefill), a context length above max_context_len or below zero (decode)
+  or shorter than its query rows (prefill), slots past the pool (counted
+  once per token) and copy pairs out of range (once per pair).
+"""
+import numpy as np
+import pytest
+import torch
+
+import paged_kv_cache_403_amd as P
+from paged_kv_cache_403_amd import build as B
+
+pytestmark = pytest.mark.gpu
+
+NB, HKV, G, BS, D = 64, 2, 4, 16, 128
+HQ = HKV * G
+MAXB = 8
+MAXCTX = MAXB * BS
+SCALE = D ** -0.5
+DT = torch.bfloat16
+LENS = [1, 17, 70, 80, 90, MAXCTX]
+GROUP_START = [0, 2, 5, 6]  # sequences 2..4 share their first 4 blocks
+PRE_N = [5, 40, 1]
+PRE_L = [20, 100, 64]  # contexts of prefill sequences 0..2, over the tables of decode rows 1, 5, 4
+
+
+@pytest.fixture(scope="module")
+def debug_lib():
+    return P.binding.load(B.LIB_DEBUG)
+
+
+def _inputs():
+    g = torch.Generator().manual_seed(4031)
+    rng = np.random.default_rng(4031)
+    k = torch.randn(NB, HKV, BS, D, generator=g).to(DT).cuda()
+    v = torch.randn(NB, HKV, D, BS, generator=g).to(DT).cuda()
+    tables = np.full((len(LENS), MAXB), -1, np.int32)
+    for s, L in enumerate(LENS):
+        nb = (L + BS - 1) // BS
+        tables[s, :nb] = rng.choice(NB, nb, replace=False)
+    for s in (3, 4):
+        tables[s, :4] = tables[2, :4]
+    pre_tables = tables[[1, 5, 4]].copy()
+    for row, L in zip(pre_tables, PRE_L):
+        assert (row[:(L + BS - 1) // BS] >= 0).all()  # every block inside each context is a real one
+    q = torch.randn(len(LENS), HQ, D, generator=g).to(DT).cuda()
+    qp = torch.randn(sum(PRE_N), HQ, D, generator=g).to(DT).cuda()
+    return dict(k=k, v=v, tables=tables, lens=np.array(LENS, np.int32), q=q, qp=qp,
+                pre_tables=pre_tables, pre_lens=np.array(PRE_L, np.int32))
+
+
+def _dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def _decode(inp, tables, lens, partition_size):
+    cache = P.make_cache(inp["k"], inp["v"])
+    out = torch.empty_like(inp["q"])
+    S = len(lens)
+    ws_bytes = P.pa_decode_workspace_bytes(S, HQ, D, MAXCTX, partition_size)
+    ws = torch.empty(max(ws_bytes, 4), dtype=torch.uint8, device="cuda") if ws_bytes else None
+    P.pa_decode(cache, inp["q"], out, _dev(tables), _dev(lens), MAXCTX, SCALE, partition_size, ws)
+    return out
+
+
+def _grouped(inp, tables, lens):
+    cache = P.make_cache(inp["k"], inp["v"])
+    out = torch.empty_like(inp["q"])
+    ws = torch.empty(max(P.pa_decode_grouped_workspace_bytes(len(lens), HQ, D, MAXCTX), 4), dtype=torch.uint8,
+                     device="cuda")
+    P.pa_decode_grouped(cache, inp["q"], out, _dev(tables), _dev(lens), MAXCTX, SCALE,
+                        _dev(np.array(GROUP_START, np.int32)), 0, ws)
+    return out
+
+
+def _prefill(inp, tables, lens):
+    cache = P.make_cache(inp["k"], inp["v"])
+    out = torch.empty_like(inp["qp"])
+    cu = np.concatenate([[0], np.cumsum(PRE_N)]).astype(np.int32)
+    P.pa_prefill_chunk(cache, inp["qp"], out, _dev(cu), _dev(lens), _dev(tables), max(PRE_N), MAXCTX, SCALE)
+    return out
+
+
+def _append_copy(slots, pairs):
+    """A fresh zero pool, the append of 12 seeded rows at `slots`, then the
+    copy of `pairs`; the pool's bytes."""
+    g = torch.Generator().manual_seed(4032)
+    k = torch.zeros(NB, HKV, BS, D, dtype=DT, device="cuda")
+    v = torch.zeros(NB, HKV, D, BS, dtype=DT, device="cuda")
+    cache = P.make_cache(k, v)
+    kn = torch.randn(len(slots), HKV, D, generator=g).to(DT).cuda()
+    vn = torch.randn(len(slots), HKV, D, generator=g).to(DT).cuda()
+    P.pa_kv_append(cache, kn, vn, _dev(np.asarray(slots, np.int64)))
+    P.pa_copy_blocks(cache, _dev(np.asarray(pairs, np.int32).reshape(-1, 2)))
+    torch.cuda.synchronize()
+    return torch.cat([k.view(torch.uint8).flatten(), v.view(torch.uint8).flatten()]).cpu().numpy()
+
+
+VALID_SLOTS = [5, 17, -1, 100, 101, 300, -1, 512, 513, 700, 1023, 0]
+VALID_PAIRS = [[0, 40], [6, 41], [31, 42]]
+
+
+def _all(inp):
+    return {
+        "decode": _decode(inp, inp["tables"], inp["lens"], 0),
+        "decode_split": _decode(inp, inp["tables"], inp["lens"], 32),
+        "grouped": _grouped(inp, inp["tables"], inp["lens"]),
+        "prefill": _prefill(inp, inp["pre_tables"], inp["pre_lens"]),
+        "pool": _append_copy(VALID_SLOTS, VALID_PAIRS),
+    }
+
+
+def _counts(reset=True):
+    return [int(x) for x in P.pa_debug_counters(reset=reset)]
+
+
+def _bits(t):
+    return t.view(torch.int16).cpu().numpy() if isinstance(t, torch.Tensor) else t
+
+
+def test_valid_metadata_counts_nothing_and_matches_the_product(debug_lib):
+    print("[debug build] valid metadata", flush=True)
+    inp = _inputs()
+    ref = {n: _bits(t) for n, t in _all(inp).items()}
+    torch.cuda.synchronize()
+    with P.binding.using(debug_lib):
+        _counts()
+        got = {n: _bits(t) for n, t in _all(inp).items()}
+        torch.cuda.synchronize()
+        assert _counts() == [0, 0, 0, 0]
+    for n in ref:
+        assert np.array_equal(ref[n], got[n]), n
+
+
+def _only(counts, kind):
+    assert counts[kind] > 0, counts
+    assert all(c == 0 for i, c in enumerate(counts) if i != kind), counts
+
+
+def test_out_of_range_block_ids_are_counted(debug_lib):
+    inp = _inputs()
+    bad = inp["tables"].copy()
+    bad[5, 3] = NB + 7  # inside sequence 5's length
+    shared = inp["tables"].copy()
+    shared[2:5, 1] = -5  # inside the prefix that sequences 2..4 share
+    pbad = inp["pre_tables"].copy()
+    pbad[1, 2] = NB  # prefill sequence 1 (context 100)
+    with P.binding.using(debug_lib):
+        _counts()
+        for name, fn in [("decode", lambda: _decode(inp, bad, inp["lens"], 0)),
+                         ("decode_split", lambda: _decode(inp, bad, inp["lens"], 32)),
+                         ("grouped", lambda: _grouped(inp, bad, inp["lens"])),
+                         ("grouped_prefix", lambda: _grouped(inp, shared, inp["lens"])),
+                         ("prefill", lambda: _prefill(inp, pbad, inp["pre_lens"]))]:
+            print(f"[debug build] block id out of range: {name}", flush=True)
+            fn()
+            _only(_counts(), P.PA_DBG_BLOCK_ID)
+
+
+def test_out_of_range_context_lengths_are_counted(debug_lib):
+    inp = _inputs()
+    full = inp["tables"].copy()
+    for s in range(len(LENS)):
+        full[s] = inp["tables"][5]  # every entry valid, so only the lengths are wrong
+    with P.binding.using(debug_lib):
+        _counts()
+        for name, delta in [("above", (2, MAXCTX + 5)), ("negative", (0, -3))]:
+            lens = inp["lens"].copy()
+            lens[delta[0]] = delta[1]
+            print(f"[debug build] context length {name}", flush=True)
+            _decode(inp, full, lens, 0)
+            _only(_counts(), P.PA_DBG_CONTEXT_LEN)
+            _grouped(inp, full, lens)
+            _only(_counts(), P.PA_DBG_CONTEXT_LEN)
+        print("[debug build] prefill context shorter than its query rows", flush=True)
+        plens = inp["pre_lens"].copy()
+        plens[1] = PRE_N[1] - 3
+        _prefill(inp, inp["pre_tables"], plens)
+        _only(_counts(), P.PA_DBG_CONTEXT_LEN)
+
+
+def test_skipped_slots_and_copy_pairs_are_counted_once_each(debug_lib):
+    slots = list(VALID_SLOTS)
+    slots[2], slots[6], slots[9] = NB * BS, NB * BS + 77, 1 << 40  # three past the pool, none negative
+    pairs = VALID_PAIRS + [[-1, 5], [3, NB]]
+    with P.binding.using(debug_lib):
+        _counts()
+        print("[debug build] slots past the pool", flush=True)
+        _append_copy(slots, VALID_PAIRS)
+        c = _counts()
+        assert c == [0, 0, 3, 0], c
+        print("[debug build] copy pairs out of range", flush=True)
+        _append_copy(VALID_SLOTS, pairs)
+        c = _counts()
+        assert c == [0, 0, 0, 2], c
