@@ -10,7 +10,9 @@ ABI:
   id out of range inside a sequence's length (decode, grouped decode,
   prefill), a context length above max_context_len or below zero (decode)
   or shorter than its query rows (prefill), slots past the pool (counted
-  once per token) and copy pairs out of range (once per pair).
+  once per token) and copy pairs out of range (once per pair);
+- the same over an FP8 pool (its own append kernel, the FP8 decode and
+  prefill instances).
 """
 import numpy as np
 import pytest
@@ -202,3 +204,50 @@ def test_skipped_slots_and_copy_pairs_are_counted_once_each(debug_lib):
         _append_copy(VALID_SLOTS, pairs)
         c = _counts()
         assert c == [0, 0, 0, 2], c
+
+
+def test_fp8_pool_counts(debug_lib):
+    """The FP8 append kernel and the FP8 decode and prefill instances count
+    as the 16-bit ones do: nothing on valid metadata, each planted kind
+    otherwise."""
+    g = torch.Generator().manual_seed(4033)
+    k = torch.randint(0, 0x78, (NB, HKV, BS, D), dtype=torch.uint8, generator=g).cuda()
+    v = torch.randint(0, 0x78, (NB, HKV, D, BS), dtype=torch.uint8, generator=g).cuda()
+    cache = P.make_cache(k, v, DT, 0.02, 0.03)
+    inp = _inputs()
+    kn = torch.randn(len(VALID_SLOTS), HKV, D, generator=g).to(DT).cuda()
+    vn = torch.randn(len(VALID_SLOTS), HKV, D, generator=g).to(DT).cuda()
+    out = torch.empty_like(inp["q"])
+    outp = torch.empty_like(inp["qp"])
+    cu = _dev(np.concatenate([[0], np.cumsum(PRE_N)]).astype(np.int32))
+    ws_bytes = P.pa_decode_workspace_bytes(len(LENS), HQ, D, MAXCTX, 32)
+    ws = torch.empty(max(ws_bytes, 4), dtype=torch.uint8, device="cuda")
+
+    def decode(tables):
+        P.pa_decode(cache, inp["q"], out, _dev(tables), _dev(inp["lens"]), MAXCTX, SCALE, 32, ws)
+
+    def prefill(tables):
+        P.pa_prefill_chunk(cache, inp["qp"], outp, cu, _dev(inp["pre_lens"]), _dev(tables), max(PRE_N), MAXCTX,
+                           SCALE)
+
+    bad = inp["tables"].copy()
+    bad[5, 3] = NB + 7
+    pbad = inp["pre_tables"].copy()
+    pbad[1, 2] = NB
+    slots = list(VALID_SLOTS)
+    slots[2], slots[6], slots[9] = NB * BS, NB * BS + 77, 1 << 40
+    with P.binding.using(debug_lib):
+        _counts()
+        print("[debug build] fp8 pool: valid metadata", flush=True)
+        P.pa_kv_append(cache, kn, vn, _dev(np.asarray(VALID_SLOTS, np.int64)))
+        decode(inp["tables"])
+        prefill(inp["pre_tables"])
+        assert _counts() == [0, 0, 0, 0]
+        print("[debug build] fp8 pool: slots past the pool", flush=True)
+        P.pa_kv_append(cache, kn, vn, _dev(np.asarray(slots, np.int64)))
+        assert _counts() == [0, 0, 3, 0]
+        print("[debug build] fp8 pool: block ids out of range", flush=True)
+        decode(bad)
+        _only(_counts(), P.PA_DBG_BLOCK_ID)
+        prefill(pbad)
+        _only(_counts(), P.PA_DBG_BLOCK_ID)
