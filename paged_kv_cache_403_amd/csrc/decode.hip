@@ -102,7 +102,7 @@ void decode_persistent_kernel(DecodeParams P) {
     const int part = __builtin_amdgcn_readfirstlane(P.items[2 * item + 1]);
     const int L = clamp_len(P.ctx_lens[s], P.max_context);
     __syncthreads();  // the previous item's LDS merge is complete
-    decode_item<ST, D, BS, G, AT>(sh, P, s, kvh, part, L);
+    decode_item<ST, D, BS, G, AT, split_tile_buffers<ST, D, BS, G>()>(sh, P, s, kvh, part, L);
   }
 }
 

@@ -166,6 +166,19 @@ constexpr int decode_tile(int BS) {
                   : ((ST::bytes == 1 && G <= 4) || (ST::bytes == 2 && (G <= 2 || (D == 64 && G <= 4))) ? 64 : 32);
 }
 
+// Register tile buffers of the split decode items' walk (the persistent
+// split kernel and the prefix-grouped suffix kernel): one -- no prefetch
+// inside a wavefront -- for head_dim 128 with 16-token tiles and 4 q heads
+// per KV head, where a second buffer costs the registers of two more
+// resident wavefronts per SIMD (~120 registers instead of ~245) and those
+// wavefronts hide the items' loads better than the prefetch does;
+// otherwise the shape's choice.  (The one-pass grid runs faster with the
+// prefetch.)
+template <typename ST, int D, int BS, int G>
+constexpr int split_tile_buffers() {
+  return (D == 128 && G == 4 && decode_tile<ST, D, G>(BS) == 16) ? 1 : 0;
+}
+
 template <int G, int D, int BS>
 struct DecodeLds {
   float red_acc[kWaves][G][D];
@@ -185,11 +198,13 @@ __device__ __forceinline__ int clamp_len(int L, int max_context) {
 // groups, the q registers, the online softmax state and the tile walk.  (The
 // state is kept free of lane-dependent indexing -- a lane's own head is
 // picked by selects -- so the compiler keeps it in registers.)
-template <typename ST, int D, int BS, int G, typename AT = ST>
+// NBO > 0 overrides the shape's number of register tile buffers.
+template <typename ST, int D, int BS, int G, typename AT = ST, int NBO = 0>
 struct DecodeWave {
   static constexpr int TS = decode_tile<ST, D, G>(BS);  // tokens per key tile
   static constexpr int SUB = BS / TS;                   // tiles per block
   using S = DecodeShape<ST, D, TS, G>;
+  static constexpr int NBUF = NBO > 0 ? NBO : S::NBUF;
   static constexpr int VEC = S::VEC, LPR = S::LPR, RPI = S::RPI, NI = S::NI, NV = S::NV, NRED = S::NRED,
                        CPD = S::CPD;
   static constexpr int QCH = VEC * AT::bytes / 16;  // 16-byte q chunks per K chunk
@@ -392,7 +407,7 @@ struct DecodeWave {
       auto block_id = [&](int j) __attribute__((always_inline)) -> int { return __builtin_amdgcn_readlane(tv, j); };
       auto sub_of = [&](int j) __attribute__((always_inline)) -> int { return SUB == 1 ? 0 : (first + (c0 + j) * stride) % SUB; };
       auto tile_of = [&](int j) __attribute__((always_inline)) -> int { return first + (c0 + j) * stride; };
-      constexpr int NB = S::NBUF;
+      constexpr int NB = NBUF;
       u32x4 kb[NB][NI], vb[NB][NI];
 #pragma unroll
       for (int b = 0; b < NB - 1; ++b)
@@ -446,11 +461,12 @@ struct DecodeWave {
 // `partial` to leave partials, at slot slot0 + part, even for a single
 // partition.
 // ST is the pool's element type, AT the type of q and out (the same except
-// for FP8 pools, whose codes meet 16-bit q values).
-template <typename ST, int D, int BS, int G, typename AT = ST>
+// for FP8 pools, whose codes meet 16-bit q values).  NBO: register tile
+// buffers of the walk (0: the shape's choice).
+template <typename ST, int D, int BS, int G, typename AT = ST, int NBO = 0>
 __device__ __forceinline__ void decode_item(DecodeLds<G, D, BS>& sh, const DecodeParams& P, int s, int kvh,
                                             int part, int L, int start = 0, int slot0 = 0, bool partial = false) {
-  using W = DecodeWave<ST, D, BS, G, AT>;
+  using W = DecodeWave<ST, D, BS, G, AT, NBO>;
   constexpr int TS = W::TS, NI = W::NI;
   using aelem = typename AT::elem;
   aelem* __restrict__ out = static_cast<aelem*>(P.out);

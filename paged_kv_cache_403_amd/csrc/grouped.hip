@@ -784,8 +784,9 @@ void grouped_suffix_kernel(GroupedParams GP) {
     const int L = clamp_len(P.ctx_lens[s], P.max_context);
     const bool only = __builtin_amdgcn_readfirstlane(GP.nslots[s]) == 1 &&
                       __builtin_amdgcn_readfirstlane(GP.slot_base[s]) == 0;
-    decode_item<ST, D, BS, G, AT>(sh, P, s, it - item * hk, part, L, __builtin_amdgcn_readfirstlane(GP.seq_start[s]),
-                                  __builtin_amdgcn_readfirstlane(GP.slot_base[s]), !only);
+    decode_item<ST, D, BS, G, AT, split_tile_buffers<ST, D, BS, G>()>(
+        sh, P, s, it - item * hk, part, L, __builtin_amdgcn_readfirstlane(GP.seq_start[s]),
+        __builtin_amdgcn_readfirstlane(GP.slot_base[s]), !only);
   }
 }
 
