@@ -49,7 +49,8 @@ namespace {
 // scheduling).  Each workgroup ranks the lengths itself from LDS.
 constexpr int kRankMax = 256;
 template <typename ST, int D, int BS, int G, typename AT = ST>
-__global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams P) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(decode_waves_per_eu<ST, D, BS, G, false>(), 8)))
+void decode_kernel(DecodeParams P) {
   __shared__ DecodeLds<G, D, BS> sh;
   __shared__ int lens_sh[kRankMax];
   __shared__ int pick;
@@ -79,18 +80,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams P) {
 // one cost nothing for the partitions they do not have.  Consecutive items
 // are the KV heads of one (sequence, partition), which read neighbouring
 // tiles of the same blocks.
-// Wavefronts per SIMD the persistent kernel is held to: three for the
-// 16-bit instances with 32-token key tiles and up to 4 q heads per KV head
-// (168 registers fit without spills, against 186 unconstrained, one more
-// resident workgroup per compute unit to keep loads in flight); otherwise
-// what the compiler gives.
-template <typename ST, int D, int BS, int G>
-constexpr int persistent_waves_per_eu() {
-  return (ST::bytes == 2 && D == 128 && decode_tile<ST, D, G>(BS) == 32 && G == 4) ? 3 : 1;
-}
-
 template <typename ST, int D, int BS, int G, typename AT = ST>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(persistent_waves_per_eu<ST, D, BS, G>(), 8)))
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(decode_waves_per_eu<ST, D, BS, G, true>(), 8)))
 void decode_persistent_kernel(DecodeParams P) {
   __shared__ DecodeLds<G, D, BS> sh;
   const int hk = P.num_kv_heads;

@@ -179,6 +179,35 @@ constexpr int split_tile_buffers() {
   return (D == 128 && G == 4 && decode_tile<ST, D, G>(BS) == 16) ? 1 : 0;
 }
 
+// Shapes whose walk state would otherwise leave one wavefront per SIMD: 8 q
+// heads per KV head on 16-bit and FP8 pools (G sets of q chunks,
+// accumulators and probability reads per lane), and FP8 pools with tiles of
+// 32 or more tokens at 4 or more q heads (each 16-byte V chunk widens to
+// sixteen fp32 values) -- as long as a lane holds at most 32 accumulators.
+// Unconstrained, the compiler gave them 177-503 registers; with one register
+// tile buffer and a bound of two wavefronts per SIMD they take 97-232, with
+// no spills, and run up to 1.55x faster (bit-identical output).  fp32 pools
+// at 8 q heads ran 10-13% slower that way and keep the shape's choice.
+template <typename ST, int D, int BS, int G>
+constexpr bool decode_lean() {
+  constexpr int TS = decode_tile<ST, D, G>(BS);
+  return ST::bytes <= 2 && G * DecodeShape<ST, D, TS, G>::NI <= 32 &&
+         (G == 8 || (ST::bytes == 1 && G >= 4 && TS >= 32));
+}
+
+// Wavefronts per SIMD a decode kernel is held to (amdgpu_waves_per_eu):
+// two for the lean shapes above; for the split items (persistent split
+// kernel, grouped suffix kernel) three for 16-bit pools of head_dim 128
+// with 32-token tiles and 4 q heads per KV head (168 registers fit without
+// spills, against 186 unconstrained: one more resident workgroup per compute
+// unit keeps more loads in flight); otherwise what the compiler gives.
+template <typename ST, int D, int BS, int G, bool SPLIT>
+constexpr int decode_waves_per_eu() {
+  return (SPLIT && ST::bytes == 2 && D == 128 && decode_tile<ST, D, G>(BS) == 32 && G == 4) ? 3
+         : decode_lean<ST, D, BS, G>()                                                          ? 2
+                                                                                                 : 1;
+}
+
 template <int G, int D, int BS>
 struct DecodeLds {
   float red_acc[kWaves][G][D];
@@ -198,13 +227,14 @@ __device__ __forceinline__ int clamp_len(int L, int max_context) {
 // groups, the q registers, the online softmax state and the tile walk.  (The
 // state is kept free of lane-dependent indexing -- a lane's own head is
 // picked by selects -- so the compiler keeps it in registers.)
-// NBO > 0 overrides the shape's number of register tile buffers.
+// NBO > 0 overrides the number of register tile buffers (otherwise one for
+// the lean shapes, else the shape's choice).
 template <typename ST, int D, int BS, int G, typename AT = ST, int NBO = 0>
 struct DecodeWave {
   static constexpr int TS = decode_tile<ST, D, G>(BS);  // tokens per key tile
   static constexpr int SUB = BS / TS;                   // tiles per block
   using S = DecodeShape<ST, D, TS, G>;
-  static constexpr int NBUF = NBO > 0 ? NBO : S::NBUF;
+  static constexpr int NBUF = NBO > 0 ? NBO : (decode_lean<ST, D, BS, G>() ? 1 : S::NBUF);
   static constexpr int VEC = S::VEC, LPR = S::LPR, RPI = S::RPI, NI = S::NI, NV = S::NV, NRED = S::NRED,
                        CPD = S::CPD;
   static constexpr int QCH = VEC * AT::bytes / 16;  // 16-byte q chunks per K chunk

@@ -277,15 +277,6 @@ struct GroupedParams {
   const int32_t* pre_count;
 };
 
-// Wavefronts per SIMD the suffix kernel is held to: as for the split
-// decode kernel of the same shape, which runs the same items (three for
-// 16-bit pools of head_dim 128 with 32-token decode tiles and 4 q heads per
-// KV head, where 168 registers fit; otherwise what the compiler gives).
-template <typename ST, int D, int BS, int G>
-constexpr int suffix_waves_per_eu() {
-  return (ST::bytes == 2 && D == 128 && decode_tile<ST, D, G>(BS) == 32 && G == 4) ? 3 : 1;
-}
-
 // Geometry of a shared-prefix item.  Each wavefront walks its own key tiles
 // of 32 keys (as in the split decode items: tiles w, w + 4, ...) and streams
 // them from HBM straight into a ring of its own in LDS (global_load_lds, 16
@@ -766,11 +757,11 @@ void grouped_prefix_kernel(GroupedParams GP) {
 }
 
 // Suffix items times the KV heads: each sequence's own tokens, decoded as
-// the split decode items are.  An item that is its sequence's only slot
+// the split decode items are (and held to the same wavefronts per SIMD).  An item that is its sequence's only slot
 // writes the output directly; every other one leaves partials for the merge
 // kernel.
 template <typename ST, int D, int BS, int G, typename AT>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(suffix_waves_per_eu<ST, D, BS, G>(), 8)))
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(decode_waves_per_eu<ST, D, BS, G, true>(), 8)))
 void grouped_suffix_kernel(GroupedParams GP) {
   __shared__ DecodeLds<G, D, BS> sh;
   const DecodeParams& P = GP.dec;

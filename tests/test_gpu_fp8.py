@@ -48,9 +48,11 @@ def test_reduced_fp8_parity(name, part):
     assert err <= TOL[wl.spec.dtype]
 
 
-FP8_SHAPES = [  # (Hq, Hkv, D, BS, activation dtype): q heads per KV head 1, 2, 4, 8
+FP8_SHAPES = [  # (Hq, Hkv, D, BS, activation dtype): q heads per KV head 1, 2, 4, 4, 8, 8, 4, 8
     (16, 16, 128, 16, "f16"), (16, 8, 128, 32, "bf16"), (32, 8, 128, 16, "bf16"), (16, 4, 128, 32, "f16"),
     (64, 8, 128, 16, "f16"), (8, 1, 128, 32, "bf16"),
+    # 64-token blocks: whole-block tiles at 4 q heads, 32-token parts at 8
+    (32, 8, 128, 64, "f16"), (64, 8, 128, 64, "bf16"),
 ]
 
 
