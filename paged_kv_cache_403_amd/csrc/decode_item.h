@@ -182,7 +182,7 @@ constexpr int split_tile_buffers() {
 // Shapes whose walk state would otherwise leave one wavefront per SIMD: 8 q
 // heads per KV head on 16-bit and FP8 pools (G sets of q chunks,
 // accumulators and probability reads per lane), and FP8 pools with tiles of
-// 32 or more tokens at 4 or more q heads (each 16-byte V chunk widens to
+// 32 or more tokens at 2 or more q heads (each 16-byte V chunk widens to
 // sixteen fp32 values) -- as long as a lane holds at most 32 accumulators.
 // Unconstrained, the compiler gave them 177-503 registers; with one register
 // tile buffer and a bound of two wavefronts per SIMD they take 97-232, with
@@ -192,7 +192,7 @@ template <typename ST, int D, int BS, int G>
 constexpr bool decode_lean() {
   constexpr int TS = decode_tile<ST, D, G>(BS);
   return ST::bytes <= 2 && G * DecodeShape<ST, D, TS, G>::NI <= 32 &&
-         (G == 8 || (ST::bytes == 1 && G >= 4 && TS >= 32));
+         (G == 8 || (ST::bytes == 1 && G >= 2 && TS >= 32));
 }
 
 // Wavefronts per SIMD a decode kernel is held to (amdgpu_waves_per_eu):
