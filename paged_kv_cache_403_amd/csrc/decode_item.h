@@ -4,7 +4,10 @@
 // decode.hip).
 #pragma once
 
+#include <type_traits>
+
 #include "common.h"
+#include "mfma.h"
 
 namespace pa {
 
@@ -481,6 +484,279 @@ struct DecodeWave {
   __device__ __forceinline__ int dim_of(int i) const { return (i * 64 + lane) / CPD; }
 };
 
+// Decode shapes walked on the matrix cores, where the vector walk's per-byte
+// work (G heads of dot products and multiply-adds per K/V element, and the
+// widening of FP8 codes) leaves it bound by the vector ALUs: head_dim 128
+// at 8 q heads per KV head with FP8 pools of 16- to 64-token blocks or
+// 16-bit pools of 16- or 32-token blocks, and FP8 pools of 16-token blocks
+// at 4 q heads.  Measured against the vector walk (flushed medians): 1.43-
+// 1.84x with FP8 and 1.09-1.32x with 16-bit pools at 8 q heads, 1.08x for
+// FP8 at 4 q heads in one pass; 16-bit pools with 64-token blocks at 8 q
+// heads ran 0.93x, and at 4 q heads 16-bit pools gained nothing (they are
+// bound by HBM already) and FP8 with 32- or 64-token blocks lost 2-10%.
+template <typename ST, int D, int BS, int G>
+constexpr bool decode_mfma() {
+  return D == 128 && ST::bytes <= 2 && BS >= 16 &&
+         ((G == 8 && (ST::bytes == 1 || BS <= 32)) || (ST::bytes == 1 && G == 4 && BS == 16));
+}
+
+// One wavefront's part of a decode work item on the matrix cores
+// (v_mfma_f32_16x16x32).  A key tile is 32 tokens.  The G q heads are the
+// columns of the products (16 columns, the ones past G zero):
+//  * S^T = K Q^T in two 16-token groups: lane (m, g) = (l % 16, l / 16)
+//    feeds K row tau_X(m) = 8 (m / 4) + 4 X + m % 4 of the tile (group X)
+//    and 8 dimensions of it per product, so the accumulator of lane (n, g)
+//    holds head n's scores of tokens 8 g + 4 X + i -- over both groups the 8
+//    tokens 8 g .. 8 g + 7, which is the B-operand layout of
+//  * O^T = V^T P^T (k = the tile's 32 tokens): lane (m, g) reads 8
+//    consecutive tokens of V^T row 16 ds + m straight from the pool's
+//    transposed V tile; P enters as a 16-bit value and its remainder (two
+//    products), so the probabilities keep about 16 significant bits;
+//  * online softmax per head in the exp2 domain on the accumulators (the
+//    four lanes of a head's column combine by two exchanges);
+//  * K and V come from the pool with 16-byte loads (8 bytes for FP8 V),
+//    FP8 codes widened exactly to the activation type.  The dimensions a
+//    lane feeds per K product are 32 kk + 8 g (16-bit) or, so that one
+//    16-byte load of codes feeds two products, 64 (kk / 2) + 16 g +
+//    8 (kk % 2); q is laid out the same way.
+// A tile may start before the partition (32-token tiles over 16-token
+// blocks): tokens outside [tok_lo, tok_end) are masked out of the scores,
+// and V rows at or past tok_end are zeroed (a zero probability would not
+// cancel a NaN in an unused slot).
+template <typename ST, int D, int BS, int G, typename AT>
+struct DecodeWaveMx {
+  static constexpr int TS = 32;                     // tokens per key tile
+  static constexpr int SUB = BS > TS ? BS / TS : 1;  // tiles per block
+  static constexpr int NBT = BS < TS ? TS / BS : 1;  // blocks per tile
+  static constexpr bool FP8P = ST::bytes == 1;
+  static constexpr int KLD = FP8P ? 4 : 8;  // 16-byte K loads per lane per tile
+  static_assert(D == 128 && G <= 16 && NBT <= 2, "matrix-core decode shape");
+  using elem = typename ST::elem;
+  using aelem = typename AT::elem;
+
+  int lane, m, g;
+  u32x4 qb[4];   // q as the B operand of the 4 K products
+  f32x4 o[8];    // O^T: lane (n, g) holds dims 16 ds + 4 g + i of head n
+  float m_run;   // running max of head n (lane % 16), in log2 units
+  float l_run;   // this lane's share of head n's sum
+  float m_fin, l_fin;
+
+  __device__ __forceinline__ DecodeWaveMx() {
+    lane = lane_id();
+    m = lane & 15;
+    g = lane >> 4;
+#pragma unroll
+    for (int ds = 0; ds < 8; ++ds) o[ds] = f32x4{0.f, 0.f, 0.f, 0.f};
+    m_run = -INFINITY;
+    l_run = 0.f;
+  }
+
+  // first dimension of the 8 a lane of group gg feeds to K product kk
+  static __device__ __forceinline__ int dmap(int kk, int gg) {
+    return FP8P ? 64 * (kk >> 1) + 16 * gg + 8 * (kk & 1) : 32 * kk + 8 * gg;
+  }
+
+  __device__ __forceinline__ void load_q(const DecodeParams& P, int s, int kvh) {
+    const aelem* __restrict__ q = static_cast<const aelem*>(P.q);
+    const int n = m;  // this lane's column
+    const aelem* qrow = q + (static_cast<int64_t>(s) * P.num_kv_heads * G + kvh * G + (n < G ? n : 0)) * D;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) qb[kk] = n < G ? load16(qrow + dmap(kk, g)) : u32x4{0, 0, 0, 0};
+  }
+
+  __device__ __forceinline__ void walk(const DecodeParams& P, int s, int kvh, int first, int stride, int count,
+                                       int tok_lo, int tok_end) {
+    const elem* __restrict__ kc = static_cast<const elem*>(P.kc);
+    const elem* __restrict__ vc = static_cast<const elem*>(P.vc);
+    const float scale_log2 = P.scale_log2;
+    const int32_t* trow = P.tables + static_cast<int64_t>(s) * P.max_blocks;
+    const int64_t head_off = static_cast<int64_t>(kvh) * BS * D;
+    const int64_t blk_stride = static_cast<int64_t>(P.num_kv_heads) * BS * D;
+    const int num_blocks = P.num_blocks;
+    // this lane's K rows (tile tokens) of the two groups and its V tokens
+    const int tk0 = 8 * (m >> 2) + (m & 3), tk1 = tk0 + 4;
+    const int tv = 8 * g;
+
+    auto base_of = [&](int b) __attribute__((always_inline)) -> int64_t {
+      b = (b >= 0 && b < num_blocks) ? b : 0;
+      return static_cast<int64_t>(b) * blk_stride + head_off;
+    };
+    // element offset, within the tile's block(s), of tile token tk's K row
+    // and of V^T row 0 at tile token tk; the block is bA or bB (NBT == 2)
+    auto k_off = [&](int sub, int tk) __attribute__((always_inline)) -> int {
+      return ((sub * TS + tk) % BS) * D;
+    };
+    auto v_off = [&](int sub, int tk) __attribute__((always_inline)) -> int { return (sub * TS + tk) % BS; };
+
+    auto load_tile = [&](int bA, int bB, int sub, u32x4* kr, u32x4* vr) __attribute__((always_inline)) {
+      const int64_t b0 = base_of(NBT == 2 && tk0 >= BS ? bB : bA);
+      const int64_t b1 = base_of(NBT == 2 && tk1 >= BS ? bB : bA);
+      const int64_t bv = base_of(NBT == 2 && tv >= BS ? bB : bA);
+      const elem* k0 = kc + b0 + k_off(sub, tk0);
+      const elem* k1 = kc + b1 + k_off(sub, tk1);
+      if constexpr (FP8P) {
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+          kr[p] = load16_nt(k0 + 64 * p + 16 * g);
+          kr[2 + p] = load16_nt(k1 + 64 * p + 16 * g);
+        }
+      } else {
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+          kr[kk] = load16_nt(k0 + dmap(kk, g));
+          kr[4 + kk] = load16_nt(k1 + dmap(kk, g));
+        }
+      }
+      const elem* v0 = vc + bv + v_off(sub, tv) + static_cast<int64_t>(m) * BS;
+#pragma unroll
+      for (int ds = 0; ds < 8; ++ds) {
+        if constexpr (FP8P) {
+          typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+          const u32x2 w = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(v0 + 16 * ds * BS));
+          vr[ds] = u32x4{w[0], w[1], 0u, 0u};
+        } else {
+          vr[ds] = load16_nt(v0 + 16 * ds * BS);
+        }
+      }
+    };
+
+    // the K operand of product kk of group X
+    auto k_operand = [&](const u32x4* kr, int X, int kk) __attribute__((always_inline)) -> u32x4 {
+      if constexpr (FP8P) {
+        const u32x4& w = kr[2 * X + (kk >> 1)];
+        const uint32_t a = (kk & 1) ? w[2] : w[0];
+        const uint32_t b = (kk & 1) ? w[3] : w[1];
+        return u32x4{widen_fp8_pair<AT, false>(a), widen_fp8_pair<AT, true>(a), widen_fp8_pair<AT, false>(b),
+                     widen_fp8_pair<AT, true>(b)};
+      } else {
+        return kr[4 * X + kk];
+      }
+    };
+
+    auto process = [&](int t, const u32x4* kr, const u32x4* vr) __attribute__((always_inline)) {
+      const int t0 = t * TS;
+      const bool edge = t0 < tok_lo || t0 + TS > tok_end;
+      // scores of tokens 8 g + 4 X + i for head (lane % 16)
+      f32x4 sc[2];
+#pragma unroll
+      for (int X = 0; X < 2; ++X) {
+        sc[X] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) sc[X] = mfma16<AT>(k_operand(kr, X, kk), qb[kk], sc[X]);
+      }
+      float x[8];
+      float mx = -INFINITY;
+#pragma unroll
+      for (int X = 0; X < 2; ++X)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float v = sc[X][i] * scale_log2;
+          if (edge) {
+            const int tok = t0 + 8 * g + 4 * X + i;
+            v = (tok >= tok_lo && tok < tok_end) ? v : -INFINITY;
+          }
+          x[4 * X + i] = v;
+          mx = fmaxf(mx, v);
+        }
+      mx = fmaxf(mx, xor_lane<16>(mx));
+      mx = fmaxf(mx, xor_lane<32>(mx));
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+      float p[8];
+      float ps = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        p[e] = __builtin_amdgcn_exp2f(x[e] - m_new);
+        ps += p[e];
+      }
+      l_run = l_run * alpha + ps;
+      if (__builtin_amdgcn_ballot_w64(alpha != 1.f) != 0) {
+#pragma unroll
+        for (int ds = 0; ds < 8; ++ds) o[ds] *= alpha;
+      }
+      // P^T as a 16-bit value and its remainder
+      uint32_t hi[4], lo[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        hi[k] = pack2<AT>(p[2 * k], p[2 * k + 1]);
+        float h0, h1;
+        widen2<AT>(hi[k], h0, h1);
+        lo[k] = pack2<AT>(p[2 * k] - h0, p[2 * k + 1] - h1);
+      }
+      const u32x4 phi{hi[0], hi[1], hi[2], hi[3]};
+      const u32x4 plo{lo[0], lo[1], lo[2], lo[3]};
+      // V^T rows: tokens 8 g .. 8 g + 7 of the tile; those at or past
+      // tok_end are zeroed
+      const int vend = tok_end - (t0 + tv);  // tokens of this lane's 8 that are kept (may be <= 0 or >= 8)
+#pragma unroll
+      for (int ds = 0; ds < 8; ++ds) {
+        u32x4 a;
+        if constexpr (FP8P) {
+          a = u32x4{widen_fp8_pair<AT, false>(vr[ds][0]), widen_fp8_pair<AT, true>(vr[ds][0]),
+                    widen_fp8_pair<AT, false>(vr[ds][1]), widen_fp8_pair<AT, true>(vr[ds][1])};
+        } else {
+          a = vr[ds];
+        }
+        if (vend < 8) {
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const uint32_t keep_lo = 2 * k < vend ? 0x0000ffffu : 0u;
+            const uint32_t keep_hi = 2 * k + 1 < vend ? 0xffff0000u : 0u;
+            a[k] &= (keep_lo | keep_hi);
+          }
+        }
+        o[ds] = mfma16<AT>(a, phi, o[ds]);
+        o[ds] = mfma16<AT>(a, plo, o[ds]);
+      }
+    };
+
+    // tiles in chunks of 64: their block-table entries come in one vector
+    // load per block of a tile (read back with v_readlane); entries at or past
+    // tok_end are never read
+    for (int c0 = 0; c0 < count; c0 += 64) {
+      const int cn = min(64, count - c0);
+      const int tl = first + (c0 + lane) * stride;  // this lane's tile of the chunk
+      const int eA = NBT == 2 ? 2 * tl : tl / SUB;
+      const int tvA = (lane < cn && eA * BS < tok_end) ? trow[eA] : 0;
+      const int tvB = (NBT == 2 && lane < cn && (eA + 1) * BS < tok_end) ? trow[eA + 1] : 0;
+      PA_DEBUG_COUNT(PA_DBG_BLOCK_ID, lane < cn && eA * BS < tok_end && (tvA < 0 || tvA >= num_blocks));
+      PA_DEBUG_COUNT(PA_DBG_BLOCK_ID,
+                     NBT == 2 && lane < cn && (eA + 1) * BS < tok_end && (tvB < 0 || tvB >= num_blocks));
+      auto tile_of = [&](int j) __attribute__((always_inline)) -> int { return first + (c0 + j) * stride; };
+      auto load_j = [&](int j, u32x4* kr, u32x4* vr) __attribute__((always_inline)) {
+        load_tile(__builtin_amdgcn_readlane(tvA, j), NBT == 2 ? __builtin_amdgcn_readlane(tvB, j) : 0,
+                  SUB == 1 ? 0 : tile_of(j) % SUB, kr, vr);
+      };
+      u32x4 kb[KLD], vb[8];
+      for (int j = 0; j < cn; ++j) {
+        load_j(j, kb, vb);
+        process(tile_of(j), kb, vb);
+      }
+    }
+  }
+
+  // the head sums over the four lanes of each column, and the wavefront's
+  // state into LDS: O^T of head n < G at red_acc[wave][n], (m, l) by the
+  // lanes of group 0
+  __device__ __forceinline__ void store(DecodeLds<G, D, BS>& sh, int wave) {
+    float l = l_run;
+    l += xor_lane<16>(l);
+    l += xor_lane<32>(l);
+    const int n = m;
+    if (n < G) {
+#pragma unroll
+      for (int ds = 0; ds < 8; ++ds)
+        *reinterpret_cast<float4*>(&sh.red_acc[wave][n][16 * ds + 4 * g]) =
+            float4{o[ds][0], o[ds][1], o[ds][2], o[ds][3]};
+      if (g == 0) {
+        sh.red_m[wave][n] = m_run;
+        sh.red_l[wave][n] = l;
+      }
+    }
+  }
+};
+
 // One work item: the G q heads of KV head `kvh` of sequence `s` over the
 // tokens of partition `part` (the whole context when it is the only one),
 // read by the workgroup's four wavefronts taking the partition's tiles round
@@ -496,8 +772,9 @@ struct DecodeWave {
 template <typename ST, int D, int BS, int G, typename AT = ST, int NBO = 0>
 __device__ __forceinline__ void decode_item(DecodeLds<G, D, BS>& sh, const DecodeParams& P, int s, int kvh,
                                             int part, int L, int start = 0, int slot0 = 0, bool partial = false) {
-  using W = DecodeWave<ST, D, BS, G, AT, NBO>;
-  constexpr int TS = W::TS, NI = W::NI;
+  constexpr bool MX = decode_mfma<ST, D, BS, G>();
+  using W = std::conditional_t<MX, DecodeWaveMx<ST, D, BS, G, AT>, DecodeWave<ST, D, BS, G, AT, NBO>>;
+  constexpr int TS = W::TS;
   using aelem = typename AT::elem;
   aelem* __restrict__ out = static_cast<aelem*>(P.out);
   const int num_q_heads = P.num_kv_heads * G;
@@ -517,26 +794,31 @@ __device__ __forceinline__ void decode_item(DecodeLds<G, D, BS>& sh, const Decod
 
   const int tok_begin = start + part * part_tokens;  // a multiple of BS
   const int tok_end = min(L, tok_begin + part_tokens);
-  const int tile_begin = tok_begin / TS;                 // a multiple of SUB
+  const int tile_begin = tok_begin / TS;  // a multiple of SUB (matrix-core walk: may start before tok_begin)
   const int nb = (tok_end + TS - 1) / TS - tile_begin;  // key tiles in this partition
   const int my_tiles = nb > wave ? (nb - wave + kWaves - 1) / kWaves : 0;
 
   W w;
   w.load_q(P, s, kvh);
-  w.walk(P, &sh.p_lds[wave][0][0], s, kvh, tile_begin + wave, kWaves, my_tiles, tok_end);
-  float lh[G];
-  w.finish(lh);
-  if (w.tg == 0) {
+  if constexpr (MX) {
+    w.walk(P, s, kvh, tile_begin + wave, kWaves, my_tiles, tok_begin, tok_end);
+    w.store(sh, wave);
+  } else {
+    w.walk(P, &sh.p_lds[wave][0][0], s, kvh, tile_begin + wave, kWaves, my_tiles, tok_end);
+    float lh[G];
+    w.finish(lh);
+    if (w.tg == 0) {
 #pragma unroll
-    for (int h = 0; h < G; ++h)
+      for (int h = 0; h < G; ++h)
 #pragma unroll
-      for (int i = 0; i < NI; ++i) sh.red_acc[wave][h][w.dim_of(i)] = w.acc[h][i];
-  }
-  if (w.lane == 0) {
+        for (int i = 0; i < W::NI; ++i) sh.red_acc[wave][h][w.dim_of(i)] = w.acc[h][i];
+    }
+    if (w.lane == 0) {
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      sh.red_m[wave][h] = w.m[h];
-      sh.red_l[wave][h] = lh[h];
+      for (int h = 0; h < G; ++h) {
+        sh.red_m[wave][h] = w.m[h];
+        sh.red_l[wave][h] = lh[h];
+      }
     }
   }
   __syncthreads();

@@ -31,6 +31,24 @@ __device__ __forceinline__ f32x16 mfma32<F16>(const u32x4& a, const u32x4& b, co
                                                 0);
 }
 
+// v_mfma_f32_16x16x32_{bf16,f16}: lane l holds row (l % 16) of A and column
+// (l % 16) of B, each with the 8 consecutive k-elements starting at
+// 8 * (l / 16); the accumulator lane l holds column (l % 16), rows
+// 4 (l / 16) + i, element i (checked on gfx950 with an exact integer product).
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+template <typename ST>
+__device__ __forceinline__ f32x4 mfma16(const u32x4& a, const u32x4& b, const f32x4& c);
+template <>
+__device__ __forceinline__ f32x4 mfma16<BF16>(const u32x4& a, const u32x4& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0,
+                                                 0, 0);
+}
+template <>
+__device__ __forceinline__ f32x4 mfma16<F16>(const u32x4& a, const u32x4& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0, 0,
+                                                0);
+}
+
 // two fp32 -> one dword of two 16-bit values (round to nearest even)
 template <typename ST>
 __device__ __forceinline__ uint32_t pack2(float a, float b);
