@@ -523,7 +523,20 @@ constexpr bool decode_mfma() {
 // blocks): tokens outside [tok_lo, tok_end) are masked out of the scores,
 // and V rows at or past tok_end are zeroed (a zero probability would not
 // cancel a NaN in an unused slot).
-template <typename ST, int D, int BS, int G, typename AT>
+// Register tile buffers of the matrix-core walk: two (the next tile's loads
+// in flight while a tile is processed) for the split items of FP8 pools at 4
+// q heads per KV head, which hold two wavefronts per SIMD either way (184 or
+// 216 registers) and ran 5% faster so (97.5 -> 92.3 us on the shared-prefix
+// batch); one otherwise -- the second buffer cost one-pass and 8-head
+// shapes a resident wavefront, or spilled (16-bit pools), for no gain.  The
+// split kernels are the callers that pass NBO = split_tile_buffers() (1 for
+// that shape); the one-pass kernel passes 0.
+template <typename ST, int D, int BS, int G, int NBO>
+constexpr int mx_tile_buffers() {
+  return (NBO == 1 && ST::bytes == 1 && G == 4) ? 2 : 1;
+}
+
+template <typename ST, int D, int BS, int G, typename AT, int NB = 1>
 struct DecodeWaveMx {
   static constexpr int TS = 32;                     // tokens per key tile
   static constexpr int SUB = BS > TS ? BS / TS : 1;  // tiles per block
@@ -728,10 +741,24 @@ struct DecodeWaveMx {
         load_tile(__builtin_amdgcn_readlane(tvA, j), NBT == 2 ? __builtin_amdgcn_readlane(tvB, j) : 0,
                   SUB == 1 ? 0 : tile_of(j) % SUB, kr, vr);
       };
-      u32x4 kb[KLD], vb[8];
-      for (int j = 0; j < cn; ++j) {
-        load_j(j, kb, vb);
-        process(tile_of(j), kb, vb);
+      if constexpr (NB == 1) {
+        u32x4 kb[KLD], vb[8];
+        for (int j = 0; j < cn; ++j) {
+          load_j(j, kb, vb);
+          process(tile_of(j), kb, vb);
+        }
+      } else {
+        static_assert(NB == 2, "tile buffers");
+        u32x4 kb0[KLD], vb0[8], kb1[KLD], vb1[8];
+        load_j(0, kb0, vb0);
+        int j = 0;
+        for (; j + 2 <= cn; j += 2) {
+          load_j(j + 1, kb1, vb1);
+          process(tile_of(j), kb0, vb0);
+          if (j + 2 < cn) load_j(j + 2, kb0, vb0);
+          process(tile_of(j + 1), kb1, vb1);
+        }
+        if (j < cn) process(tile_of(j), kb0, vb0);
       }
     }
   }
@@ -773,7 +800,8 @@ template <typename ST, int D, int BS, int G, typename AT = ST, int NBO = 0>
 __device__ __forceinline__ void decode_item(DecodeLds<G, D, BS>& sh, const DecodeParams& P, int s, int kvh,
                                             int part, int L, int start = 0, int slot0 = 0, bool partial = false) {
   constexpr bool MX = decode_mfma<ST, D, BS, G>();
-  using W = std::conditional_t<MX, DecodeWaveMx<ST, D, BS, G, AT>, DecodeWave<ST, D, BS, G, AT, NBO>>;
+  using W = std::conditional_t<MX, DecodeWaveMx<ST, D, BS, G, AT, mx_tile_buffers<ST, D, BS, G, NBO>()>,
+                               DecodeWave<ST, D, BS, G, AT, NBO>>;
   constexpr int TS = W::TS;
   using aelem = typename AT::elem;
   aelem* __restrict__ out = static_cast<aelem*>(P.out);
