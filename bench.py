@@ -383,6 +383,25 @@ def measure_block_sizes(name, timer, iters, warmup, sizes=(8, 16, 32, 64)):
             "static_reservation_tokens": int(lens.max())}
 
 
+def measure_gqa8(timer, iters, warmup):
+    """Decode at 8 q heads per KV head (the matrix-core walk): 4 sequences of
+    65536 tokens, 64 q / 8 KV heads, head_dim 128, 16-token blocks, the
+    library's partitions, on a bf16 pool and on an FP8 pool."""
+    import workloads
+
+    rows = []
+    for fp8 in (False, True):
+        wl = workloads.custom(64, 8, 128, 16, "bf16", [65536] * 4, name="long_gqa8_decode")
+        if fp8:
+            wl = workloads.with_fp8_kv(wl)
+        st = Step(wl, -1)
+        st.copy_append()
+        rows.append({"kv_dtype": "fp8" if fp8 else "bf16", **decode_entry(st, timer, iters, warmup)})
+        del st
+    return {"workload": "long_gqa8_decode: 4 x 65536 tokens, 64 q / 8 KV heads, head_dim 128, bf16 activations, "
+                        "block_size 16", "rows": rows}
+
+
 # ---- the fp64 oracle on the host -----------------------------------------------------
 
 def host_info():
@@ -516,6 +535,7 @@ def main():
     ap.add_argument("--no-configs", action="store_true", help="skip the other configurations")
     ap.add_argument("--no-fp8", action="store_true", help="skip the FP8 KV-pool measurements")
     ap.add_argument("--no-block-sizes", action="store_true", help="skip the block-size sweep")
+    ap.add_argument("--no-gqa8", action="store_true", help="skip the 8-q-heads-per-KV-head decode batch")
     ap.add_argument("--oracle-s", type=float, default=12.0, help="oracle seconds for the headline baseline")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB a few times (the known-size reference for "
@@ -621,6 +641,8 @@ def main():
             result["fp8_kv"] = fp8
         if not args.no_block_sizes:
             result["block_sizes"] = measure_block_sizes("mha_decode_7b", timer, max(20, K // 2), W)
+        if not args.no_gqa8:
+            result["gqa8"] = measure_gqa8(timer, max(20, K // 2), W)
     if not args.no_cpu_baseline:
         log("timing the CPU oracle")
         hi = host_info()
