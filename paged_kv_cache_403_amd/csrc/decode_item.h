@@ -500,6 +500,19 @@ constexpr bool decode_mfma() {
          ((G == 8 && (ST::bytes == 1 || BS <= 32)) || (ST::bytes == 1 && G == 4 && BS == 16));
 }
 
+// Register tile buffers of the matrix-core walk: two (the next tile's loads
+// in flight while a tile is processed) for the split items of FP8 pools at 4
+// q heads per KV head, which hold two wavefronts per SIMD either way (184 or
+// 216 registers) and ran 5% faster so (97.5 -> 92.3 us on the shared-prefix
+// batch); one otherwise -- the second buffer cost one-pass and 8-head
+// shapes a resident wavefront, or spilled (16-bit pools), for no gain.  The
+// split kernels are the callers that pass NBO = split_tile_buffers() (1 for
+// that shape); the one-pass kernel passes 0.
+template <typename ST, int D, int BS, int G, int NBO>
+constexpr int mx_tile_buffers() {
+  return (NBO == 1 && ST::bytes == 1 && G == 4) ? 2 : 1;
+}
+
 // One wavefront's part of a decode work item on the matrix cores
 // (v_mfma_f32_16x16x32).  A key tile is 32 tokens.  The G q heads are the
 // columns of the products (16 columns, the ones past G zero):
@@ -523,19 +536,6 @@ constexpr bool decode_mfma() {
 // blocks): tokens outside [tok_lo, tok_end) are masked out of the scores,
 // and V rows at or past tok_end are zeroed (a zero probability would not
 // cancel a NaN in an unused slot).
-// Register tile buffers of the matrix-core walk: two (the next tile's loads
-// in flight while a tile is processed) for the split items of FP8 pools at 4
-// q heads per KV head, which hold two wavefronts per SIMD either way (184 or
-// 216 registers) and ran 5% faster so (97.5 -> 92.3 us on the shared-prefix
-// batch); one otherwise -- the second buffer cost one-pass and 8-head
-// shapes a resident wavefront, or spilled (16-bit pools), for no gain.  The
-// split kernels are the callers that pass NBO = split_tile_buffers() (1 for
-// that shape); the one-pass kernel passes 0.
-template <typename ST, int D, int BS, int G, int NBO>
-constexpr int mx_tile_buffers() {
-  return (NBO == 1 && ST::bytes == 1 && G == 4) ? 2 : 1;
-}
-
 template <typename ST, int D, int BS, int G, typename AT, int NB = 1>
 struct DecodeWaveMx {
   static constexpr int TS = 32;                     // tokens per key tile
@@ -552,7 +552,6 @@ struct DecodeWaveMx {
   f32x4 o[8];    // O^T: lane (n, g) holds dims 16 ds + 4 g + i of head n
   float m_run;   // running max of head n (lane % 16), in log2 units
   float l_run;   // this lane's share of head n's sum
-  float m_fin, l_fin;
 
   __device__ __forceinline__ DecodeWaveMx() {
     lane = lane_id();
