@@ -237,15 +237,20 @@ __global__ __launch_bounds__(kPlanThreads) void grouped_plan_kernel(PlanParams P
   // 6. suffix items in falling size (a counting sort over size classes):
   //    the persistent kernel deals positions out round robin, so the short
   //    items come last and fill in behind the long ones
-  if (tid == 0) {
-    int acc = 0;
-    for (int k = kSufBuckets - 1; k >= 0; --k) {
-      const int c = bucket_count[k];
-      bucket_count[k] = acc;
-      acc += c;
+  if (tid < 64) {  // exclusive scan of the class counts from the largest class down, by one wavefront
+    const int k = kSufBuckets - 1 - tid;
+    const int c = tid < kSufBuckets ? bucket_count[k] : 0;
+    int x = c;
+#pragma unroll
+    for (int o = 1; o < kSufBuckets; o <<= 1) {
+      const int y = __shfl_up(x, o, 64);
+      if (tid >= o) x += y;
     }
-    *P.pre_count = carry2;
-    *P.suf_count = acc;
+    if (tid < kSufBuckets) bucket_count[k] = x - c;
+    if (tid == kSufBuckets - 1) {
+      *P.pre_count = carry2;
+      *P.suf_count = x;
+    }
   }
   __syncthreads();
   for (int s = tid; s < S; s += kPlanThreads) {
