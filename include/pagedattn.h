@@ -246,6 +246,41 @@ int pa_prefill_chunk(const pa_cache* cache, const void* q, void* out, const int3
                      const int32_t* block_tables, int32_t max_blocks_per_seq, int32_t max_q_len,
                      int32_t max_context_len, float scale, void* stream);
 
+/* Chunked prefill as pa_prefill_chunk, with each workgroup's keys split into
+ * key_splits ranges run by workgroups of their own, whose partial results
+ * (per row: output unnormalised, running max, sum) are combined by
+ * log-sum-exp -- the merge of split-K decode (partial results over disjoint
+ * key sets combine exactly) -- in a second kernel.  A batch of few chunks
+ * otherwise occupies few compute units (a workgroup takes 256 rows of one KV
+ * head: one 512-token chunk at 4 q heads per KV head and 8 KV heads is 64
+ * workgroups); the split spreads it over the chip.
+ *   key_splits    1..8; 1 runs pa_prefill_chunk (no workspace needed); 0
+ *                 takes pa_prefill_choose_splits()
+ *   workspace     device, 16-byte aligned, at least
+ *                 pa_prefill_workspace_bytes(total_q, num_q_heads, head_dim,
+ *                 key_splits) bytes (fp32 partials); rewritten by each call,
+ *                 so calls sharing it must be ordered on one stream
+ * Errors as pa_prefill_chunk, plus PA_EINVAL for key_splits < 0,
+ * PA_EUNSUPPORTED above 8 and PA_EWORKSPACE for a missing or short
+ * workspace, all before anything is enqueued.  Outputs equal
+ * pa_prefill_chunk's up to the rounding of the merge. */
+int pa_prefill_chunk_split(const pa_cache* cache, const void* q, void* out, const int32_t* cu_q_lens,
+                           const int32_t* context_lens, int32_t num_seqs, int32_t total_q, int32_t num_q_heads,
+                           const int32_t* block_tables, int32_t max_blocks_per_seq, int32_t max_q_len,
+                           int32_t max_context_len, float scale, int32_t key_splits, void* workspace,
+                           size_t workspace_bytes, void* stream);
+
+/* Key splits the library takes for a prefill batch (host arithmetic only):
+ * 1 when the batch gives 256 workgroups (one per compute unit) or more,
+ * otherwise enough to reach that, at most 8 and keeping at least 4 key tiles
+ * of 64 keys per range of the longest context. */
+int32_t pa_prefill_choose_splits(const pa_cache* cache, int32_t num_seqs, int32_t num_q_heads, int32_t max_q_len,
+                                 int32_t max_context_len);
+
+/* Workspace bytes of pa_prefill_chunk_split: total_q * num_q_heads *
+ * key_splits * (head_dim + 2) floats; 0 for key_splits <= 1. */
+size_t pa_prefill_workspace_bytes(int32_t total_q, int32_t num_q_heads, int32_t head_dim, int32_t key_splits);
+
 const char* pa_status_str(int status);
 
 /* HIP's text for the calling thread's most recent PA_EHIP, or the reason of

@@ -10,5 +10,6 @@ from .binding import (  # noqa: F401
     BlockManager, PagedAttnError, Scheduler, lib, make_cache, pa_cache, pa_copy_blocks, pa_decode,
     pa_decode_choose_partition, pa_decode_grouped, pa_decode_grouped_workspace_bytes, pa_decode_noalloc,
     pa_decode_workspace_bytes,
-    pa_debug_counters, pa_kv_append, pa_prefill_chunk, status_str,
+    pa_debug_counters, pa_kv_append, pa_prefill_choose_splits, pa_prefill_chunk, pa_prefill_chunk_split,
+    pa_prefill_workspace_bytes, status_str,
 )

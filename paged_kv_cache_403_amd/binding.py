@@ -70,6 +70,10 @@ _SIGNATURES = {
                                          _i32, _vp, ctypes.c_size_t, _vp]),
     "pa_prefill_chunk": (ctypes.c_int, [_cp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp, _i32, _i32, _i32,
                                         ctypes.c_float, _vp]),
+    "pa_prefill_chunk_split": (ctypes.c_int, [_cp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp, _i32, _i32, _i32,
+                                              ctypes.c_float, _i32, _vp, ctypes.c_size_t, _vp]),
+    "pa_prefill_choose_splits": (_i32, [_cp, _i32, _i32, _i32, _i32]),
+    "pa_prefill_workspace_bytes": (ctypes.c_size_t, [_i32, _i32, _i32, _i32]),
     "pa_status_str": (ctypes.c_char_p, [ctypes.c_int]),
     "pa_last_error": (ctypes.c_char_p, []),
     "pa_debug_counters": (ctypes.c_int, [_vp, _i32]),
@@ -367,6 +371,32 @@ def pa_prefill_chunk(cache: pa_cache, q, out, cu_q_lens, context_lens, block_tab
                                 int(block_tables.shape[1]), int(max_q_len), int(max_context_len), float(scale),
                                 _stream(stream, q))
     _check(rc, "pa_prefill_chunk")
+
+
+def pa_prefill_choose_splits(cache: pa_cache, num_seqs, num_q_heads, max_q_len, max_context_len) -> int:
+    return int(lib().pa_prefill_choose_splits(ctypes.byref(cache), int(num_seqs), int(num_q_heads), int(max_q_len),
+                                              int(max_context_len)))
+
+
+def pa_prefill_workspace_bytes(total_q, num_q_heads, head_dim, key_splits) -> int:
+    return int(lib().pa_prefill_workspace_bytes(int(total_q), int(num_q_heads), int(head_dim), int(key_splits)))
+
+
+def pa_prefill_chunk_split(cache: pa_cache, q, out, cu_q_lens, context_lens, block_tables, max_q_len,
+                           max_context_len, scale, key_splits=0, workspace=None, stream=None):
+    _check_rows(cache, q, out)
+    num_seqs = int(context_lens.shape[0])
+    _check_tables(block_tables, context_lens, num_seqs)
+    _need(cu_q_lens, "cu_q_lens", dtype=_torch().int32, shape=(num_seqs + 1,))
+    _same_device(q, out, cu_q_lens, context_lens, block_tables, workspace)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    rc = lib().pa_prefill_chunk_split(ctypes.byref(cache), _dev_ptr(q, "q"), _dev_ptr(out, "out"),
+                                      _dev_ptr(cu_q_lens, "cu_q_lens"), _dev_ptr(context_lens, "context_lens"),
+                                      num_seqs, int(q.shape[0]), int(q.shape[1]),
+                                      _dev_ptr(block_tables, "block_tables"), int(block_tables.shape[1]),
+                                      int(max_q_len), int(max_context_len), float(scale), int(key_splits),
+                                      _dev_ptr(workspace, "workspace"), ws_bytes, _stream(stream, q))
+    _check(rc, "pa_prefill_chunk_split")
 
 
 # ---- host block manager ---------------------------------------------------------------

@@ -313,10 +313,17 @@ int pa_decode(const pa_cache* cache, const void* q, void* out, int32_t num_seqs,
   return hip_status(pa::launch_decode(a, static_cast<hipStream_t>(stream)));
 }
 
-int pa_prefill_chunk(const pa_cache* cache, const void* q, void* out, const int32_t* cu_q_lens,
-                     const int32_t* context_lens, int32_t num_seqs, int32_t total_q, int32_t num_q_heads,
-                     const int32_t* block_tables, int32_t max_blocks_per_seq, int32_t max_q_len,
-                     int32_t max_context_len, float scale, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Everything pa_prefill_chunk and pa_prefill_chunk_split check and derive
+// before they touch the GPU; *nothing is set when there is no row to run.
+int prefill_prepare(const pa_cache* cache, const void* q, void* out, const int32_t* cu_q_lens,
+                    const int32_t* context_lens, int32_t num_seqs, int32_t total_q, int32_t num_q_heads,
+                    const int32_t* block_tables, int32_t max_blocks_per_seq, int32_t max_q_len,
+                    int32_t max_context_len, float scale, pa::PrefillArgs* out_args, bool* nothing) {
+  *nothing = false;
   int rc = check_cache(cache);
   if (rc != PA_OK) return rc;
   if (cache->dtype == PA_F32) return PA_EUNSUPPORTED;
@@ -332,9 +339,13 @@ int pa_prefill_chunk(const pa_cache* cache, const void* q, void* out, const int3
   // the block-table entries of the longest context are staged in LDS
   if (pa::prefill_lds_bytes(cache->dtype, cache->head_dim, cache->block_size, max_context_len) > pa::kPrefillMaxLds)
     return PA_EUNSUPPORTED;
-  if (num_seqs == 0 || total_q == 0 || max_q_len == 0) return PA_OK;
+  if (num_seqs == 0 || total_q == 0 || max_q_len == 0) {
+    *nothing = true;
+    return PA_OK;
+  }
   if (!q || !out || !cu_q_lens || !context_lens || !block_tables) return PA_EINVAL;
-  pa::PrefillArgs a{};
+  pa::PrefillArgs& a = *out_args;
+  a = pa::PrefillArgs{};
   a.q = q;
   a.out = out;
   a.k_cache = cache->k_cache;
@@ -359,6 +370,63 @@ int pa_prefill_chunk(const pa_cache* cache, const void* q, void* out, const int3
   a.max_blocks_per_seq = max_blocks_per_seq;
   a.max_q_len = max_q_len;
   a.max_context_len = max_context_len;
+  return PA_OK;
+}
+
+size_t prefill_workspace(int32_t total_q, int32_t num_q_heads, int32_t head_dim, int32_t key_splits) {
+  if (total_q <= 0 || num_q_heads <= 0 || head_dim <= 0 || key_splits <= 1) return 0;
+  return static_cast<size_t>(total_q) * num_q_heads * key_splits * (head_dim + 2) * sizeof(float);
+}
+
+}  // namespace
+
+extern "C" {
+
+int pa_prefill_chunk(const pa_cache* cache, const void* q, void* out, const int32_t* cu_q_lens,
+                     const int32_t* context_lens, int32_t num_seqs, int32_t total_q, int32_t num_q_heads,
+                     const int32_t* block_tables, int32_t max_blocks_per_seq, int32_t max_q_len,
+                     int32_t max_context_len, float scale, void* stream) {
+  pa::PrefillArgs a{};
+  bool nothing = false;
+  const int rc = prefill_prepare(cache, q, out, cu_q_lens, context_lens, num_seqs, total_q, num_q_heads,
+                                 block_tables, max_blocks_per_seq, max_q_len, max_context_len, scale, &a, &nothing);
+  if (rc != PA_OK || nothing) return rc;
+  return hip_status(pa::launch_prefill(a, static_cast<hipStream_t>(stream)));
+}
+
+int32_t pa_prefill_choose_splits(const pa_cache* cache, int32_t num_seqs, int32_t num_q_heads, int32_t max_q_len,
+                                 int32_t max_context_len) {
+  if (!cache || cache->num_kv_heads <= 0 || num_q_heads <= 0 || num_q_heads % cache->num_kv_heads != 0) return 1;
+  return pa::prefill_choose_splits(num_seqs, cache->num_kv_heads, num_q_heads / cache->num_kv_heads, max_q_len,
+                                   max_context_len);
+}
+
+size_t pa_prefill_workspace_bytes(int32_t total_q, int32_t num_q_heads, int32_t head_dim, int32_t key_splits) {
+  return prefill_workspace(total_q, num_q_heads, head_dim, key_splits);
+}
+
+int pa_prefill_chunk_split(const pa_cache* cache, const void* q, void* out, const int32_t* cu_q_lens,
+                           const int32_t* context_lens, int32_t num_seqs, int32_t total_q, int32_t num_q_heads,
+                           const int32_t* block_tables, int32_t max_blocks_per_seq, int32_t max_q_len,
+                           int32_t max_context_len, float scale, int32_t key_splits, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  if (key_splits < 0) return PA_EINVAL;
+  if (key_splits > pa::kPrefillMaxSplits) return PA_EUNSUPPORTED;
+  pa::PrefillArgs a{};
+  bool nothing = false;
+  const int rc = prefill_prepare(cache, q, out, cu_q_lens, context_lens, num_seqs, total_q, num_q_heads,
+                                 block_tables, max_blocks_per_seq, max_q_len, max_context_len, scale, &a, &nothing);
+  if (rc != PA_OK || nothing) return rc;
+  const int32_t k = key_splits == 0 ? pa::prefill_choose_splits(num_seqs, cache->num_kv_heads, a.group, max_q_len,
+                                                                max_context_len)
+                                    : key_splits;
+  if (k > 1) {
+    const size_t need = prefill_workspace(total_q, num_q_heads, cache->head_dim, k);
+    if (!workspace || workspace_bytes < need) return PA_EWORKSPACE;
+    a.key_splits = k;
+    a.ws_o = static_cast<float*>(workspace);
+    a.ws_ml = a.ws_o + static_cast<size_t>(total_q) * num_q_heads * k * cache->head_dim;
+  }
   return hip_status(pa::launch_prefill(a, static_cast<hipStream_t>(stream)));
 }
 

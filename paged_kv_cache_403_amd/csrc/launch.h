@@ -62,6 +62,13 @@ struct PrefillArgs {
   // that mean code * k_scale (K) and code * v_scale (V)
   int32_t kv_fp8 = 0;
   float k_scale = 1.f, v_scale = 1.f;
+  // key split: each row tile's key tiles in key_splits ranges, whose
+  // partials (ws_o: [total_q * Hq][key_splits][head_dim] unnormalised,
+  // ws_ml: [.][key_splits][2] running max in log2 units and sum) a second
+  // kernel merges by log-sum-exp; 1 = no split, no workspace
+  int32_t key_splits = 1;
+  float* ws_o = nullptr;
+  float* ws_ml = nullptr;
 };
 
 hipError_t launch_kv_append(const void* k_new, const void* v_new, const int64_t* slots, int32_t num_tokens,
@@ -81,6 +88,14 @@ hipError_t launch_copy_blocks(const int32_t* pairs, int32_t num_pairs, void* k_c
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t st);
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st);
+
+// Key splits of chunked prefill: at most kPrefillMaxSplits; the library's
+// choice spreads a batch of few row tiles over about kPrefillTargetItems
+// workgroups (one per compute unit), each range keeping >= 4 key tiles.
+constexpr int32_t kPrefillMaxSplits = 8;
+constexpr int64_t kPrefillTargetItems = 256;
+int32_t prefill_choose_splits(int32_t num_seqs, int32_t num_kv_heads, int32_t group, int32_t max_q_len,
+                              int32_t max_context_len);
 
 // Dynamic LDS one chunked-prefill workgroup needs: two K/V tile stages plus
 // the block-table entries of every key tile (bound by max_context_len).  The

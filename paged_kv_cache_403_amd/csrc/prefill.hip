@@ -72,13 +72,16 @@ struct PrefillShape {
   static_assert(BS % CPE == 0 || CPE == 8, "a V chunk stays inside one block's dim row");
 };
 
-template <typename ST, typename PT, int D, int BS, int G>
+// KS: the key-split instance (nsplit key ranges, partials to the
+// workspace); the other one runs each row tile's keys whole, as if nsplit
+// were 1 at compile time.
+template <typename ST, typename PT, int D, int BS, int G, bool KS>
 __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(
     const typename ST::elem* __restrict__ q, const typename PT::elem* __restrict__ kc,
     const typename PT::elem* __restrict__ vc, const int32_t* __restrict__ tables, int max_blocks,
     const int32_t* __restrict__ ctx_lens, const int32_t* __restrict__ cu_q, int num_blocks, int num_kv_heads,
     int num_units, int row_tiles, int max_context, float scale_log2, float v_scale,
-    typename ST::elem* __restrict__ out) {
+    typename ST::elem* __restrict__ out, int nsplit, float* __restrict__ ws_o, float* __restrict__ ws_ml) {
   using S = PrefillShape<ST, PT, D, BS, G>;
   using elem = typename ST::elem;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
@@ -95,20 +98,23 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(
   const int xcd = blockIdx.x % kXcds;
   const int slot = blockIdx.x / kXcds;
   const int xunits = num_units > xcd ? (num_units - xcd + kXcds - 1) / kXcds : 0;
-  const int nitems = xunits * row_tiles;
+  const int nsp = KS ? nsplit : 1;
+  const int nitems = xunits * row_tiles * nsp;  // (unit, row tile, key range)
   if (slot >= nitems) return;
   int item = slot;
   if (nitems <= kSortMax) {
     int* cost = reinterpret_cast<int*>(tbl);  // the table area is free until the item is known
     __shared__ int chosen;
     for (int e = tid; e < nitems; e += kThreads) {
-      const int u = xcd + kXcds * (e / row_tiles);
+      const int u = xcd + kXcds * (e / (row_tiles * nsp));
       const int su = u / num_kv_heads;
       const int nu = cu_q[su + 1] - cu_q[su];
       const int Lu = min(ctx_lens[su], max_context);
-      const int t0 = (e % row_tiles) * S::TOK;
-      // key tiles the item reads (0: no rows)
-      cost[e] = (nu <= 0 || t0 >= nu || Lu < nu) ? 0 : (Lu - nu + min(nu, t0 + S::TOK) - 1) / kKeys + 1;
+      const int t0 = ((e / nsp) % row_tiles) * S::TOK;
+      const int ke = e % nsp;
+      // key tiles the row tile reads (0: no rows), and this item's share
+      const int tt = (nu <= 0 || t0 >= nu || Lu < nu) ? 0 : (Lu - nu + min(nu, t0 + S::TOK) - 1) / kKeys + 1;
+      cost[e] = (ke + 1) * tt / nsp - ke * tt / nsp;
     }
     __syncthreads();
     for (int e = tid; e < nitems; e += kThreads) {
@@ -124,10 +130,11 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(
     item = chosen;
     __syncthreads();  // cost[] is overwritten by the block table below
   }
-  const int unit = xcd + kXcds * (item / row_tiles);
+  const int unit = xcd + kXcds * (item / (row_tiles * nsp));
   const int s = unit / num_kv_heads;
   const int g = unit - s * num_kv_heads;
-  const int tile = item % row_tiles;
+  const int tile = (item / nsp) % row_tiles;
+  const int ksplit = item % nsp;
 
   const int lane = lane_id();
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -155,8 +162,22 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(
   const int tok_last = min(n, tok0 + S::TOK) - 1;
   const int kmax = L - n + tok_last;  // last key any row of the tile sees
   const int ntiles = kmax / kKeys + 1;
+  // this item's key tiles (all of them without a split)
+  const int t_lo = KS ? ksplit * ntiles / nsp : 0;
+  const int t_hi = KS ? (ksplit + 1) * ntiles / nsp : ntiles;
   const int diag0 = L - n + tok0;  // keys above this may be masked for some row
   const int nblk_valid = (L + BS - 1) / BS;
+  // partial rows of this item in the workspace (key-split instance)
+  const int64_t prow = (static_cast<int64_t>(q0 + tok) * num_q_heads + hq) * nsp + ksplit;
+  if (KS && t_lo >= t_hi) {
+    // more key ranges than the row tile has key tiles: an empty partial
+    if (row_ok && half == 0) *reinterpret_cast<float2*>(ws_ml + 2 * prow) = float2{-INFINITY, 0.f};
+    return;
+  }
+  // From here on the item has at least one key tile (ntiles >= 1 since
+  // L >= n), so the prologue and the first tile run unconditionally; a
+  // guarded prologue would leave the Q loads outstanding on one path, and
+  // the wait for them would then sit inside the tile loop.
 
   // block-table entries of every tile, out-of-range ids replaced by block 0
   {
@@ -257,14 +278,18 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(
   for (int ds = 0; ds < S::DSUB; ++ds) o_acc[ds] = f32x16{};
 
   __syncthreads();  // block table in LDS
-  fetch(0);
-  stage(0, 0);
+  fetch(t_lo);
+  stage(t_lo, 0);
   __syncthreads();
 
   const int arow = key_perm(nl);
-  for (int t = 0; t < ntiles; ++t) {
-    const int buf = t & 1;
-    if (t + 1 < ntiles) fetch(t + 1);
+  // one key tile; `first` marks the sequence's first tile (tile 0), the
+  // only one whose probabilities enter PV in two parts.  It runs once for
+  // the item's first tile and then in a loop with first = false, so the
+  // loop body carries no first-tile path.
+  auto tile_step = [&](int t, bool first) __attribute__((always_inline)) {
+    const int buf = (t - t_lo) & 1;
+    if (t + 1 < t_hi) fetch(t + 1);
     const elem* kl = smem + buf * S::STAGE;
     const elem* vl = kl + S::K_ELEMS;
 
@@ -311,7 +336,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(
     // The next tile goes from registers to LDS between the score and the
     // softmax phases: its buffer was released by the previous iteration's
     // barrier, and LDS is otherwise idle while the exponentials run.
-    if (t + 1 < ntiles) stage(t + 1, buf ^ 1);
+    if (t + 1 < t_hi) stage(t + 1, buf ^ 1);
     if (active) {
       // the reference max moves only when the tile's max passes it by kLazy
       const bool move = mx > m_run + kLazy;
@@ -319,10 +344,14 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(
       const float m_new = move ? mx : m_run;
       const float alpha = move ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
       m_run = m_new;
+      // a row that has seen no key yet (only possible in a key range after
+      // the first: all of its keys so far lie past its diagonal) keeps
+      // probabilities of 0 instead of exp2(-inf + inf)
+      const float m_ref = (KS && m_new == -INFINITY) ? 0.f : m_new;
       float psum = 0.f;
       // P^T as B operand, one per 16-key step
       u32x4 pb[4], pl[4];
-      const bool split = t == 0;  // first tile: probabilities as two 16-bit parts
+      const bool split = first;  // first tile: probabilities as two 16-bit parts
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
@@ -330,7 +359,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(
           float p[8];
 #pragma unroll
           for (int u = 0; u < 8; ++u) {
-            p[u] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[ks][a8 * 8 + u], scale_log2, -m_new));
+            p[u] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[ks][a8 * 8 + u], scale_log2, -m_ref));
             psum += p[u];
           }
           uint32_t hi[4];
@@ -365,10 +394,25 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(
       }
     }
     __syncthreads();
-  }
+  };
+  tile_step(t_lo, t_lo == 0);
+  for (int t = t_lo + 1; t < t_hi; ++t) tile_step(t, false);
 
   const float l_tot = halves_sum(l_run);  // both halves of the row
   if (!row_ok) return;
+  if constexpr (KS) {
+    // partials of this key range: O unnormalised, (max, sum); lane value j
+    // of dim-subtile ds is dim 32 ds + 8 (j/4) + 4 half + j%4
+    float* po = ws_o + prow * D;
+#pragma unroll
+    for (int ds = 0; ds < S::DSUB; ++ds)
+#pragma unroll
+      for (int j4 = 0; j4 < 4; ++j4)
+        *reinterpret_cast<float4*>(po + ds * 32 + j4 * 8 + half * 4) =
+            float4{o_acc[ds][j4 * 4 + 0], o_acc[ds][j4 * 4 + 1], o_acc[ds][j4 * 4 + 2], o_acc[ds][j4 * 4 + 3]};
+    if (half == 0) *reinterpret_cast<float2*>(ws_ml + 2 * prow) = float2{m_run, l_tot};
+    return;
+  }
   const float inv = v_scale / l_tot;
   elem* op = out + (static_cast<int64_t>(q0 + tok) * num_q_heads + hq) * D;
   // lane value j of dim-subtile ds is dim 32 ds + 8 (j/4) + 4 half + j%4
@@ -384,6 +428,47 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(
     }
 }
 
+// Log-sum-exp merge of the key ranges' partials: a thread per (row, 4
+// dimensions); rows are (token, q head) of the chunks, rows past the last
+// chunk's token are not the kernel's.  A range without keys (sum 0) carries
+// no weight.
+constexpr int kMergeThreads = 256;
+template <typename ST, int D>
+__global__ __launch_bounds__(kMergeThreads) void prefill_merge_kernel(const float* __restrict__ ws_o,
+                                                                      const float* __restrict__ ws_ml,
+                                                                      const int32_t* __restrict__ cu_q, int num_seqs,
+                                                                      int num_q_heads, int nsplit, float v_scale,
+                                                                      typename ST::elem* __restrict__ out) {
+  const int64_t idx = static_cast<int64_t>(blockIdx.x) * kMergeThreads + threadIdx.x;
+  const int64_t row = idx / (D / 4);
+  const int d0 = static_cast<int>(idx % (D / 4)) * 4;
+  if (row >= static_cast<int64_t>(cu_q[num_seqs]) * num_q_heads) return;
+  float M = -INFINITY;
+  for (int k = 0; k < nsplit; ++k) {
+    const float2 ml = *reinterpret_cast<const float2*>(ws_ml + 2 * (row * nsplit + k));
+    if (ml.y > 0.f) M = fmaxf(M, ml.x);
+  }
+  float4 num = {0.f, 0.f, 0.f, 0.f};
+  float den = 0.f;
+  for (int k = 0; k < nsplit; ++k) {
+    const float2 ml = *reinterpret_cast<const float2*>(ws_ml + 2 * (row * nsplit + k));
+    if (ml.y > 0.f) {
+      const float w = __builtin_amdgcn_exp2f(ml.x - M);
+      const float4 o = *reinterpret_cast<const float4*>(ws_o + (row * nsplit + k) * D + d0);
+      num.x = __builtin_fmaf(o.x, w, num.x);
+      num.y = __builtin_fmaf(o.y, w, num.y);
+      num.z = __builtin_fmaf(o.z, w, num.z);
+      num.w = __builtin_fmaf(o.w, w, num.w);
+      den = __builtin_fmaf(ml.y, w, den);
+    }
+  }
+  const float inv = den > 0.f ? v_scale / den : 0.f;
+  uint2 wv;
+  wv.x = pack2<ST>(num.x * inv, num.y * inv);
+  wv.y = pack2<ST>(num.z * inv, num.w * inv);
+  *reinterpret_cast<uint2*>(out + row * D + d0) = wv;
+}
+
 template <typename ST, typename PT, int D, int BS, int G>
 hipError_t launch_t(const PrefillArgs& a, hipStream_t st) {
   using S = PrefillShape<ST, PT, D, BS, G>;
@@ -391,10 +476,12 @@ hipError_t launch_t(const PrefillArgs& a, hipStream_t st) {
   const int row_tiles = (a.max_q_len + S::TOK - 1) / S::TOK;
   if (row_tiles == 0 || a.num_seqs == 0) return hipSuccess;
   const int units = a.num_seqs * a.num_kv_heads;
-  const int64_t grid = static_cast<int64_t>((units + kXcds - 1) / kXcds) * kXcds * row_tiles;
+  const int nsplit = a.key_splits > 1 ? a.key_splits : 1;
+  if (nsplit > 1 && (!a.ws_o || !a.ws_ml)) return hipErrorInvalidValue;
+  const int64_t grid = static_cast<int64_t>((units + kXcds - 1) / kXcds) * kXcds * row_tiles * nsplit;
   if (grid > 0x7fffffff) return hipErrorInvalidValue;
   const int max_tiles = (a.max_context_len + kKeys - 1) / kKeys;
-  const int per_xcd = (units + kXcds - 1) / kXcds * row_tiles;
+  const int per_xcd = (units + kXcds - 1) / kXcds * row_tiles * nsplit;
   const size_t tbl_entries = std::max<size_t>(static_cast<size_t>(max_tiles) * S::BLOCKS,
                                               per_xcd <= kSortMax ? static_cast<size_t>(per_xcd) : 0);
   const size_t lds = 2 * S::STAGE * sizeof(elem) + tbl_entries * sizeof(int32_t);
@@ -402,15 +489,29 @@ hipError_t launch_t(const PrefillArgs& a, hipStream_t st) {
   // above 64 KiB of dynamic LDS must be allowed explicitly; a function-local
   // static is set once, also when several host threads launch at once
   static const hipError_t lds_attr =
-      hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_kernel<ST, PT, D, BS, G>),
+      hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_kernel<ST, PT, D, BS, G, false>),
                           hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(kPrefillMaxLds));
   if (lds_attr != hipSuccess) return lds_attr;
+  static const hipError_t lds_attr_ks =
+      hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_kernel<ST, PT, D, BS, G, true>),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(kPrefillMaxLds));
+  if (lds_attr_ks != hipSuccess) return lds_attr_ks;
   using pelem = typename PT::elem;
-  hipLaunchKernelGGL((prefill_kernel<ST, PT, D, BS, G>), dim3(static_cast<unsigned>(grid)), dim3(kThreads), lds, st,
+  auto kernel = nsplit > 1 ? prefill_kernel<ST, PT, D, BS, G, true> : prefill_kernel<ST, PT, D, BS, G, false>;
+  hipLaunchKernelGGL(kernel, dim3(static_cast<unsigned>(grid)), dim3(kThreads), lds, st,
                      static_cast<const elem*>(a.q), static_cast<const pelem*>(a.k_cache),
                      static_cast<const pelem*>(a.v_cache), a.block_tables, a.max_blocks_per_seq, a.context_lens,
                      a.cu_q_lens, a.num_blocks, a.num_kv_heads, units, row_tiles, a.max_context_len,
-                     a.scale * kLog2e * a.k_scale, a.v_scale, static_cast<elem*>(a.out));
+                     a.scale * kLog2e * a.k_scale, a.v_scale, static_cast<elem*>(a.out), nsplit, a.ws_o, a.ws_ml);
+  if (nsplit == 1) return hipGetLastError();
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t threads = static_cast<int64_t>(a.total_q) * a.num_kv_heads * G * (D / 4);
+  const int64_t blocks = (threads + kMergeThreads - 1) / kMergeThreads;
+  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((prefill_merge_kernel<ST, D>), dim3(static_cast<unsigned>(blocks)), dim3(kMergeThreads), 0, st,
+                     a.ws_o, a.ws_ml, a.cu_q_lens, a.num_seqs, a.num_kv_heads * G, nsplit, a.v_scale,
+                     static_cast<elem*>(a.out));
   return hipGetLastError();
 }
 
@@ -468,6 +569,20 @@ size_t prefill_lds_bytes(int32_t dtype, int32_t head_dim, int32_t block_size, in
   // table entries of every tile, or the item costs of the longest-first
   // ordering if more
   return 2 * stage * 2 + std::max<size_t>(max_tiles * blocks_per_tile, kSortMax) * sizeof(int32_t);
+}
+
+int32_t prefill_choose_splits(int32_t num_seqs, int32_t num_kv_heads, int32_t group, int32_t max_q_len,
+                              int32_t max_context_len) {
+  if (num_seqs <= 0 || num_kv_heads <= 0 || group <= 0 || max_q_len <= 0 || max_context_len <= 0) return 1;
+  const int64_t tok = kRows / group;  // tokens per row tile
+  const int64_t row_tiles = (max_q_len + tok - 1) / tok;
+  const int64_t units = static_cast<int64_t>(num_seqs) * num_kv_heads;
+  const int64_t grid = (units + kXcds - 1) / kXcds * kXcds * row_tiles;
+  if (grid >= kPrefillTargetItems) return 1;
+  int64_t k = (kPrefillTargetItems + grid - 1) / grid;
+  const int64_t tiles = (static_cast<int64_t>(max_context_len) + kKeys - 1) / kKeys;
+  k = std::min<int64_t>(k, std::max<int64_t>(1, tiles / 4));
+  return static_cast<int32_t>(std::min<int64_t>(k, kPrefillMaxSplits));
 }
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st) {

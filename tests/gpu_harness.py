@@ -28,12 +28,14 @@ class ProductResult:
 
 
 def run_step(wl, fill=SENTINEL, free_order=None, partition_size=0, device="cuda", keep_pool=True,
-             prefill_all=False, return_cache=False, grouped=False, group_start=None):
+             prefill_all=False, return_cache=False, grouped=False, group_start=None, key_splits=None):
     """One step of `wl`: setup appends, the step's copies and appends, then
     decode for one-token sequences and chunked prefill for the others (or
     prefill for all when prefill_all).  grouped: decode through the
     prefix-grouped entry point with the hint `group_start` (int32 starts
-    over the decode sequences, None for no hint)."""
+    over the decode sequences, None for no hint).  key_splits: chunked
+    prefill through the key-split entry point with that many ranges (0: the
+    library's choice), None for pa_prefill_chunk."""
     sp = wl.spec
     order = wl.free_order if free_order is None else free_order
     cache = PagedKVCache(sp.num_blocks, sp.num_kv_heads, sp.block_size, sp.head_dim, sp.dtype, device, order,
@@ -81,8 +83,16 @@ def run_step(wl, fill=SENTINEL, free_order=None, partition_size=0, device="cuda"
         cu = np.concatenate([[0], np.cumsum(n_new[idx])]).astype(np.int32)
         tables = plan.block_tables[torch.from_numpy(idx).to(device)].contiguous()
         lens = plan.context_lens[torch.from_numpy(idx).to(device)].contiguous()
-        P.pa_prefill_chunk(cache.desc, q, out, torch.from_numpy(cu).to(device), lens, tables,
-                           int(n_new[idx].max()), int(plan.host_lens[idx].max()), sp.scale)
+        max_q, max_c = int(n_new[idx].max()), int(plan.host_lens[idx].max())
+        if key_splits is None:
+            P.pa_prefill_chunk(cache.desc, q, out, torch.from_numpy(cu).to(device), lens, tables, max_q, max_c,
+                               sp.scale)
+        else:
+            k = key_splits or P.pa_prefill_choose_splits(cache.desc, len(idx), sp.num_q_heads, max_q, max_c)
+            ws_bytes = P.pa_prefill_workspace_bytes(q.shape[0], sp.num_q_heads, sp.head_dim, k)
+            ws = torch.empty(max(ws_bytes, 4), dtype=torch.uint8, device=device) if ws_bytes else None
+            P.pa_prefill_chunk_split(cache.desc, q, out, torch.from_numpy(cu).to(device), lens, tables, max_q,
+                                     max_c, sp.scale, key_splits, ws)
         out_all[rows] = to_host(out)
     torch.cuda.synchronize()
     if return_cache:

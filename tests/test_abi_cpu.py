@@ -134,6 +134,47 @@ def test_prefill_rejects_fp32():
     assert _prefill(_cache(dtype=P.PA_F32)) == P.PA_EUNSUPPORTED
 
 
+def _prefill_split(cache, key_splits, ws=None, ws_bytes=0, num_seqs=2, total_q=10, num_q_heads=32, max_blocks=8,
+                   max_q=5, max_ctx=100, scale=0.1):
+    return P.lib().pa_prefill_chunk_split(ctypes.byref(cache), FAKE, FAKE, FAKE, FAKE, num_seqs, total_q,
+                                          num_q_heads, FAKE, max_blocks, max_q, max_ctx, scale, key_splits, ws,
+                                          ws_bytes, None)
+
+
+def test_split_prefill_validation_before_any_hip_call():
+    """Key splits out of range, a missing or short workspace and every
+    pa_prefill_chunk check are refused before anything is enqueued."""
+    c = _cache()
+    assert _prefill_split(c, -1) == P.PA_EINVAL
+    assert _prefill_split(c, 9) == P.PA_EUNSUPPORTED
+    need = P.pa_prefill_workspace_bytes(10, 32, 128, 4)
+    assert need == 10 * 32 * 4 * (128 + 2) * 4
+    assert _prefill_split(c, 4) == P.PA_EWORKSPACE
+    assert _prefill_split(c, 4, FAKE, need - 1) == P.PA_EWORKSPACE
+    assert _prefill_split(c, 4, scale=-1.0) == P.PA_EINVAL
+    assert _prefill_split(c, 4, max_q=200) == P.PA_EINVAL
+    assert _prefill_split(_cache(dtype=P.PA_F32), 4) == P.PA_EUNSUPPORTED
+    # nothing to run: no workspace asked for
+    assert _prefill_split(c, 4, num_seqs=0, total_q=0) == P.PA_OK
+    assert P.pa_prefill_workspace_bytes(10, 32, 128, 1) == 0
+    assert P.pa_prefill_workspace_bytes(0, 32, 128, 4) == 0
+
+
+def test_split_prefill_choice():
+    """Splits only a batch of fewer workgroups than compute units, up to 8,
+    with at least 4 key tiles of 64 keys per range."""
+    c = _cache()  # 8 KV heads
+    # one 512-token chunk at 4 q heads per KV head: 8 units x 8 row tiles = 64 workgroups -> 4 ranges
+    assert P.pa_prefill_choose_splits(c, 1, 32, 512, 8192) == 4
+    # the same on a short context: 4 key tiles allow a single range
+    assert P.pa_prefill_choose_splits(c, 1, 32, 512, 256) == 1
+    # 8 chunks: 512 workgroups, no split
+    assert P.pa_prefill_choose_splits(c, 8, 32, 512, 8192) == 1
+    # one 64-token chunk: 8 workgroups -> capped at 8 ranges
+    assert P.pa_prefill_choose_splits(c, 1, 32, 64, 65536) == 8
+    assert P.pa_prefill_choose_splits(c, 0, 32, 64, 65536) == 1
+
+
 def test_prefill_rejects_contexts_whose_table_exceeds_lds():
     """The chunk's block-table entries are staged in LDS next to the two K/V
     tile buffers: a context whose table does not fit is refused before any
