@@ -29,7 +29,9 @@ rates (tiny decode latency; the 7B-shaped MHA decode; the shared-prefix batch
 through plain and prefix-grouped decode, rates on unique and logical bytes,
 and its copy-on-write copies; the long batch at the library's partition
 choice; the mixed chunked-prefill step), the FP8 pool, the block-size sweep,
-and the fp64 oracle's rate on the host cores for each configuration.
+decode at 8 q heads per KV head, prefill of one or two chunks with and
+without the key split, and the fp64 oracle's rate on the host cores for each
+configuration.
 
 Prints one JSON line on stdout; progress goes to stderr.
 """
@@ -402,6 +404,49 @@ def measure_gqa8(timer, iters, warmup):
                         "block_size 16", "rows": rows}
 
 
+def measure_prefill_split(timer, iters, warmup):
+    """Prefill of few chunks, where one workgroup per (row tile, KV head)
+    leaves most compute units idle: one and two 512-token chunks on 4096 and
+    16384 cached tokens (32 q / 8 KV heads, head_dim 128, bf16, 16-token
+    blocks), the whole-keys launch against the key split the library
+    chooses (pa_prefill_chunk_split with key_splits 0)."""
+    import torch
+
+    import workloads
+
+    rows = []
+    for cached in ((4096,), (16384,), (4096, 4096), (16384, 16384)):
+        wl = workloads.custom(32, 8, 128, 16, "bf16", [c + 512 for c in cached], n_new=[512] * len(cached),
+                              name="few_chunk_prefill")
+        sp = wl.spec
+        st = Step(wl, 0)
+        st.copy_append()
+        P = st.P
+        k = P.pa_prefill_choose_splits(st.cache.desc, len(st.pre), sp.num_q_heads, st.maxq_pre, st.maxc_pre)
+        ws = torch.empty(max(P.pa_prefill_workspace_bytes(st.q_pre.shape[0], sp.num_q_heads, sp.head_dim, k), 16),
+                         dtype=torch.uint8, device="cuda")
+
+        def split():
+            P.pa_prefill_chunk_split(st.cache.desc, st.q_pre, st.out_pre, st.cu_pre, st.len_pre, st.tab_pre,
+                                     st.maxq_pre, st.maxc_pre, sp.scale, k, ws)
+
+        whole_us, _ = timer.median_us(st.prefill, iters, warmup)
+        split_us, _ = timer.median_us(split, iters, warmup)
+        row = {"chunks": len(cached), "cached_tokens": cached[0], "key_splits": k, "flops": st.pre_flops,
+               "whole_us": round(whole_us, 2), "split_us": round(split_us, 2)}
+        for tag, us in (("whole", whole_us), ("split", split_us)):
+            tf = st.pre_flops / (us * 1e-6) / 1e12
+            row[tag + "_tflops"] = round(tf, 2)
+            row[tag + "_frac"] = round(tf / MFMA_BF16_PEAK_TFLOPS, 4)
+        log(f"few-chunk prefill {len(cached)} x 512 on {cached[0]}: whole {whole_us:.1f} us, "
+            f"{k} key splits {split_us:.1f} us")
+        rows.append(row)
+        del st, ws
+        torch.cuda.empty_cache()
+    return {"workload": "few_chunk_prefill: 1 or 2 chunks of 512 tokens on 4096 or 16384 cached tokens, 32 q / 8 KV "
+                        "heads, head_dim 128, bf16, block_size 16", "peak": MFMA_BF16_PEAK_TFLOPS, "rows": rows}
+
+
 # ---- the fp64 oracle on the host -----------------------------------------------------
 
 def host_info():
@@ -536,6 +581,8 @@ def main():
     ap.add_argument("--no-fp8", action="store_true", help="skip the FP8 KV-pool measurements")
     ap.add_argument("--no-block-sizes", action="store_true", help="skip the block-size sweep")
     ap.add_argument("--no-gqa8", action="store_true", help="skip the 8-q-heads-per-KV-head decode batch")
+    ap.add_argument("--no-prefill-split", action="store_true",
+                    help="skip the few-chunk prefill batches (whole keys against the key split)")
     ap.add_argument("--oracle-s", type=float, default=12.0, help="oracle seconds for the headline baseline")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB a few times (the known-size reference for "
@@ -643,6 +690,8 @@ def main():
             result["block_sizes"] = measure_block_sizes("mha_decode_7b", timer, max(20, K // 2), W)
         if not args.no_gqa8:
             result["gqa8"] = measure_gqa8(timer, max(20, K // 2), W)
+        if not args.no_prefill_split:
+            result["prefill_split"] = measure_prefill_split(timer, max(20, K // 2), W)
     if not args.no_cpu_baseline:
         log("timing the CPU oracle")
         hi = host_info()
