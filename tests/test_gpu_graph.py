@@ -1,8 +1,9 @@
 """The library's launches under HIP graph capture.
 
 A mixed step -- copy-on-write copies, the append of every new token,
-chunked prefill and split decode (planner, walk and merge) -- and a
-prefix-grouped decode call are captured once in a graph and replayed with
+chunked prefill and split decode (planner, walk and merge) --, a
+prefix-grouped decode call and a key-split prefill (partials and merge) are
+each captured once in a graph and replayed with
 fresh queries in the graph's input buffers.  Between replays the same work
 runs eagerly with synchronisations around it; every replay must give the
 eager outputs bit for bit.  The outputs are filled with NaN before each
@@ -100,3 +101,45 @@ def test_grouped_decode_graph_replays_match_eager():
         assert torch.equal(_bits(out), _bits(want)), r
         assert not torch.isnan(want.float()).any()
     print(f"[gpu] graph: {REPLAYS} grouped replays bit-equal to eager", flush=True)
+
+
+def test_split_prefill_graph_replays_match_eager():
+    """Key-split prefill (partials into the workspace, then the merge) on
+    one 512-token chunk over 2048 cached tokens, at the library's split."""
+    import paged_kv_cache_403_amd as P
+
+    wl = workloads.custom(32, 8, 128, 16, "bf16", [2048 + 512], n_new=[512], seed=5, name="one_chunk")
+    sp = wl.spec
+    st = bench.Step(wl, 0)
+    st.copy_append()
+    k = P.pa_prefill_choose_splits(st.cache.desc, len(st.pre), sp.num_q_heads, st.maxq_pre, st.maxc_pre)
+    assert k > 1
+    print(f"[gpu] graph: split prefill, {k} key splits", flush=True)
+    ws = torch.empty(P.pa_prefill_workspace_bytes(st.q_pre.shape[0], sp.num_q_heads, sp.head_dim, k),
+                     dtype=torch.uint8, device="cuda")
+
+    def split():
+        P.pa_prefill_chunk_split(st.cache.desc, st.q_pre, st.out_pre, st.cu_pre, st.len_pre, st.tab_pre,
+                                 st.maxq_pre, st.maxc_pre, sp.scale, k, ws)
+
+    gen = torch.Generator().manual_seed(4037)
+    split()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        split()
+    torch.cuda.synchronize()
+    for r in range(REPLAYS):
+        _new_queries(st, gen)
+        torch.cuda.synchronize()
+        split()
+        torch.cuda.synchronize()
+        want = st.out_pre.clone()
+        st.out_pre.fill_(float("nan"))
+        ws.fill_(0xFF)  # NaN partials: a replay must rewrite every one it reads
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(_bits(st.out_pre), _bits(want)), r
+        assert not torch.isnan(want.float()).any()
+    print(f"[gpu] graph: {REPLAYS} split-prefill replays bit-equal to eager", flush=True)
