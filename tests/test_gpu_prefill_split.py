@@ -10,6 +10,7 @@ import numpy as np
 import pytest
 
 import workloads
+from fullsize_check import check_rows, chunk_edges
 from gpu_harness import TOL, run_step
 from oracle import attention as A
 from oracle.cache import run_workload
@@ -81,3 +82,18 @@ def test_split_prefill_nan_in_unused_slots_does_not_leak():
     b = run_step(wl, keep_pool=False, key_splits=4)
     assert np.isfinite(to_f64(a.out, "bf16")).all()
     assert np.array_equal(a.out, b.out)
+
+
+@pytest.mark.parametrize("n_chunks,cached", [(1, 4096), (1, 16384), (2, 4096), (2, 16384)])
+def test_split_prefill_fullsize_few_chunks(n_chunks, cached):
+    """The few-chunk batches bench.py times (512-token chunks, 32 q / 8 KV
+    heads, head_dim 128, bf16, 16-token blocks) at the split the library
+    chooses: the first and last row of every chunk and 14 random ones, every
+    q head, against the definition."""
+    wl = workloads.custom(32, 8, 128, 16, "bf16", [cached + 512] * n_chunks, n_new=[512] * n_chunks,
+                          seed=cached + n_chunks, name="few_chunk_prefill")
+    print(f"[gpu] split prefill full size: {n_chunks} x 512 on {cached} cached", flush=True)
+    res = run_step(wl, keep_pool=False, key_splits=0)
+    worst, n, where = check_rows(wl, res.out, TOL["bf16"], rows_of=chunk_edges(np.random.default_rng(cached), 14))
+    assert n >= n_chunks * 2 * 32, n  # first and last rows at least, every q head
+    print(f"[gpu]   {n} rows, worst |err| {worst:.3g} at {where}", flush=True)
