@@ -76,12 +76,13 @@ def test_decode_checks(entry):
     _raises("must be a device tensor", call, q, out, tab, lens)
 
 
-def test_prefill_checks():
+@pytest.mark.parametrize("entry", ["whole", "split"])
+def test_prefill_checks(entry):
     c = _cache()
     q, out, tab, lens = _dec_args(S=10)
     tab, lens = tab[:2], lens[:2]
     cu = torch.tensor([0, 5, 10], dtype=torch.int32)
-    f = P.pa_prefill_chunk
+    f = P.pa_prefill_chunk if entry == "whole" else P.pa_prefill_chunk_split
     _raises("out must have shape", f, c, q, out[:9], cu, lens, tab, 5, 100, 0.1)
     _raises("cu_q_lens must be torch.int32", f, c, q, out, cu.long(), lens, tab, 5, 100, 0.1)
     _raises("cu_q_lens must have shape", f, c, q, out, cu[:2], lens, tab, 5, 100, 0.1)
