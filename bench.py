@@ -408,16 +408,20 @@ def measure_prefill_split(timer, iters, warmup):
     """Prefill of few chunks, where one workgroup per (row tile, KV head)
     leaves most compute units idle: one and two 512-token chunks on 4096 and
     16384 cached tokens (32 q / 8 KV heads, head_dim 128, bf16, 16-token
-    blocks), the whole-keys launch against the key split the library
-    chooses (pa_prefill_chunk_split with key_splits 0)."""
+    blocks; the one chunk on 16384 also over an FP8 pool), the whole-keys
+    launch against the key split the library chooses (pa_prefill_chunk_split
+    with key_splits 0)."""
     import torch
 
     import workloads
 
     rows = []
-    for cached in ((4096,), (16384,), (4096, 4096), (16384, 16384)):
+    cases = [(c, False) for c in ((4096,), (16384,), (4096, 4096), (16384, 16384))] + [((16384,), True)]
+    for cached, fp8 in cases:
         wl = workloads.custom(32, 8, 128, 16, "bf16", [c + 512 for c in cached], n_new=[512] * len(cached),
                               name="few_chunk_prefill")
+        if fp8:
+            wl = workloads.with_fp8_kv(wl)
         sp = wl.spec
         st = Step(wl, 0)
         st.copy_append()
@@ -432,19 +436,21 @@ def measure_prefill_split(timer, iters, warmup):
 
         whole_us, _ = timer.median_us(st.prefill, iters, warmup)
         split_us, _ = timer.median_us(split, iters, warmup)
-        row = {"chunks": len(cached), "cached_tokens": cached[0], "key_splits": k, "flops": st.pre_flops,
+        row = {"chunks": len(cached), "cached_tokens": cached[0], "kv_dtype": "fp8" if fp8 else "bf16",
+               "key_splits": k, "flops": st.pre_flops,
                "whole_us": round(whole_us, 2), "split_us": round(split_us, 2)}
         for tag, us in (("whole", whole_us), ("split", split_us)):
             tf = st.pre_flops / (us * 1e-6) / 1e12
             row[tag + "_tflops"] = round(tf, 2)
             row[tag + "_frac"] = round(tf / MFMA_BF16_PEAK_TFLOPS, 4)
-        log(f"few-chunk prefill {len(cached)} x 512 on {cached[0]}: whole {whole_us:.1f} us, "
+        log(f"few-chunk prefill {len(cached)} x 512 on {cached[0]} ({row['kv_dtype']} pool): whole {whole_us:.1f} us, "
             f"{k} key splits {split_us:.1f} us")
         rows.append(row)
         del st, ws
         torch.cuda.empty_cache()
     return {"workload": "few_chunk_prefill: 1 or 2 chunks of 512 tokens on 4096 or 16384 cached tokens, 32 q / 8 KV "
-                        "heads, head_dim 128, bf16, block_size 16", "peak": MFMA_BF16_PEAK_TFLOPS, "rows": rows}
+                        "heads, head_dim 128, bf16 activations (bf16 pool; one row over an FP8 pool), block_size 16",
+            "peak": MFMA_BF16_PEAK_TFLOPS, "rows": rows}
 
 
 # ---- the fp64 oracle on the host -----------------------------------------------------
